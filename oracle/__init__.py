@@ -1,0 +1,247 @@
+"""CPU oracle for the sliding-window ring / grouped-verify attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``sliding_window_ring_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``swr_oracle.c`` (plain C, IEEE binary64, fixed
+summation order); this module only builds it with gcc and marshals numpy
+arrays through ctypes.  Each function below names the passage of the pages it
+follows; the C file states the readings taken where the pages are silent.
+
+Pages:
+  * "Announcing Carat: An inference engine designed for Gemma 4" (ring buffer
+    section; "More FLOPs can be faster"; "Doing it all in one kernel can be
+    slower").
+  * "Improving Decode Throughput on Intel Gaudi 3" ("Patching sliding window KV
+    allocation"; "Our approach").
+  * "gemma-cuda-hybrid" README ("Features": GQA shapes, FP8 e4m3 KV cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "swr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+FP8 = 1
+
+_CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile swr_oracle.c with gcc into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _bind(h):
+    """Declare the C signatures on a loaded oracle library."""
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    F, D = ctypes.c_float, ctypes.c_double
+    h.orc_bf16_value_n.argtypes = [P, I64, P]
+    h.orc_e4m3_value_n.argtypes = [P, I64, P]
+    h.orc_e4m3_encode_n.argtypes = [P, I64, F, P]
+    h.orc_region_bytes.argtypes = [I, I, I, I]
+    h.orc_region_bytes.restype = I64
+    h.orc_kv_append.argtypes = [P, P, P, P, I, I, F, F, P, P, P, P, I, I, I, I, I]
+    h.orc_swa_decode.argtypes = [P, P, P, P, I, I, D, D, P, P, I, I, I, I, D, P]
+    h.orc_gqa_verify.argtypes = [P, P, P, P, I, I, D, D, P, P, P, P, I, I, I, I, I, D, P]
+    h.orc_global_attend.argtypes = [P, P, P, P, I, I, D, D, P, P, P, I, I, I, I, I, I, D, P]
+    h.orc_num_threads.restype = I
+    return h
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = _bind(ctypes.CDLL(build()))
+    return _lib
+
+
+def build_variant(src_text: str, out_dir: str) -> str:
+    """Compile an edited copy of the oracle source (tests use this to plant a
+    mistake and check that the pins catch it).  Returns the library path."""
+    c = os.path.join(out_dir, "swr_oracle_variant.c")
+    so = os.path.join(out_dir, "liboracle_variant.so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", *_CFLAGS, c, "-o", so, "-lm"])
+    return so
+
+
+class use_library:
+    """Context manager: route this module's functions to another build of the
+    oracle (a planted-mistake variant) for the duration of the block."""
+
+    def __init__(self, path: str):
+        self.handle = _bind(ctypes.CDLL(path))
+
+    def __enter__(self):
+        global _lib
+        lib()
+        self.saved, _lib = _lib, self.handle
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().orc_num_threads()
+
+
+# ---------------------------------------------------------------- formats
+
+def bf16_value(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (upper half of an IEEE binary32)."""
+    x = _c(bits, np.uint16)
+    out = np.empty(x.shape, np.float64)
+    lib().orc_bf16_value_n(_p(x), x.size, _p(out))
+    return out
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """OCP E4M3FN decode ("gemma-cuda-hybrid", Features: FP8 e4m3 KV)."""
+    x = _c(codes, np.uint8)
+    out = np.empty(x.shape, np.float64)
+    lib().orc_e4m3_value_n(_p(x), x.size, _p(out))
+    return out
+
+
+def e4m3_encode(bits, scale: float) -> np.ndarray:
+    """E4M3FN code of bf16 values divided by a per-tensor scale: nearest code
+    to the exact quotient, ties to even, saturating at +-448."""
+    x = _c(bits, np.uint16)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_n(_p(x), x.size, ctypes.c_float(scale), _p(out))
+    return out
+
+
+def region_bytes(cap: int, hkv: int, d: int, dtype: int) -> int:
+    """Bytes of one K (or V) region of `cap` slots (cap a multiple of 8)."""
+    n = lib().orc_region_bytes(cap, hkv, d, dtype)
+    if n < 0:
+        raise ValueError("invalid region shape")
+    return int(n)
+
+
+# ---------------------------------------------------------------- layout helpers
+
+def k_elem_index(slot, g, d, hkv, dd):
+    """Element index of K(slot, g, d): token-major rows."""
+    return (slot * hkv + g) * dd + d
+
+
+def v_elem_index(slot, g, d, hkv, dd):
+    """Element index of V(slot, g, d): 8-slot blocks, the 8 slots of a block
+    contiguous for each (g, d)."""
+    return ((slot // 8 * hkv + g) * dd + d) * 8 + slot % 8
+
+
+# ---------------------------------------------------------------- operations
+
+def _check_rc(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, k_new, v_new, pos0,
+              n_new=None, wrap=True):
+    """Append tokens to each request's region, in place.
+
+    Ring mode (wrap=True): slot = position mod cap ("Announcing Carat", ring
+    buffer section; "Improving Decode Throughput on Intel Gaudi 3", "Our
+    approach": K and V of a token go to the same slot).  Global mode
+    (wrap=False): slot = position.  k_new, v_new: bf16 bits [B][T][Hkv][D].
+    """
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    B, T, hkv, d = k_new.shape
+    k_off = _c(k_off, np.int64)
+    v_off = _c(v_off, np.int64)
+    pos0 = _c(pos0, np.int32)
+    nn = None if n_new is None else _c(n_new, np.int32)
+    assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
+    rc = lib().orc_kv_append(_p(k_pool), _p(v_pool), _p(k_off), _p(v_off), cap, dtype,
+                             ctypes.c_float(k_scale), ctypes.c_float(v_scale), _p(k_new), _p(v_new),
+                             _p(pos0), _p(nn), B, T, hkv, d, 1 if wrap else 0)
+    _check_rc(rc, "kv_append")
+
+
+def swa_decode(k_pool, v_pool, k_off, v_off, W, dtype, k_scale, v_scale, q, pos, hkv, scale):
+    """Sliding-window decode over each request's ring, read in storage order.
+
+    q: bf16 bits [B][Hq][D]; pos[b]: the query's position, its token already in
+    the ring.  Returns float64 [B][Hq][D].
+    """
+    q = _c(q, np.uint16)
+    B, hq, d = q.shape
+    out = np.empty((B, hq, d), np.float64)
+    rc = lib().orc_swa_decode(_p(k_pool), _p(v_pool), _p(_c(k_off, np.int64)),
+                              _p(_c(v_off, np.int64)), W, dtype, k_scale, v_scale, _p(q),
+                              _p(_c(pos, np.int32)), B, hq, hkv, d, scale, _p(out))
+    _check_rc(rc, "swa_decode")
+    return out
+
+
+def gqa_verify(k_pool, v_pool, k_off, v_off, W, dtype, k_scale, v_scale, k_prop, v_prop, q, pos0,
+               hkv, scale):
+    """Speculative verify on a sliding layer: G heads x S proposals per KV head.
+
+    q: bf16 bits [B][S][Hq][D]; k_prop, v_prop: bf16 bits [B][S][Hkv][D];
+    the ring holds positions < pos0[b].  Returns float64 [B][S][Hq][D].
+    """
+    q = _c(q, np.uint16)
+    B, S, hq, d = q.shape
+    out = np.empty((B, S, hq, d), np.float64)
+    rc = lib().orc_gqa_verify(_p(k_pool), _p(v_pool), _p(_c(k_off, np.int64)),
+                              _p(_c(v_off, np.int64)), W, dtype, k_scale, v_scale,
+                              _p(_c(k_prop, np.uint16)), _p(_c(v_prop, np.uint16)), _p(q),
+                              _p(_c(pos0, np.int32)), B, S, hq, hkv, d, scale, _p(out))
+    _check_rc(rc, "gqa_verify")
+    return out
+
+
+def global_attend(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, q, q_pos, key_count,
+                  hkv, scale, padded=True):
+    """Global-layer attention over contiguous regions ("Announcing Carat",
+    "More FLOPs can be faster": scores over key_count keys, causal softmax by
+    query position, weighted sum of values; padded=True contracts over the
+    64-padded key range with a masked tail).
+
+    q: bf16 bits [B][S][Hq][D]; q_pos: [B][S]; key_count: [B].
+    Returns float64 [B][S][Hq][D].
+    """
+    q = _c(q, np.uint16)
+    B, S, hq, d = q.shape
+    out = np.empty((B, S, hq, d), np.float64)
+    rc = lib().orc_global_attend(_p(k_pool), _p(v_pool), _p(_c(k_off, np.int64)),
+                                 _p(_c(v_off, np.int64)), cap, dtype, k_scale, v_scale, _p(q),
+                                 _p(_c(q_pos, np.int32)), _p(_c(key_count, np.int32)),
+                                 1 if padded else 0, B, S, hq, hkv, d, scale, _p(out))
+    _check_rc(rc, "global_attend")
+    return out

@@ -1,0 +1,85 @@
+"""Planted mistakes: each case edits one plausible mistake into a copy of the
+oracle source, builds it, and checks that at least one pin fails against it.
+This is the evidence that the pins constrain the oracle (a pin that passes
+for a broken oracle would prove nothing).  Runs on the CPU only.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_attention as att
+import test_oracle_formats as fmt
+import test_oracle_ring as ring
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "swr_oracle.c")).read()
+
+# (name, original snippet, planted mistake)
+MISTAKES = [
+    ("e4m3 exponent bias 8", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    ("e4m3 subnormal scale", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("e4m3 ties away from zero", "code = (lo % 2 == 0) ? lo : lo + 1;", "code = lo + 1;"),
+    ("e4m3 ties truncate", "code = (lo % 2 == 0) ? lo : lo + 1;", "code = lo;"),
+    ("encode divides by scale twice", "double v = fabs(x) / (double)scale;",
+     "double v = fabs(x) / (double)scale / (double)scale;"),
+    ("V region not blocked",
+     "return (((size_t)(s / 8) * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d) * 8 +\n         (size_t)(s % 8);",
+     "return ((size_t)s * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d;"),
+    ("append slot off by one", "int64_t s = wrap ? p % cap : p;", "int64_t s = wrap ? (p + 1) % cap : p;"),
+    ("dot product drops the last dim", "for (int d = 0; d < D; ++d) dot += q[(size_t)r * D + d] * kd[d];",
+     "for (int d = 0; d < D - 1; ++d) dot += q[(size_t)r * D + d] * kd[d];"),
+    ("score scale missing", "s[(size_t)r * nk + k] = scale * dot;", "s[(size_t)r * nk + k] = dot;"),
+    ("weight sum counts keys", "l[r] += w;", "l[r] += (w > 0.0) ? 1.0 : 0.0;"),
+    ("GQA heads interleaved",
+     "orc_bf16_value(q[(((size_t)b * S + i) * Hq + (size_t)g * G + h) * D + d]);",
+     "orc_bf16_value(q[(((size_t)b * S + i) * Hq + (size_t)h * (Hq / G) + g) * D + d]);"),
+    ("verify window one key too wide", "lo[i * G + h] = qp - W + 1 > 0 ? qp - W + 1 : 0; /* R1 per row */",
+     "lo[i * G + h] = qp - W > 0 ? qp - W : 0;"),
+    ("verify not causal among proposals", "hi[i * G + h] = qp;                              /* causal among proposals */",
+     "hi[i * G + h] = p0 + S - 1;"),
+    ("proposal positions shifted", "keys[nr + i] = (key_ref){-(int64_t)i - 1, p0 + i};",
+     "keys[nr + i] = (key_ref){-(int64_t)i - 1, p0 + i + 1};"),
+    ("ring slot position ignores wrap", "return last - (((last - s) % W) + W) % W;",
+     "return s + (last / W) * W;"),
+    ("global mask not causal", "hi[i * G + h] = qp < kc - 1 ? qp : kc - 1;", "hi[i * G + h] = kc - 1;"),
+    ("global mask one key late", "hi[i * G + h] = qp < kc - 1 ? qp : kc - 1;",
+     "hi[i * G + h] = qp + 1 < kc - 1 ? qp + 1 : kc - 1;"),
+    ("decode reads one slot short", "int nk = (int)(p + 1 < W ? p + 1 : W); /* slots ever written */",
+     "int nk = (int)(p < W ? p : W);"),
+]
+
+CHECKS = [
+    fmt.test_e4m3_decode_matches_torch_all_codes,
+    fmt.test_e4m3_landmarks,
+    lambda: fmt.test_e4m3_encode_matches_torch_power_of_two_scales(2.0 ** -4),
+    fmt.test_e4m3_encode_exact_rational_brute_force,
+    fmt.test_e4m3_encode_ties_to_even,
+    fmt.test_e4m3_round_trip_all_finite_codes,
+    ring.test_slot_is_position_mod_window_one_by_one,
+    ring.test_fp8_append_stores_encoded_codes,
+    *att.ALL_CHECKS,
+]
+
+
+def test_every_mistake_snippet_is_present_once():
+    for name, orig, _ in MISTAKES:
+        assert SRC.count(orig) == 1, name
+
+
+def test_unmodified_source_passes_all_checks():
+    for c in CHECKS:
+        c()
+
+
+@pytest.mark.parametrize("name,orig,bad", MISTAKES, ids=[m[0] for m in MISTAKES])
+def test_planted_mistake_is_caught(name, orig, bad, tmp_path):
+    path = oracle.build_variant(SRC.replace(orig, bad), str(tmp_path))
+    caught = None
+    with oracle.use_library(path):
+        for c in CHECKS:
+            try:
+                c()
+            except (AssertionError, ValueError) as e:  # a pin failed
+                caught = (getattr(c, "__name__", "check"), e)
+                break
+    assert caught is not None, f"no pin catches: {name}"

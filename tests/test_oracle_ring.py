@@ -1,0 +1,105 @@
+"""Pins for the oracle's append / slot mapping.
+
+"Announcing Carat" (Replacing page lookups with a ring buffer): a token's slot
+is its absolute position modulo the window, and a new token reuses the oldest
+slot without moving the rest.  "Improving Decode Throughput on Intel Gaudi 3"
+(Our approach): K and V of a token are written together, so both rings carry
+the same rotation.  The region layout read back here uses numpy reshapes of
+the declared layout (K rows [slot][Hkv][D]; V in 8-slot blocks
+[slot/8][Hkv][D][8]), not the oracle's own index arithmetic.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from helpers import f64
+
+
+def k_view(pool, off, cap, hkv, d):
+    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(cap, hkv, d)
+
+
+def v_view(pool, off, cap, hkv, d):
+    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(cap // 8, hkv, d, 8)
+
+
+def position_tokens(n, hkv, d, base=0):
+    """Token t carries value (base + t) in every element (exact in bf16 for
+    small integers), and its V carries -(base + t)."""
+    vals = np.arange(base, base + n, dtype=np.float32)
+    k = np.broadcast_to(vals[:, None, None], (n, hkv, d))
+    return synthetic.bf16_bits(k), synthetic.bf16_bits(-k)
+
+
+def test_slot_is_position_mod_window_one_by_one():
+    W, hkv, d = 16, 2, 8
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    kp = np.zeros(rb, np.uint8)
+    vp = np.zeros(rb, np.uint8)
+    off = np.zeros(1, np.int64)
+    k, v = position_tokens(40, hkv, d, base=1)  # value = position + 1 (0 = empty)
+    for t in range(40):
+        oracle.kv_append(kp, vp, off, off, W, oracle.BF16, 1.0, 1.0, k[None, t:t + 1], v[None, t:t + 1],
+                         np.array([t], np.int32))
+        K = f64(k_view(kp, 0, W, hkv, d))
+        V = f64(v_view(vp, 0, W, hkv, d))
+        for s in range(W):
+            # newest position j <= t with j = s (mod W), or empty
+            cands = [j for j in range(t + 1) if j % W == s]
+            want = (max(cands) + 1) if cands else 0
+            assert np.all(K[s] == want), (t, s)
+            assert np.all(V[s // 8, :, :, s % 8] == -want), (t, s)
+
+
+def test_batched_append_equals_sequential_appends():
+    W, hkv, d, T = 16, 1, 8, 37
+    g = synthetic.rng(5)
+    k = synthetic.normal_bf16(g, (3, T, hkv, d))
+    v = synthetic.normal_bf16(g, (3, T, hkv, d))
+    pos0 = np.array([0, 5, 1000], np.int32)
+    n_new = np.array([37, 20, 3], np.int32)
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    off = np.arange(3, dtype=np.int64) * rb
+    kp1, vp1 = np.zeros(3 * rb, np.uint8), np.zeros(3 * rb, np.uint8)
+    oracle.kv_append(kp1, vp1, off, off, W, oracle.BF16, 1, 1, k, v, pos0, n_new)
+    kp2, vp2 = np.zeros(3 * rb, np.uint8), np.zeros(3 * rb, np.uint8)
+    for b in range(3):
+        for t in range(n_new[b]):
+            oracle.kv_append(kp2, vp2, off[b:b + 1], off[b:b + 1], W, oracle.BF16, 1, 1,
+                             k[b:b + 1, t:t + 1], v[b:b + 1, t:t + 1], np.array([pos0[b] + t], np.int32))
+    assert np.array_equal(kp1, kp2) and np.array_equal(vp1, vp2)
+
+
+def test_global_mode_slot_is_position_and_bounds():
+    cap, hkv, d = 64, 2, 8
+    rb = oracle.region_bytes(cap, hkv, d, oracle.BF16)
+    kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
+    off = np.zeros(1, np.int64)
+    k, v = position_tokens(10, hkv, d, base=50)
+    oracle.kv_append(kp, vp, off, off, cap, oracle.BF16, 1, 1, k[None], v[None], np.array([50], np.int32),
+                     wrap=False)
+    K = f64(k_view(kp, 0, cap, hkv, d))
+    for s in range(cap):
+        assert np.all(K[s] == (s if 50 <= s < 60 else 0))
+    with pytest.raises(ValueError):  # position 64 would be outside the region
+        oracle.kv_append(kp, vp, off, off, cap, oracle.BF16, 1, 1, k[None], v[None],
+                         np.array([55], np.int32), wrap=False)
+
+
+def test_fp8_append_stores_encoded_codes():
+    W, hkv, d = 16, 2, 32
+    g = synthetic.rng(9)
+    k = synthetic.normal_bf16(g, (1, 5, hkv, d))
+    v = synthetic.normal_bf16(g, (1, 5, hkv, d))
+    ks, vs = 0.0123, 0.0456
+    rb = oracle.region_bytes(W, hkv, d, oracle.FP8)
+    kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
+    off = np.zeros(1, np.int64)
+    oracle.kv_append(kp, vp, off, off, W, oracle.FP8, ks, vs, k, v, np.array([14], np.int32))
+    K = kp.reshape(W, hkv, d)
+    V = vp.reshape(W // 8, hkv, d, 8)
+    for t in range(5):
+        s = (14 + t) % W
+        assert np.array_equal(K[s], oracle.e4m3_encode(k[0, t], ks))
+        assert np.array_equal(V[s // 8, :, :, s % 8], oracle.e4m3_encode(v[0, t], vs))
