@@ -1,0 +1,225 @@
+/*
+ * swr.h -- C ABI of libswr.so: sliding-window ring and grouped-verify
+ * attention for Gemma-4-style decode and speculative verification on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows:
+ *   [Carat] "Announcing Carat: An inference engine designed for Gemma 4"
+ *           - "Replacing page lookups with a ring buffer": each request owns a
+ *             fixed ring; a token's slot is its absolute position modulo the
+ *             window; a new token reuses the oldest slot without moving data.
+ *           - "More FLOPs can be faster": global layers, key_count = context +
+ *             proposals, scores over the keys, causal softmax by query
+ *             position, weighted sum of values; the key dimension padded up
+ *             to a multiple of 64 with a zero-initialised, masked tail.
+ *           - "Doing it all in one kernel can be slower": the query heads that
+ *             share a KV head times the proposed positions form one group of
+ *             rows (8 x 4 = 32) against the same keys and values.
+ *   [Gaudi] "Improving Decode Throughput on Intel Gaudi 3"
+ *           - "Patching sliding window KV allocation": sliding layers keep
+ *             only the last 1024 tokens.
+ *           - "Our approach": rings are carved from the same HBM pool as the
+ *             global-layer KV; K and V are written in lockstep, so the rings
+ *             share one rotation and attention reads them in place.
+ *   [Thor]  "gemma-cuda-hybrid" README, "Features": grouped-query attention
+ *           reading KV once per KV head; FP8 (e4m3) KV cache.
+ *
+ * Conventions for every call below
+ *   - All pointers marked "device" point to GPU memory the caller owns; the
+ *     library allocates no device memory and keeps no state between calls
+ *     (the pool functions keep host-side bookkeeping only).
+ *   - Calls are asynchronous on `stream`; the caller keeps every buffer alive
+ *     until the stream has passed the call.
+ *   - Every call validates its host-side arguments first and, on failure,
+ *     returns an error without touching device memory or launching.  Kernel
+ *     launch failures are reported as SWR_ERR_LAUNCH.  Nothing throws.
+ *   - bf16 means the 16-bit bfloat16 format; fp32 sums; outputs are rounded to
+ *     bf16 with round-to-nearest-even.
+ *   - Values that live in device memory (positions, key counts) cannot be
+ *     checked on the host; the preconditions stated for them are the
+ *     caller's.  Region reads and writes are bounded in hardware to
+ *     `cap` slots, so a broken precondition gives wrong numbers, not a fault.
+ *
+ * KV region layout (one request, one layer; K and V regions separate)
+ *   slot s in [0, cap), KV head g in [0, Hkv), dim d in [0, D):
+ *     K element (s, g, d) at element index (s*Hkv + g)*D + d
+ *     V element (s, g, d) at element index ((s/8)*Hkv + g)*D*8 + d*8 + (s%8)
+ *   Element size: 2 bytes (SWR_KV_BF16) or 1 byte (SWR_KV_FP8_E4M3).
+ *   K rows are token-major so one append writes one row per token; V is kept
+ *   in blocks of 8 slots so that the 8 values of a dim for 8 consecutive slots
+ *   are contiguous, which is the operand shape of the gfx950 bf16 matrix
+ *   instruction along the key axis.  cap is a multiple of 8.  A region is
+ *   cap*Hkv*D*element_size bytes (swr_kv_region_bytes).
+ *   Ring regions: cap = W, slot = position mod W.  Global regions: slot =
+ *   position, and cap >= pad64(key_count) with slots beyond key_count holding
+ *   finite values (the pool's zero fill provides this).
+ */
+#ifndef SWR_H
+#define SWR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swr_status {
+  SWR_OK = 0,
+  SWR_ERR_INVALID = 1,     /* a null pointer, a negative size, an inconsistent shape */
+  SWR_ERR_UNSUPPORTED = 2, /* a shape outside the compiled set (see each call) */
+  SWR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than swr_workspace_bytes() */
+  SWR_ERR_LAUNCH = 4,      /* the HIP runtime reported an error */
+  SWR_ERR_NOMEM = 5        /* the pool has no free range large enough */
+} swr_status;
+
+typedef enum swr_kv_dtype {
+  SWR_KV_BF16 = 0,     /* elements are bf16 */
+  SWR_KV_FP8_E4M3 = 1  /* elements are OCP E4M3FN codes; value = decode(code) * scale */
+} swr_kv_dtype;
+
+typedef enum swr_op {
+  SWR_OP_SWA_DECODE = 0,
+  SWR_OP_GQA_VERIFY = 1,
+  SWR_OP_GLOBAL_ATTEND = 2
+} swr_op;
+
+/* One layer's view of per-request K/V regions inside one or two device
+ * buffers (usually the shared pool: [Gaudi] "Our approach"). */
+typedef struct swr_kv {
+  void* k_base;          /* device: base of the buffer holding K regions */
+  void* v_base;          /* device: base of the buffer holding V regions (may equal k_base) */
+  const int64_t* k_off;  /* device [B]: byte offset of request b's K region from k_base (16-B aligned) */
+  const int64_t* v_off;  /* device [B]: same for V */
+  int32_t cap;           /* slots per region: the window W for rings, the capacity for global regions */
+  int32_t dtype;         /* swr_kv_dtype */
+  float k_scale;         /* fp8 only: per-tensor scale of K (> 0, finite) */
+  float v_scale;         /* fp8 only: per-tensor scale of V (> 0, finite) */
+} swr_kv;
+
+/* ------------------------------------------------------------------ append */
+
+/* Write new tokens' K and V into each request's region ([Carat] ring section;
+ * [Gaudi] "Our approach": K and V of a token go to the same slot).
+ *   k_new, v_new : device bf16 [B][T][Hkv][D] (row-major, 16-B aligned)
+ *   pos0         : device int32 [B], position of token 0 of request b (>= 0)
+ *   n_new        : device int32 [B] tokens to write for request b (0..T), or
+ *                  NULL for T each
+ *   wrap != 0    : ring, slot = position mod cap.  When n_new > cap only the
+ *                  last cap tokens are written, which is what writing them one
+ *                  after another leaves behind.
+ *   wrap == 0    : global region, slot = position (position < cap; larger
+ *                  positions are dropped).
+ *   fp8 regions store the code nearest to value/scale (exact quotient,
+ *   ties to even, saturating at +-448; NaN -> 0x7F with its sign).
+ * Supported: D in {64, 128, 256, 512}; T >= 1; B >= 0 (B == 0 is a no-op). */
+swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
+                         const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv, int D,
+                         int wrap, hipStream_t stream);
+
+/* -------------------------------------------------------- sliding decode */
+
+/* Sliding-window GQA decode, one query token per request ([Carat] ring
+ * section; [Gaudi] "Our approach": the ring is read in place, no gather, no
+ * un-rotation).  The query at pos[b] sees the keys at positions
+ * max(0, pos-W+1) .. pos, all of which are in the ring (its own token was
+ * appended first), i.e. ring slots 0 .. min(pos+1, W)-1 in any rotation.
+ *   ring  : ring regions, ring->cap = W
+ *   q     : device bf16 [B][Hq][D]; query head h reads KV head h / (Hq/Hkv)
+ *   out   : device bf16 [B][Hq][D]
+ *   pos   : device int32 [B], >= 0
+ *   scale : multiplies q.k before the softmax (e.g. 1/sqrt(D))
+ *   ws    : device workspace of ws_bytes >= swr_workspace_bytes(SWR_OP_SWA_DECODE, B, 1, Hq,
+ *           Hkv, D, W) (may be NULL when that is 0)
+ * Supported: D in {64, 128, 256, 512}; Hq/Hkv in 1..16. */
+swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const int32_t* pos, int B,
+                          int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------- sliding verify */
+
+/* Speculative verification on a sliding layer ([Carat] "Doing it all in one
+ * kernel can be slower": G query heads x S proposed positions per KV head).
+ * The ring holds committed positions < pos0[b]; the S proposals are passed
+ * separately so that none of the keys the first rows still need is evicted.
+ * Row (i, h) at position pos0+i sees ring keys with position >= pos0+i-W+1
+ * and proposals 0..i.  After acceptance the caller appends the accepted
+ * prefix with swr_kv_append.
+ *   k_prop, v_prop : device bf16 [B][S][Hkv][D]
+ *   q, out         : device bf16 [B][S][Hq][D]
+ *   pos0           : device int32 [B], >= 0
+ *   ws             : >= swr_workspace_bytes(SWR_OP_GQA_VERIFY, B, S, Hq, Hkv, D, W)
+ * Supported: D in {64, 128, 256, 512}; 1 <= S <= 8; (Hq/Hkv)*S <= 32. */
+swr_status swr_gqa_verify(const swr_kv* ring, const void* k_prop, const void* v_prop,
+                          const void* q, void* out, const int32_t* pos0, int B, int S, int Hq,
+                          int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------- global layers */
+
+/* Global-layer grouped attention over contiguous regions ([Carat] "More FLOPs
+ * can be faster" and "Doing it all in one kernel can be slower").  Keys
+ * 0 .. key_count[b]-1 are in the region (proposals appended first, so
+ * key_count = context + proposals); the contraction runs over
+ * pad64(key_count) keys whose tail is masked; row (i, h) sees keys
+ * j <= q_pos[b][i] (and j < key_count[b]).
+ *   kv            : global regions; each holds >= pad64(key_count[b]) slots
+ *   q, out        : device bf16 [B][S][Hq][D]
+ *   q_pos         : device int32 [B][S]
+ *   key_count     : device int32 [B], 1 <= key_count[b] <= max_key_count
+ *   max_key_count : host bound on key_count, sizes the launch and workspace
+ *   ws            : >= swr_workspace_bytes(SWR_OP_GLOBAL_ATTEND, B, S, Hq, Hkv, D, max_key_count)
+ * Supported: D in {64, 128, 256, 512}; 1 <= S <= 8; (Hq/Hkv)*S <= 32. */
+swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const int32_t* q_pos,
+                             const int32_t* key_count, int max_key_count, int B, int S, int Hq,
+                             int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Workspace bytes an attention call needs (0 when it needs none).  For
+ * decode and verify `cap_or_max_keys` is the window W; for global attention it
+ * is max_key_count.  Returns 0 for unsupported shapes as well (the call then
+ * reports the shape error).  The workspace holds per-split partial results
+ * (running maximum, weight sum and unnormalised output rows, fp32). */
+size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap_or_max_keys);
+
+/* ------------------------------------------------------------ the pool */
+
+/* Host-side carve of one device buffer into K/V regions ([Gaudi] "Our
+ * approach": rings and global KV share one HBM pool).  The pool only keeps
+ * byte ranges; it never touches device memory.  First fit, 256-byte aligned
+ * ranges.  Thread-safe. */
+typedef struct swr_pool swr_pool;
+
+/* Bytes of one K (or V) region of `cap` slots (-1 if the shape is invalid). */
+int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype);
+
+swr_status swr_pool_create(size_t bytes, swr_pool** pool);
+void swr_pool_destroy(swr_pool* pool);
+/* Reserve `bytes` (> 0); *offset receives its 256-B aligned start. */
+swr_status swr_pool_alloc(swr_pool* pool, size_t bytes, int64_t* offset);
+/* Release a range returned by swr_pool_alloc (SWR_ERR_INVALID if unknown). */
+swr_status swr_pool_free(swr_pool* pool, int64_t offset);
+/* Reserve a K region and a V region for `tokens` tokens of one layer.
+ * global == 0: a ring, cap = tokens rounded up to a multiple of 8.
+ * global != 0: a contiguous region, cap = tokens rounded up to a multiple of
+ * 64 ([Carat] "More FLOPs can be faster": the padded tail).  The caller zero
+ * fills the two ranges on its stream (swr_zero_fill) before first use. */
+swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dtype, int global,
+                             int64_t* k_offset, int64_t* v_offset, int32_t* cap);
+/* Bytes in use and the largest free range. */
+swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_free);
+
+/* Zero `bytes` of device memory at `ptr` with a kernel on `stream` (no
+ * memset node, so it may be captured into a graph). */
+swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char* swr_status_string(swr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWR_H */

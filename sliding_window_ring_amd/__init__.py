@@ -1,0 +1,271 @@
+"""Python binding of libswr.so (include/swr.h): sliding-window ring and
+grouped-verify attention on MI355X (gfx950).
+
+This module only marshals arguments: torch tensors supply device memory and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  If libswr.so has not been built, importing this package raises
+ImportError (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswr.so")
+
+SWR_KV_BF16 = 0
+SWR_KV_FP8_E4M3 = 1
+SWR_OP_SWA_DECODE = 0
+SWR_OP_GQA_VERIFY = 1
+SWR_OP_GLOBAL_ATTEND = 2
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
+          4: "HIP launch error", 5: "pool exhausted"}
+
+EXPORTS = [
+    "swr_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend", "swr_workspace_bytes",
+    "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
+    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_status_string",
+]
+
+
+class SwrKV(ctypes.Structure):
+    """Mirror of `swr_kv` in include/swr.h."""
+    _fields_ = [
+        ("k_base", ctypes.c_void_p), ("v_base", ctypes.c_void_p),
+        ("k_off", ctypes.c_void_p), ("v_off", ctypes.c_void_p),
+        ("cap", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+    ]
+
+
+class SwrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python sliding_window_ring_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    KV = ctypes.POINTER(SwrKV)
+    sig = {
+        "swr_kv_append": ([KV, P, P, P, P, I, I, I, I, I, P], I),
+        "swr_swa_decode": ([KV, P, P, P, I, I, I, I, F, P, SZ, P], I),
+        "swr_gqa_verify": ([KV, P, P, P, P, P, I, I, I, I, I, F, P, SZ, P], I),
+        "swr_global_attend": ([KV, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
+        "swr_workspace_bytes": ([I, I, I, I, I, I, I], SZ),
+        "swr_kv_region_bytes": ([I, I, I, I], I64),
+        "swr_pool_create": ([SZ, ctypes.POINTER(P)], I),
+        "swr_pool_destroy": ([P], None),
+        "swr_pool_alloc": ([P, SZ, ctypes.POINTER(I64)], I),
+        "swr_pool_free": ([P, I64], I),
+        "swr_pool_alloc_kv": ([P, I, I, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                               ctypes.POINTER(ctypes.c_int32)], I),
+        "swr_pool_stats": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I),
+        "swr_zero_fill": ([P, SZ, P], I),
+        "swr_status_string": ([I], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SwrError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+@dataclass
+class KVLayer:
+    """One layer's K/V regions: per-request byte offsets into base buffers
+    (usually one shared pool tensor).  Mirrors `swr_kv`."""
+    k_base: torch.Tensor          # device uint8 buffer holding the K regions
+    v_base: torch.Tensor          # device uint8 buffer holding the V regions
+    k_off: torch.Tensor           # device int64 [B]
+    v_off: torch.Tensor           # device int64 [B]
+    cap: int                      # slots per region (ring: W)
+    dtype: int = SWR_KV_BF16
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    _c: SwrKV = field(default=None, repr=False)
+
+    def c(self) -> SwrKV:
+        _dev(self.k_off, "k_off", torch.int64)
+        _dev(self.v_off, "v_off", torch.int64)
+        self._c = SwrKV(self.k_base.data_ptr(), self.v_base.data_ptr(), self.k_off.data_ptr(),
+                        self.v_off.data_ptr(), self.cap, self.dtype, self.k_scale, self.v_scale)
+        return self._c
+
+
+def region_bytes(cap: int, hkv: int, d: int, dtype: int = SWR_KV_BF16) -> int:
+    n = lib.swr_kv_region_bytes(cap, hkv, d, dtype)
+    if n < 0:
+        raise ValueError("invalid region shape")
+    return int(n)
+
+
+def workspace_bytes(op: int, B: int, S: int, Hq: int, Hkv: int, D: int, cap_or_max_keys: int) -> int:
+    return int(lib.swr_workspace_bytes(op, B, S, Hq, Hkv, D, cap_or_max_keys))
+
+
+def _workspace(op, B, S, Hq, Hkv, D, n, ws, device):
+    need = workspace_bytes(op, B, S, Hq, Hkv, D, n)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def kv_append(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch.Tensor,
+              n_new: Optional[torch.Tensor] = None, wrap: bool = True, stream=None) -> None:
+    """swr_kv_append: k_new, v_new bf16 [B][T][Hkv][D]; pos0 (and n_new) int32 [B]."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(pos0, "pos0", torch.int32)
+    if n_new is not None:
+        _dev(n_new, "n_new", torch.int32)
+    B, T, hkv, d = k_new.shape
+    _check("swr_kv_append", lib.swr_kv_append(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(pos0),
+                                              _ptr(n_new), B, T, hkv, d, 1 if wrap else 0,
+                                              _stream(stream)))
+
+
+def swa_decode(ring: KVLayer, q: torch.Tensor, pos: torch.Tensor, hkv: int, scale: float,
+               out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """swr_swa_decode: q bf16 [B][Hq][D]; pos int32 [B] -> out bf16 [B][Hq][D]."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(pos, "pos", torch.int32)
+    B, hq, d = q.shape
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    ws, wsb = _workspace(SWR_OP_SWA_DECODE, B, 1, hq, hkv, d, ring.cap, ws, q.device)
+    _check("swr_swa_decode", lib.swr_swa_decode(ctypes.byref(ring.c()), _ptr(q), _ptr(out), _ptr(pos), B,
+                                                hq, hkv, d, scale, _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def gqa_verify(ring: KVLayer, k_prop: torch.Tensor, v_prop: torch.Tensor, q: torch.Tensor,
+               pos0: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """swr_gqa_verify: q bf16 [B][S][Hq][D], k_prop/v_prop bf16 [B][S][Hkv][D],
+    pos0 int32 [B] -> out bf16 [B][S][Hq][D]."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_prop, "k_prop", torch.bfloat16)
+    _dev(v_prop, "v_prop", torch.bfloat16)
+    _dev(pos0, "pos0", torch.int32)
+    B, S, hq, d = q.shape
+    hkv = k_prop.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    ws, wsb = _workspace(SWR_OP_GQA_VERIFY, B, S, hq, hkv, d, ring.cap, ws, q.device)
+    _check("swr_gqa_verify", lib.swr_gqa_verify(ctypes.byref(ring.c()), _ptr(k_prop), _ptr(v_prop), _ptr(q),
+                                                _ptr(out), _ptr(pos0), B, S, hq, hkv, d, scale, _ptr(ws),
+                                                wsb, _stream(stream)))
+    return out
+
+
+def global_attend(kv: KVLayer, q: torch.Tensor, q_pos: torch.Tensor, key_count: torch.Tensor,
+                  max_key_count: int, hkv: int, scale: float, out: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """swr_global_attend: q bf16 [B][S][Hq][D], q_pos int32 [B][S], key_count
+    int32 [B] -> out bf16 [B][S][Hq][D]."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(q_pos, "q_pos", torch.int32)
+    _dev(key_count, "key_count", torch.int32)
+    B, S, hq, d = q.shape
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    ws, wsb = _workspace(SWR_OP_GLOBAL_ATTEND, B, S, hq, hkv, d, max_key_count, ws, q.device)
+    _check("swr_global_attend", lib.swr_global_attend(ctypes.byref(kv.c()), _ptr(q), _ptr(out), _ptr(q_pos),
+                                                      _ptr(key_count), max_key_count, B, S, hq, hkv, d, scale,
+                                                      _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def zero_fill(t: torch.Tensor, offset: int = 0, nbytes: Optional[int] = None, stream=None) -> None:
+    """swr_zero_fill over bytes [offset, offset+nbytes) of a device tensor."""
+    _dev(t, "t")
+    total = t.numel() * t.element_size()
+    nbytes = total - offset if nbytes is None else nbytes
+    if offset < 0 or offset + nbytes > total:
+        raise ValueError("range outside the tensor")
+    _check("swr_zero_fill", lib.swr_zero_fill(ctypes.c_void_p(t.data_ptr() + offset), nbytes, _stream(stream)))
+
+
+class Pool:
+    """Host bookkeeping (swr_pool_*) over one device byte buffer shared by
+    ring and global regions ("Improving Decode Throughput on Intel Gaudi 3",
+    Our approach)."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        _check("swr_pool_create", lib.swr_pool_create(nbytes, ctypes.byref(h)))
+        self._h = h
+
+    def alloc(self, nbytes: int) -> int:
+        off = ctypes.c_int64()
+        _check("swr_pool_alloc", lib.swr_pool_alloc(self._h, nbytes, ctypes.byref(off)))
+        return off.value
+
+    def free(self, offset: int) -> None:
+        _check("swr_pool_free", lib.swr_pool_free(self._h, offset))
+
+    def alloc_kv(self, tokens: int, hkv: int, d: int, dtype: int = SWR_KV_BF16, global_layer: bool = False,
+                 zero: bool = True, stream=None):
+        """Reserve a K and a V region; zero-fills both on the stream.
+        Returns (k_offset, v_offset, cap)."""
+        ko, vo, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check("swr_pool_alloc_kv", lib.swr_pool_alloc_kv(self._h, tokens, hkv, d, dtype, 1 if global_layer else 0,
+                                                          ctypes.byref(ko), ctypes.byref(vo), ctypes.byref(cap)))
+        if zero:
+            rb = region_bytes(cap.value, hkv, d, dtype)
+            zero_fill(self.buffer, ko.value, rb, stream)
+            zero_fill(self.buffer, vo.value, rb, stream)
+        return ko.value, vo.value, cap.value
+
+    def stats(self):
+        used, largest = ctypes.c_size_t(), ctypes.c_size_t()
+        _check("swr_pool_stats", lib.swr_pool_stats(self._h, ctypes.byref(used), ctypes.byref(largest)))
+        return used.value, largest.value
+
+    def close(self):
+        if self._h:
+            lib.swr_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

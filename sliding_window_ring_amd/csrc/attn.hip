@@ -1,0 +1,559 @@
+// attn.hip -- grouped-query attention over per-request K/V regions on gfx950.
+//
+// One kernel template serves the three attention entry points:
+//   decode  : one query token per request over its sliding-window ring
+//             ("Announcing Carat", ring buffer section; "Improving Decode
+//             Throughput on Intel Gaudi 3", Our approach: the ring is read in
+//             place, in storage order, with no gather and no un-rotation);
+//   verify  : G heads x S proposals per KV head over the ring plus the
+//             proposals ("Announcing Carat", Doing it all in one kernel can be
+//             slower: the grouped rows share one K/V stream);
+//   global  : the same grouped rows over a contiguous region padded to a
+//             multiple of 64 keys with a masked tail ("Announcing Carat",
+//             More FLOPs can be faster).
+//
+// Work unit: one (request, KV head).  A workgroup takes a range of 32-key
+// tiles of one unit (split-K across workgroups when the batch is small); its
+// waves split the tiles (kw) and/or the head dimension (ds).  Per tile, per
+// wave:
+//   scores  = K(32 keys x ds) . Q^T(ds x rows)    bf16 MFMA 16x16x32, fp32
+//   (waves sharing a tile add their ds-partial scores through LDS)
+//   online softmax in the base-2 domain, per row, in fp32
+//   O^T    += V^T(ds x 32 keys) . P^T(32 keys x rows)   bf16 MFMA, fp32
+// Keys are laid out on the MFMA k axis so that the score fragment a lane
+// holds (row l%16, keys 8*(l/16)+0..7) is exactly the P^T fragment it must
+// supply, and the V^T fragment is one 16-byte load from the 8-slot V blocks
+// of the region layout.  No shuffles sit between the two contractions.
+#include <algorithm>
+
+#include "swr_device.h"
+#include "swr_internal.h"
+
+namespace swr {
+
+template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
+__global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnParams p) {
+  constexpr int DSPLIT = D / DS;
+  constexpr int NCH = DS / 32;  // QK k-chunks of 32 dims
+  constexpr int NDT = DS / 16;  // PV tiles of 16 dims
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr int RED = 2 * NCT * 4;  // score floats per lane per tile
+  constexpr int RS = D + 4;         // padded LDS row stride (floats)
+  extern __shared__ float smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ds = wave % DSPLIT;
+  const int kw = wave / DSPLIT;
+  const int lr = lane & 15;  // row within a 16-row column tile; also key row of the K operand
+  const int lq = lane >> 4;  // lane group: which 8 keys / 8 dims of the k axis
+
+  const int unit = blockIdx.x / p.nsplit;
+  const int split = blockIdx.x - unit * p.nsplit;
+  const int Hkv = p.Hkv, G = p.G, S = p.S;
+  const int b = unit / Hkv;
+  const int g = unit - b * Hkv;
+  const int d_base = ds * DS;
+
+  // ---------------------------------------------------------------- keys
+  int n_keys;      // valid region keys (ring: slots ever written; global: key_count)
+  int ring_head = 0;  // verify: slot of the newest committed position
+  if (MODE == MODE_DECODE) {
+    n_keys = min(p.pos[b] + 1, p.cap);
+  } else if (MODE == MODE_VERIFY) {
+    const int p0 = p.pos[b];
+    n_keys = min(p0, p.cap);
+    ring_head = p0 > 0 ? (p0 - 1) % p.cap : 0;
+  } else {
+    n_keys = min(p.key_count[b], p.cap);
+  }
+  n_keys = max(n_keys, 0);
+  const int nt_region = (n_keys + 31) >> 5;
+  const int nt_total = nt_region + (MODE == MODE_VERIFY ? 1 : 0);
+  const int t_begin = split * p.tiles_per_split;
+  const int t_end = min(nt_total, t_begin + p.tiles_per_split);
+  if (t_begin >= t_end) return;  // empty split: the combine step skips it
+  const int n_it = (t_end - t_begin + KW - 1) / KW;
+
+  // ---------------------------------------------------------------- rows
+  // Row r = i*G + h: proposal i, head h of the group (query head g*G + h).
+  bool row_ok[NCT];
+  int row_i[NCT];
+  int row_lim[NCT];  // verify: largest slot age still in the window; global: last visible key
+  bf16x8 qop[NCT][NCH];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int row = ct * 16 + lr;
+    row_ok[ct] = row < p.rows;
+    const int i = row_ok[ct] ? row / G : 0;
+    const int h = row_ok[ct] ? row - i * G : 0;
+    row_i[ct] = i;
+    if (MODE == MODE_VERIFY) row_lim[ct] = p.cap - 2 - i;
+    if (MODE == MODE_GLOBAL) row_lim[ct] = min(p.pos[b * S + i], n_keys - 1);
+    const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (row_ok[ct])
+        qop[ct][c] = *reinterpret_cast<const bf16x8*>(qrow + (4 * c + lq) * 8);
+      else
+        qop[ct][c] = bf16x8{};
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], p.region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], p.region_bytes);
+
+  f32x4 o[NCT][NDT];
+  float m_run[NCT], l_run[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int it = 0; it < n_it; ++it) {
+    const int t = t_begin + kw + it * KW;
+    if (t >= t_end) {  // wave-uniform; keeps the barrier count equal across waves
+      if (DSPLIT > 1) __syncthreads();
+      continue;
+    }
+    const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
+    const int kb = t * 32;
+
+    // ------------------------------------------------ scores = K . Q^T
+    f32x4 sc[2][NCT];
+    {
+      bf16x8 kop[2][NCH];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        // A row lr of sub-tile `sub` holds key 8*(lr/4) + 4*sub + lr%4, so the
+        // C rows lane group lq receives are keys 8*lq + 4*sub + 0..3.
+        const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
+        if (!prop_tile) {
+          const uint32_t base = ((uint32_t)((kb + e) * Hkv + g) * D + d_base) * ESZ;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const uint32_t off = base + (uint32_t)((4 * c + lq) * 8 * ESZ);
+            if (FP8)
+              kop[sub][c] = fp8x8_to_bf16x8(load8(rk, off));
+            else
+              kop[sub][c] = as_bf16x8(load16(rk, off));
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) kop[sub][c] = bf16x8{};
+          if (e < S) {
+            const uint16_t* src = p.k_prop + ((size_t)(b * S + e) * Hkv + g) * D + d_base;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) kop[sub][c] = *reinterpret_cast<const bf16x8*>(src + (4 * c + lq) * 8);
+          }
+        }
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
+          sc[sub][ct] = acc;
+        }
+    }
+
+    if (DSPLIT > 1) {  // add the head-dim slices of the scores, in slice order
+      float* buf = smem + (size_t)((it & 1) * KW + kw) * DSPLIT * RED * 64;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) buf[(ds * RED + (sub * NCT + ct) * 4 + r) * 64 + lane] = sc[sub][ct][r];
+      __syncthreads();
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < DSPLIT; ++s2) a += buf[(s2 * RED + (sub * NCT + ct) * 4 + r) * 64 + lane];
+            sc[sub][ct][r] = a;
+          }
+    }
+
+    // ------------------------------------------------ masked online softmax
+    bf16x8 pop[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float s[8];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * sub + r;     // element of the P^T fragment
+          const int key = kb + 8 * lq + e;
+          bool vis;
+          if (MODE == MODE_DECODE) {
+            vis = key < n_keys;
+          } else if (MODE == MODE_VERIFY) {
+            if (prop_tile) {
+              const int pi = 8 * lq + e;  // proposal index
+              vis = pi < S && pi <= row_i[ct];
+            } else {
+              int age = ring_head - key;  // positions back from the newest committed one
+              if (age < 0) age += p.cap;
+              vis = key < n_keys && age <= row_lim[ct];
+            }
+          } else {
+            vis = key <= row_lim[ct];
+          }
+          vis = vis && row_ok[ct];
+          s[e] = vis ? sc[sub][ct][r] * p.qk_scale : -INFINITY;
+        }
+      float tmax = s[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
+      tmax = max4lanes(tmax);
+      const float m_new = fmaxf(m_run[ct], tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[ct] - m_use);
+      float psum = 0.f;
+      bf16x8 pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 pb = (__bf16)fast_exp2(s[e] - m_use);
+        pv[e] = pb;
+        psum += (float)pb;  // the weights the PV product actually uses
+      }
+      pop[ct] = pv;
+      l_run[ct] = l_run[ct] * alpha + psum;
+      m_run[ct] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[ct][dt] *= alpha;
+    }
+
+    // ------------------------------------------------ O^T += V^T . P^T
+    {
+      bf16x8 vop[NDT];
+      if (!prop_tile) {
+        const uint32_t vbase =
+            ((uint32_t)((((kb >> 3) + lq) * Hkv + g) * D + d_base + lr)) * 8 * ESZ;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t off = vbase + (uint32_t)(dt * 16 * 8 * ESZ);
+          if (FP8)
+            vop[dt] = fp8x8_to_bf16x8(load8(rv, off));
+          else
+            vop[dt] = as_bf16x8(load16(rv, off));
+        }
+        if (kb + 32 > n_keys) {  // last region tile: zero values of keys past the valid range
+          u32x4 keep;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k0 = kb + 8 * lq + 2 * j;
+            keep[j] = (k0 < n_keys ? 0x0000FFFFu : 0u) | (k0 + 1 < n_keys ? 0xFFFF0000u : 0u);
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            vop[dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[dt]) & keep);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = d_base + 16 * dt + lr;
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int pi = 8 * lq + e;
+            uint16_t bits = 0;
+            if (pi < S) bits = p.v_prop[((size_t)(b * S + pi) * Hkv + g) * D + d];
+            v[e] = __builtin_bit_cast(__bf16, bits);
+          }
+          vop[dt] = v;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[dt], pop[ct], o[ct][dt]);
+    }
+  }
+
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) l_run[ct] = sum4lanes(l_run[ct]);
+
+  const size_t part = (size_t)unit * p.nsplit + split;
+  if (KW == 1) {
+    // This wave holds rows ct*16+lr, dims d_base + 16*dt + 4*lq + 0..3.
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int row = ct * 16 + lr;
+      if (!row_ok[ct]) continue;
+      const int i = row / G, h = row - (row / G) * G;
+      if (p.nsplit == 1) {
+        const float inv = l_run[ct] > 0.f ? p.v_scale / l_run[ct] : 0.f;
+        uint16_t* dst = p.out + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base + 4 * lq;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          bf16x4 w = {(__bf16)(o[ct][dt][0] * inv), (__bf16)(o[ct][dt][1] * inv),
+                      (__bf16)(o[ct][dt][2] * inv), (__bf16)(o[ct][dt][3] * inv)};
+          *reinterpret_cast<bf16x4*>(dst + 16 * dt) = w;
+        }
+      } else {
+        float* dst = p.ws_acc + (part * p.rows + row) * D + d_base + 4 * lq;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[ct][dt];
+        if (ds == 0 && lq == 0) {
+          p.ws_ml[(part * p.rows + row) * 2 + 0] = m_run[ct];
+          p.ws_ml[(part * p.rows + row) * 2 + 1] = l_run[ct];
+        }
+      }
+    }
+  } else {
+    // Merge the KW key-split waves through LDS, in wave order.
+    if (DSPLIT > 1) __syncthreads();  // the score buffer aliases this space
+    float* cml = smem;                         // [KW][rows][2]
+    float* co = smem + KW * p.rows * 2;        // [KW][rows][RS]
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int row = ct * 16 + lr;
+      if (!row_ok[ct]) continue;
+      if (ds == 0 && lq == 0) {
+        cml[(kw * p.rows + row) * 2 + 0] = m_run[ct];
+        cml[(kw * p.rows + row) * 2 + 1] = l_run[ct];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(co + (size_t)(kw * p.rows + row) * RS + d_base + 16 * dt + 4 * lq) =
+            o[ct][dt];
+    }
+    __syncthreads();
+    const int nchunk = p.rows * (D / 4);
+    for (int idx = threadIdx.x; idx < nchunk; idx += blockDim.x) {
+      const int row = idx / (D / 4);
+      const int d4 = (idx - row * (D / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) M = fmaxf(M, cml[(k * p.rows + row) * 2]);
+      const float M_use = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f;
+      f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const float w = fast_exp2(cml[(k * p.rows + row) * 2] - M_use);
+        L += cml[(k * p.rows + row) * 2 + 1] * w;
+        O += *reinterpret_cast<const f32x4*>(co + (size_t)(k * p.rows + row) * RS + d4) * w;
+      }
+      const int i = row / G, h = row - (row / G) * G;
+      if (p.nsplit == 1) {
+        const float inv = L > 0.f ? p.v_scale / L : 0.f;
+        bf16x4 w = {(__bf16)(O[0] * inv), (__bf16)(O[1] * inv), (__bf16)(O[2] * inv), (__bf16)(O[3] * inv)};
+        *reinterpret_cast<bf16x4*>(p.out + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d4) = w;
+      } else {
+        *reinterpret_cast<f32x4*>(p.ws_acc + (part * p.rows + row) * D + d4) = O;
+        if (d4 == 0) {
+          p.ws_ml[(part * p.rows + row) * 2 + 0] = M;
+          p.ws_ml[(part * p.rows + row) * 2 + 1] = L;
+        }
+      }
+    }
+  }
+}
+
+// Split-K merge: out = v_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// over the non-empty splits of each (request, KV head).  One thread per four
+// output dims of one row.
+template <int MODE>
+__global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D, int units) {
+  const int per_row = D / 4;
+  const int per_unit = p.rows * per_row;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= units * per_unit) return;
+  const int unit = idx / per_unit;
+  const int rem = idx - unit * per_unit;
+  const int row = rem / per_row;
+  const int d4 = (rem - row * per_row) * 4;
+  const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+
+  int n_keys;
+  if (MODE == MODE_DECODE)
+    n_keys = min(p.pos[b] + 1, p.cap);
+  else if (MODE == MODE_VERIFY)
+    n_keys = min(p.pos[b], p.cap);
+  else
+    n_keys = min(p.key_count[b], p.cap);
+  n_keys = max(n_keys, 0);
+  const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
+  const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
+
+  const size_t base = (size_t)unit * p.nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, p.ws_ml[((base + s) * p.rows + row) * 2]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nvalid; ++s) {
+    const float w = fast_exp2(p.ws_ml[((base + s) * p.rows + row) * 2] - M_use);
+    L += p.ws_ml[((base + s) * p.rows + row) * 2 + 1] * w;
+    O += *reinterpret_cast<const f32x4*>(p.ws_acc + ((base + s) * p.rows + row) * D + d4) * w;
+  }
+  const float inv = L > 0.f ? p.v_scale / L : 0.f;
+  const int i = row / p.G, h = row - (row / p.G) * p.G;
+  bf16x4 w = {(__bf16)(O[0] * inv), (__bf16)(O[1] * inv), (__bf16)(O[2] * inv), (__bf16)(O[3] * inv)};
+  *reinterpret_cast<bf16x4*>(p.out + ((size_t)(b * p.S + i) * p.Hq + g * p.G + h) * D + d4) = w;
+}
+
+// ------------------------------------------------------------------ host
+
+namespace {
+
+struct Shape {
+  int ds, kw;
+};
+
+// Waves per workgroup: D/ds share each key tile, kw split the tiles.
+Shape pick_shape(int mode, int D, int nct) {
+  if (mode == MODE_DECODE) {
+    switch (D) {
+      case 64: return {64, 4};
+      case 128: return {128, 4};
+      case 256: return {256, 4};
+      case 512: return {256, 2};
+    }
+  } else if (nct == 1) {
+    switch (D) {
+      case 64: return {64, 1};
+      case 128: return {128, 1};
+      case 256: return {256, 1};
+      case 512: return {256, 1};
+    }
+  } else {
+    switch (D) {
+      case 64: return {64, 1};
+      case 128: return {128, 1};
+      case 256: return {128, 1};
+      case 512: return {128, 1};
+    }
+  }
+  return {0, 0};
+}
+
+constexpr int kNumCU = 256;
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+template <int D, int DS, int NCT, int KW, int MODE>
+hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  if (pl.fp8)
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE>), dim3(pl.units * pl.nsplit),
+                       dim3(pl.threads), pl.lds_bytes, s, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, false, MODE>), dim3(pl.units * pl.nsplit),
+                       dim3(pl.threads), pl.lds_bytes, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  if (MODE == MODE_DECODE) {
+    switch (pl.D) {
+      case 64: return launch_fixed<64, 64, 1, 4, MODE>(pl, p, s);
+      case 128: return launch_fixed<128, 128, 1, 4, MODE>(pl, p, s);
+      case 256: return launch_fixed<256, 256, 1, 4, MODE>(pl, p, s);
+      case 512: return launch_fixed<512, 256, 1, 2, MODE>(pl, p, s);
+    }
+  } else if (pl.nct == 1) {
+    switch (pl.D) {
+      case 64: return launch_fixed<64, 64, 1, 1, MODE>(pl, p, s);
+      case 128: return launch_fixed<128, 128, 1, 1, MODE>(pl, p, s);
+      case 256: return launch_fixed<256, 256, 1, 1, MODE>(pl, p, s);
+      case 512: return launch_fixed<512, 256, 1, 1, MODE>(pl, p, s);
+    }
+  } else {
+    switch (pl.D) {
+      case 64: return launch_fixed<64, 64, 2, 1, MODE>(pl, p, s);
+      case 128: return launch_fixed<128, 128, 2, 1, MODE>(pl, p, s);
+      case 256: return launch_fixed<256, 128, 2, 1, MODE>(pl, p, s);
+      case 512: return launch_fixed<512, 128, 2, 1, MODE>(pl, p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
+                    AttnPlan* pl) {
+  if (B < 0 || S < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || cap_or_max_keys < 1) return false;
+  if (D != 64 && D != 128 && D != 256 && D != 512) return false;
+  const int G = Hq / Hkv;
+  const int rows = G * S;
+  if (mode == MODE_DECODE) {
+    if (S != 1 || G > 16) return false;
+  } else {
+    if (S > 8 || rows > 32) return false;
+  }
+  const int nct = rows > 16 ? 2 : 1;
+  const Shape sh = pick_shape(mode, D, nct);
+  if (sh.ds == 0) return false;
+  pl->mode = mode;
+  pl->D = D;
+  pl->fp8 = fp8 ? 1 : 0;
+  pl->ds = sh.ds;
+  pl->nct = nct;
+  pl->kw = sh.kw;
+  pl->units = B * Hkv;
+  pl->rows = rows;
+  pl->threads = 64 * (D / sh.ds) * sh.kw;
+  pl->max_tiles = ceil_div(cap_or_max_keys, 32) + (mode == MODE_VERIFY ? 1 : 0);
+
+  // Split-K across workgroups only when the units alone do not fill the chip.
+  int tps = pl->max_tiles;
+  if (pl->units > 0 && pl->units < kNumCU) {
+    if (mode == MODE_DECODE)
+      tps = std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU));
+    else
+      tps = std::max(4, ceil_div((long)pl->max_tiles * pl->units, 4 * kNumCU));
+    tps = std::min(tps, pl->max_tiles);
+  }
+  pl->tiles_per_split = std::max(tps, 1);
+  pl->nsplit = ceil_div(pl->max_tiles, pl->tiles_per_split);
+  pl->ws_bytes =
+      pl->nsplit > 1 ? (size_t)pl->units * pl->nsplit * rows * (size_t)(D + 2) * sizeof(float) + 256 : 0;
+
+  size_t red = (D / sh.ds) > 1 ? (size_t)2 * sh.kw * (D / sh.ds) * (2 * nct * 4) * 64 * sizeof(float) : 0;
+  size_t comb = sh.kw > 1 ? (size_t)sh.kw * rows * (2 + D + 4) * sizeof(float) : 0;
+  pl->lds_bytes = std::max(red, comb);
+  return true;
+}
+
+hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  if (pl.units == 0) return hipSuccess;
+  hipError_t e;
+  switch (pl.mode) {
+    case MODE_DECODE: e = launch_mode<MODE_DECODE>(pl, p, s); break;
+    case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
+    case MODE_GLOBAL: e = launch_mode<MODE_GLOBAL>(pl, p, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || pl.nsplit == 1) return e;
+  const long total = (long)pl.units * pl.rows * (pl.D / 4);
+  const int blocks = ceil_div(total, 256);
+  switch (pl.mode) {
+    case MODE_DECODE:
+      hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+      break;
+    case MODE_VERIFY:
+      hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+      break;
+    default:
+      hipLaunchKernelGGL(combine_kernel<MODE_GLOBAL>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swr

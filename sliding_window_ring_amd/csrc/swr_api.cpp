@@ -1,0 +1,304 @@
+// swr_api.cpp -- the C ABI declared in include/swr.h: host-side argument
+// validation, launch planning, and the host bookkeeping of the shared KV pool.
+// Every check runs before any HIP call, so an invalid call never touches
+// device memory.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <new>
+
+#include "swr.h"
+#include "swr_internal.h"
+
+using swr::AttnParams;
+using swr::AttnPlan;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+int elem_size(int dtype) { return dtype == SWR_KV_FP8_E4M3 ? 1 : 2; }
+
+// Checks the fields of a KV view that every call shares.
+swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
+  if (!kv || !kv->k_base || !kv->v_base || !kv->k_off || !kv->v_off) return SWR_ERR_INVALID;
+  if (!aligned16(kv->k_base) || !aligned16(kv->v_base)) return SWR_ERR_INVALID;
+  if (kv->cap <= 0 || kv->cap % 8 != 0) return SWR_ERR_INVALID;
+  if (kv->dtype != SWR_KV_BF16 && kv->dtype != SWR_KV_FP8_E4M3) return SWR_ERR_INVALID;
+  if (kv->dtype == SWR_KV_FP8_E4M3) {
+    if (!(kv->k_scale > 0.f) || !std::isfinite(kv->k_scale)) return SWR_ERR_INVALID;
+    if (!(kv->v_scale > 0.f) || !std::isfinite(kv->v_scale)) return SWR_ERR_INVALID;
+  }
+  const double bytes = (double)kv->cap * Hkv * D * elem_size(kv->dtype);
+  if (bytes > 4294967295.0) return SWR_ERR_UNSUPPORTED;  // regions are addressed with 32-bit offsets
+  return SWR_OK;
+}
+
+uint32_t region_bytes(const swr_kv* kv, int Hkv, int D) {
+  return (uint32_t)((uint64_t)kv->cap * Hkv * D * elem_size(kv->dtype));
+}
+
+swr_status to_status(hipError_t e) { return e == hipSuccess ? SWR_OK : SWR_ERR_LAUNCH; }
+
+// Shared validation and launch of the three attention calls.
+swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const int32_t* pos,
+                  const int32_t* key_count, const void* k_prop, const void* v_prop,
+                  int cap_or_max_keys, int B, int S, int Hq, int Hkv, int D, float scale, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || D < 1) return SWR_ERR_INVALID;
+  if (Hq % Hkv != 0) return SWR_ERR_INVALID;
+  if (!std::isfinite(scale)) return SWR_ERR_INVALID;
+  if (!supported_d(D)) return SWR_ERR_UNSUPPORTED;
+  swr_status st = check_kv(kv, Hkv, D);
+  if (st != SWR_OK) return st;
+  if (!q || !out || !pos || !aligned16(q) || !aligned16(out)) return SWR_ERR_INVALID;
+  if (mode == swr::MODE_VERIFY && (!k_prop || !v_prop || !aligned16(k_prop) || !aligned16(v_prop)))
+    return SWR_ERR_INVALID;
+  if (mode == swr::MODE_GLOBAL) {
+    if (!key_count || cap_or_max_keys < 1) return SWR_ERR_INVALID;
+    // the padded contraction reads pad64(key_count) slots of every region
+    if ((long)(cap_or_max_keys + 63) / 64 * 64 > kv->cap) return SWR_ERR_INVALID;
+  }
+  AttnPlan pl;
+  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, kv->dtype == SWR_KV_FP8_E4M3, cap_or_max_keys, &pl))
+    return SWR_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws))) return SWR_ERR_WORKSPACE;
+  if (B == 0) return SWR_OK;
+
+  AttnParams p{};
+  p.k_base = static_cast<const uint8_t*>(kv->k_base);
+  p.v_base = static_cast<const uint8_t*>(kv->v_base);
+  p.k_off = kv->k_off;
+  p.v_off = kv->v_off;
+  p.region_bytes = region_bytes(kv, Hkv, D);
+  p.cap = kv->cap;
+  const double ks = kv->dtype == SWR_KV_FP8_E4M3 ? (double)kv->k_scale : 1.0;
+  p.qk_scale = (float)((double)scale * ks * kLog2e);
+  p.v_scale = kv->dtype == SWR_KV_FP8_E4M3 ? kv->v_scale : 1.0f;
+  p.q = static_cast<const uint16_t*>(q);
+  p.out = static_cast<uint16_t*>(out);
+  p.pos = pos;
+  p.key_count = key_count;
+  p.k_prop = static_cast<const uint16_t*>(k_prop);
+  p.v_prop = static_cast<const uint16_t*>(v_prop);
+  if (pl.ws_bytes > 0) {
+    float* w = static_cast<float*>(ws);
+    p.ws_acc = w;
+    p.ws_ml = w + (size_t)pl.units * pl.nsplit * pl.rows * D;
+  }
+  p.B = B;
+  p.S = S;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.rows = pl.rows;
+  p.nsplit = pl.nsplit;
+  p.tiles_per_split = pl.tiles_per_split;
+  return to_status(swr::launch_attention(pl, p, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
+                         const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv, int D,
+                         int wrap, hipStream_t stream) {
+  if (B < 0 || T < 1 || Hkv < 1 || D < 1) return SWR_ERR_INVALID;
+  if (!supported_d(D)) return SWR_ERR_UNSUPPORTED;
+  swr_status st = check_kv(kv, Hkv, D);
+  if (st != SWR_OK) return st;
+  if (!k_new || !v_new || !pos0 || !aligned16(k_new) || !aligned16(v_new)) return SWR_ERR_INVALID;
+  if (B == 0) return SWR_OK;
+  swr::AppendParams p{};
+  p.k_base = static_cast<uint8_t*>(kv->k_base);
+  p.v_base = static_cast<uint8_t*>(kv->v_base);
+  p.k_off = kv->k_off;
+  p.v_off = kv->v_off;
+  p.region_bytes = region_bytes(kv, Hkv, D);
+  p.cap = kv->cap;
+  p.wrap = wrap ? 1 : 0;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.pos0 = pos0;
+  p.n_new = n_new;
+  p.B = B;
+  p.T = T;
+  p.Hkv = Hkv;
+  p.D = D;
+  return to_status(swr::launch_append(p, kv->dtype == SWR_KV_FP8_E4M3, stream));
+}
+
+swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const int32_t* pos, int B,
+                          int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!ring) return SWR_ERR_INVALID;
+  return attend(swr::MODE_DECODE, ring, q, out, pos, nullptr, nullptr, nullptr, ring->cap, B, 1, Hq,
+                Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+swr_status swr_gqa_verify(const swr_kv* ring, const void* k_prop, const void* v_prop,
+                          const void* q, void* out, const int32_t* pos0, int B, int S, int Hq,
+                          int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!ring) return SWR_ERR_INVALID;
+  return attend(swr::MODE_VERIFY, ring, q, out, pos0, nullptr, k_prop, v_prop, ring->cap, B, S, Hq,
+                Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const int32_t* q_pos,
+                             const int32_t* key_count, int max_key_count, int B, int S, int Hq,
+                             int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return attend(swr::MODE_GLOBAL, kv, q, out, q_pos, key_count, nullptr, nullptr, max_key_count, B,
+                S, Hq, Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap_or_max_keys) {
+  int mode;
+  switch (op) {
+    case SWR_OP_SWA_DECODE: mode = swr::MODE_DECODE; S = 1; break;
+    case SWR_OP_GQA_VERIFY: mode = swr::MODE_VERIFY; break;
+    case SWR_OP_GLOBAL_ATTEND: mode = swr::MODE_GLOBAL; break;
+    default: return 0;
+  }
+  AttnPlan pl;
+  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, 0, cap_or_max_keys, &pl)) return 0;
+  return pl.ws_bytes;
+}
+
+int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype) {
+  if (cap <= 0 || cap % 8 != 0 || Hkv <= 0 || D <= 0) return -1;
+  if (dtype != SWR_KV_BF16 && dtype != SWR_KV_FP8_E4M3) return -1;
+  return (int64_t)cap * Hkv * D * elem_size(dtype);
+}
+
+swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return SWR_OK;
+  if (!ptr) return SWR_ERR_INVALID;
+  return to_status(swr::launch_zero_fill(ptr, bytes, stream));
+}
+
+const char* swr_status_string(swr_status s) {
+  switch (s) {
+    case SWR_OK: return "ok";
+    case SWR_ERR_INVALID: return "invalid argument";
+    case SWR_ERR_UNSUPPORTED: return "unsupported shape";
+    case SWR_ERR_WORKSPACE: return "workspace missing or too small";
+    case SWR_ERR_LAUNCH: return "HIP launch error";
+    case SWR_ERR_NOMEM: return "pool exhausted";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ pool
+
+struct swr_pool {
+  size_t size;
+  std::map<int64_t, size_t> used;  // offset -> bytes (sorted by offset)
+  size_t used_bytes = 0;
+  mutable std::mutex mu;
+};
+
+namespace {
+constexpr int64_t kPoolAlign = 256;
+int64_t align_up(int64_t x) { return (x + kPoolAlign - 1) / kPoolAlign * kPoolAlign; }
+}  // namespace
+
+extern "C" {
+
+swr_status swr_pool_create(size_t bytes, swr_pool** pool) {
+  if (!pool || bytes == 0) return SWR_ERR_INVALID;
+  swr_pool* p = new (std::nothrow) swr_pool();
+  if (!p) return SWR_ERR_NOMEM;
+  p->size = bytes;
+  *pool = p;
+  return SWR_OK;
+}
+
+void swr_pool_destroy(swr_pool* pool) { delete pool; }
+
+swr_status swr_pool_alloc(swr_pool* pool, size_t bytes, int64_t* offset) {
+  if (!pool || !offset || bytes == 0) return SWR_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  // first fit: walk the used ranges in address order, try each gap
+  int64_t cursor = 0;
+  for (const auto& kv : pool->used) {
+    const int64_t start = align_up(cursor);
+    if (start + (int64_t)bytes <= kv.first) {
+      pool->used.emplace(start, bytes);
+      pool->used_bytes += bytes;
+      *offset = start;
+      return SWR_OK;
+    }
+    cursor = kv.first + (int64_t)kv.second;
+  }
+  const int64_t start = align_up(cursor);
+  if (start + (int64_t)bytes > (int64_t)pool->size) return SWR_ERR_NOMEM;
+  pool->used.emplace(start, bytes);
+  pool->used_bytes += bytes;
+  *offset = start;
+  return SWR_OK;
+}
+
+swr_status swr_pool_free(swr_pool* pool, int64_t offset) {
+  if (!pool) return SWR_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->used.find(offset);
+  if (it == pool->used.end()) return SWR_ERR_INVALID;
+  pool->used_bytes -= it->second;
+  pool->used.erase(it);
+  return SWR_OK;
+}
+
+swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dtype, int global,
+                             int64_t* k_offset, int64_t* v_offset, int32_t* cap) {
+  if (!pool || !k_offset || !v_offset || !cap || tokens <= 0 || Hkv <= 0 || D <= 0)
+    return SWR_ERR_INVALID;
+  const int mult = global ? 64 : 8;
+  const long c = ((long)tokens + mult - 1) / mult * mult;
+  if (c > INT32_MAX) return SWR_ERR_INVALID;
+  const int64_t rb = swr_kv_region_bytes((int)c, Hkv, D, dtype);
+  if (rb <= 0) return SWR_ERR_INVALID;
+  int64_t ko, vo;
+  swr_status st = swr_pool_alloc(pool, (size_t)rb, &ko);
+  if (st != SWR_OK) return st;
+  st = swr_pool_alloc(pool, (size_t)rb, &vo);
+  if (st != SWR_OK) {
+    swr_pool_free(pool, ko);
+    return st;
+  }
+  *k_offset = ko;
+  *v_offset = vo;
+  *cap = (int32_t)c;
+  return SWR_OK;
+}
+
+swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_free) {
+  if (!pool) return SWR_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  size_t largest = 0;
+  int64_t cursor = 0;
+  for (const auto& kv : pool->used) {
+    const int64_t start = align_up(cursor);
+    if (kv.first > start) largest = std::max(largest, (size_t)(kv.first - start));
+    cursor = kv.first + (int64_t)kv.second;
+  }
+  const int64_t start = align_up(cursor);
+  if ((int64_t)pool->size > start) largest = std::max(largest, (size_t)((int64_t)pool->size - start));
+  if (used) *used = pool->used_bytes;
+  if (largest_free) *largest_free = largest;
+  return SWR_OK;
+}
+
+}  // extern "C"

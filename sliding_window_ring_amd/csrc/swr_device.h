@@ -1,0 +1,96 @@
+// swr_device.h -- device-side building blocks for gfx950 (CDNA4) kernels:
+// vector types, bf16 / OCP-fp8 conversion, the bf16 MFMA wrapper, bounded
+// buffer loads and wave-level reductions.  Written for gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Third word of a raw buffer resource on gfx9-family parts (gfx950 included):
+// 32-bit data format, no swizzle.  Reads past num_records return zero and
+// writes past it are dropped, so every region access is bounded in hardware.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, 0);
+}
+
+// 8 OCP e4m3 codes (two dwords, code i in byte i) -> 8 bf16, exact
+// (every e4m3 value is a bf16 value).  Uses the gfx950 conversion with a unit
+// scale; the per-tensor scale is applied by the caller outside the MFMA.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 c) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true);
+  bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false);
+  bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], e[0], e[1], f[0], f[1]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 8
+// k-values of lane group l / 16; lane l receives C rows 4*(l/16) .. +3 of
+// column l % 16.  A and B use the same k assignment per (lane group, element),
+// so any fixed permutation of the k axis applied to both leaves D unchanged.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the lanes that hold
+// one C column of a 16x16 MFMA tile).
+__device__ __forceinline__ float max4lanes(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float sum4lanes(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace swr

@@ -1,0 +1,77 @@
+// swr_internal.h -- host-side launch plans and kernel entry declarations
+// shared by the C-ABI layer (swr_api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swr {
+
+enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2 };
+
+// Everything an attention launch reads, by value.
+struct AttnParams {
+  const uint8_t* k_base;
+  const uint8_t* v_base;
+  const int64_t* k_off;
+  const int64_t* v_off;
+  uint32_t region_bytes;   // bytes of one K (or V) region: cap*Hkv*D*esize
+  int cap;                 // slots per region (ring: W)
+  float qk_scale;          // scale * k_scale * log2(e): scores in the base-2 domain
+  float v_scale;           // applied to the normalised output
+  const uint16_t* q;       // bf16 [B][S][Hq][D]
+  uint16_t* out;           // bf16 [B][S][Hq][D]
+  const int32_t* pos;      // decode: pos[B]; verify: pos0[B]; global: q_pos[B][S]
+  const int32_t* key_count;  // global: [B]
+  const uint16_t* k_prop;  // verify: bf16 [B][S][Hkv][D]
+  const uint16_t* v_prop;
+  float* ws_acc;           // split partials: [units][nsplit][rows][D]
+  float* ws_ml;            // split partials: [units][nsplit][rows][2] (max, sum)
+  int B, S, Hq, Hkv, G, rows;
+  int nsplit;              // workgroups per (request, KV head)
+  int tiles_per_split;     // 32-key tiles each split covers
+};
+
+// Launch geometry chosen on the host for one attention call.
+struct AttnPlan {
+  int mode, D, fp8;
+  int ds;        // head dims per wave (D / ds waves share a key tile)
+  int nct;       // 16-row column tiles (rows = G*S <= 16*nct)
+  int kw;        // waves splitting the keys inside a workgroup
+  int units;     // B * Hkv
+  int rows;      // G * S
+  int max_tiles; // 32-key tiles of the longest unit
+  int nsplit;
+  int tiles_per_split;
+  size_t ws_bytes;  // 0 when nsplit == 1
+  size_t lds_bytes;
+  int threads;
+};
+
+// Fills *plan; returns false for shapes outside the compiled set.
+bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
+                    AttnPlan* plan);
+
+hipError_t launch_attention(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
+
+struct AppendParams {
+  uint8_t* k_base;
+  uint8_t* v_base;
+  const int64_t* k_off;
+  const int64_t* v_off;
+  uint32_t region_bytes;
+  int cap;
+  int wrap;
+  float k_scale, v_scale;
+  const uint16_t* k_new;  // bf16 [B][T][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* pos0;
+  const int32_t* n_new;   // may be null
+  int B, T, Hkv, D;
+};
+
+hipError_t launch_append(const AppendParams& p, int fp8, hipStream_t stream);
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace swr

@@ -28,11 +28,12 @@ def rng(seed: int) -> np.random.Generator:
 def bf16_bits(x) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return the bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb cannot pass 2^32 for non-NaN inputs; NaNs are fixed below
+    r = ((u + ((u >> 16) & 1) + np.uint32(0x7FFF)) >> 16).astype(np.uint16)
     nan = np.isnan(x)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaN quiet
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaN quiet
     return r
 
 

@@ -1,0 +1,125 @@
+"""CPU tests of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the GPU.
+
+No call here reaches a HIP runtime function: each one fails host-side
+validation first (the header promises validation precedes any launch), so
+these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_ring_amd as swr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "swr.h")).read()
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH, NOMEM = range(6)
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    body = re.sub(r"/\*.*?\*/", "", HEADER, flags=re.S)
+    return sorted(set(re.findall(r"\b(swr_[a-z0-9_]+)\s*\(", body)))
+
+
+def test_header_declares_the_boundary_calls():
+    names = declared_functions()
+    for n in ["swr_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend",
+              "swr_workspace_bytes", "swr_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(swr.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(swr.EXPORTS) == declared_functions()
+
+
+def test_status_strings():
+    for s in range(6):
+        assert swr.lib.swr_status_string(s).decode() == swr.STATUS[s]
+
+
+def kv(cap=1024, dtype=0, k_scale=1.0, v_scale=1.0, base=FAKE):
+    return swr.SwrKV(base, base, FAKE, FAKE, cap, dtype, k_scale, v_scale)
+
+
+def decode(k=None, q=FAKE, out=FAKE, pos=FAKE, B=56, Hq=64, Hkv=8, D=256, scale=0.0625, ws=None, wsb=0):
+    r = kv() if k is None else k
+    return swr.lib.swr_swa_decode(ctypes.byref(r), q, out, pos, B, Hq, Hkv, D, scale, ws, wsb, None)
+
+
+def test_decode_validation():
+    assert decode(q=None) == INVALID
+    assert decode(out=None) == INVALID
+    assert decode(pos=None) == INVALID
+    assert decode(q=FAKE + 2) == INVALID           # misaligned
+    assert decode(Hq=60) == INVALID                # not a multiple of Hkv
+    assert decode(B=-1) == INVALID
+    assert decode(D=96) == UNSUPPORTED
+    assert decode(Hq=8 * 32) == UNSUPPORTED        # 32 query heads per KV head
+    assert decode(k=kv(cap=1004)) == INVALID       # cap not a multiple of 8
+    assert decode(k=kv(cap=0)) == INVALID
+    assert decode(k=kv(dtype=7)) == INVALID
+    assert decode(k=kv(dtype=1, k_scale=0.0)) == INVALID
+    assert decode(k=kv(dtype=1, v_scale=float("nan"))) == INVALID
+    assert decode(k=kv(base=FAKE + 8)) == INVALID
+    assert decode(scale=float("inf")) == INVALID
+    assert swr.lib.swr_swa_decode(None, FAKE, FAKE, FAKE, 1, 8, 1, 64, 1.0, None, 0, None) == INVALID
+    assert decode(k=kv(cap=1 << 22)) == UNSUPPORTED  # region beyond 32-bit offsets
+
+
+def test_decode_small_batch_needs_workspace():
+    # 16 requests x 8 KV heads fill half the chip: split-K needs a workspace
+    need = swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, 16, 1, 64, 8, 256, 1024)
+    assert need > 0
+    assert decode(B=16) == WORKSPACE
+    assert decode(B=16, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, 56, 1, 64, 8, 256, 1024) == 0
+
+
+def test_verify_and_global_validation():
+    r = kv()
+    f = swr.lib.swr_gqa_verify
+    assert f(ctypes.byref(r), None, FAKE, FAKE, FAKE, FAKE, 8, 4, 64, 8, 256, 0.06, None, 0, None) == INVALID
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 9, 64, 8, 256, 0.06, None, 0, None) == UNSUPPORTED
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 128, 8, 256, 0.06, None, 0, None) == UNSUPPORTED
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 64, 8, 256, 0.06, None, 0, None) == WORKSPACE
+    g = swr.lib.swr_global_attend
+    rg = kv(cap=6016)
+    assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, None, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
+    assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6017, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
+    assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 0, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
+    assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == WORKSPACE
+
+
+def test_append_validation():
+    r = kv()
+    f = swr.lib.swr_kv_append
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, None, 56, 0, 8, 256, 1, None) == INVALID   # T == 0
+    assert f(ctypes.byref(r), None, FAKE, FAKE, None, 56, 1, 8, 256, 1, None) == INVALID
+    assert f(ctypes.byref(r), FAKE, FAKE, None, None, 56, 1, 8, 256, 1, None) == INVALID
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, None, 56, 1, 8, 200, 1, None) == UNSUPPORTED
+    assert f(None, FAKE, FAKE, FAKE, None, 56, 1, 8, 256, 1, None) == INVALID
+    # B == 0 is a valid no-op that launches nothing
+    assert f(ctypes.byref(r), FAKE, FAKE, FAKE, None, 0, 1, 8, 256, 1, None) == OK
+
+
+def test_zero_batch_attention_is_a_no_op():
+    assert decode(B=0) == OK
+
+
+def test_workspace_bytes_unsupported_is_zero():
+    assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 9, 64, 8, 256, 1024) == 0
+    assert swr.workspace_bytes(99, 8, 4, 64, 8, 256, 1024) == 0
+
+
+def test_region_bytes():
+    assert swr.region_bytes(1024, 8, 256) == 1024 * 8 * 256 * 2
+    assert swr.region_bytes(1024, 8, 256, swr.SWR_KV_FP8_E4M3) == 1024 * 8 * 256
+    with pytest.raises(ValueError):
+        swr.region_bytes(1001, 8, 256)

@@ -1,0 +1,201 @@
+"""GPU parity of the attention calls against the oracle.
+
+Every case feeds the same seeded inputs (rings and regions built by the
+oracle's append, copied to the device) to swr_swa_decode / swr_gqa_verify /
+swr_global_attend and to the float64 oracle, and holds the bf16 outputs to
+max-abs <= 1e-2 and relative L2 <= 5e-3.  Cases span several 32-key tiles
+and ragged tails, the full workload sizes (B=56 sliding decode, B=8 sliding
+verify, the 6005-key global verify), the split-K path, every head dim, and
+the degenerate cases (a single visible key, a ring that has not wrapped,
+proposals at position 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_ring_amd as swr
+import synthetic
+from gpu_common import dev_bf16, dev_i32, host_bits, host_f64, layer
+from helpers import assert_parity, global_pools, ring_pools
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_case(w, x, dtype=oracle.BF16, ks=1.0, vs=1.0):
+    scale = 1.0 / np.sqrt(w.D)
+    kp, vp, ko, vo = ring_pools(x["k"], x["v"], x["start"], x["n"], w.W, dtype, ks, vs)
+    ref = oracle.swa_decode(kp, vp, ko, vo, w.W, dtype, ks, vs, x["q"], x["pos"], w.Hkv, scale)
+    L = layer(kp, vp, ko, vo, w.W, dtype, ks, vs)
+    out = swr.swa_decode(L, dev_bf16(x["q"]), dev_i32(x["pos"]), w.Hkv, scale)
+    torch.cuda.synchronize()
+    return out, ref
+
+
+def test_decode_tiny_sequence_step_by_step():
+    """Workload 1: W=16, 2 query heads on 1 KV head, D=64; 40 tokens appended
+    one at a time on the GPU, decode after each; ring bytes bit-exact with the
+    oracle's after every append, outputs within tolerance, and step 0 (one
+    visible key) returns that key's value bits exactly."""
+    w = synthetic.TINY
+    q, k, v = synthetic.tiny_sequence()
+    rb = oracle.region_bytes(w.W, w.Hkv, w.D, oracle.BF16)
+    kp = np.zeros(rb, np.uint8)
+    vp = np.zeros(rb, np.uint8)
+    off = np.zeros(1, np.int64)
+    L = layer(kp, vp, off, off, w.W)
+    scale = 1.0 / np.sqrt(w.D)
+    for t in range(w.steps):
+        pos = np.array([t], np.int32)
+        swr.kv_append(L, dev_bf16(k[None, t:t + 1]), dev_bf16(v[None, t:t + 1]), dev_i32(pos))
+        out = swr.swa_decode(L, dev_bf16(q[None, t]), dev_i32(pos), w.Hkv, scale)
+        torch.cuda.synchronize()
+        oracle.kv_append(kp, vp, off, off, w.W, oracle.BF16, 1, 1, k[None, t:t + 1], v[None, t:t + 1], pos)
+        assert np.array_equal(L.k_base.cpu().numpy(), kp), t
+        assert np.array_equal(L.v_base.cpu().numpy(), vp), t
+        ref = oracle.swa_decode(kp, vp, off, off, w.W, oracle.BF16, 1, 1, q[None, t], pos, w.Hkv, scale)
+        assert_parity(host_f64(out), ref, f"step {t}")
+        if t == 0:
+            assert np.array_equal(host_bits(out)[0], np.repeat(v[0], w.G, axis=0))
+
+
+def test_decode_b56_full_workload():
+    w = synthetic.SWA_DECODE
+    out, ref = decode_case(w, synthetic.sliding_decode(w))
+    e = assert_parity(host_f64(out), ref, "B=56 decode")
+    print("B=56 decode max-abs %.3e rel-L2 %.3e" % e)
+
+
+@pytest.mark.parametrize("positions", [
+    (0, 1, 2, 15, 16, 31, 32, 33),          # partial rings, ragged last tiles
+    (1022, 1023, 1024, 1025, 2047, 5000, 100000, 63),
+])
+def test_decode_edges(positions):
+    w = synthetic.Workload("t", B=len(positions), Hkv=8, G=8, D=256, W=1024)
+    out, ref = decode_case(w, synthetic.sliding_decode(w, seed=21, positions=positions))
+    assert_parity(host_f64(out), ref, f"decode {positions}")
+    if positions[0] == 0:  # a single visible key: output = that value, exactly
+        x = synthetic.sliding_decode(w, seed=21, positions=positions)
+        assert np.array_equal(host_bits(out)[0], np.repeat(x["v"][0, 0], w.G, axis=0))
+
+
+@pytest.mark.parametrize("D,G,Hkv,W", [(64, 1, 4, 64), (128, 4, 2, 256), (512, 2, 2, 128), (256, 16, 1, 96),
+                                       (64, 2, 1, 16)])
+def test_decode_shapes(D, G, Hkv, W):
+    w = synthetic.Workload("t", B=5, Hkv=Hkv, G=G, D=D, W=W)
+    out, ref = decode_case(w, synthetic.sliding_decode(w, seed=22, positions=(0, W // 2 + 3, W - 1, W, 3 * W + 5)))
+    assert_parity(host_f64(out), ref, f"decode D={D} G={G}")
+
+
+def test_decode_small_batch_uses_split_k():
+    # 16 requests x 8 KV heads: fewer units than CUs, so the keys are split
+    # across workgroups and merged by the combine step
+    w = synthetic.MIXED_SLIDING
+    ctx = synthetic.mixed_contexts()
+    assert swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W) > 0
+    out, ref = decode_case(w, synthetic.sliding_decode(w, seed=23, positions=ctx))
+    assert_parity(host_f64(out), ref, "B=16 split-K decode")
+
+
+@pytest.mark.parametrize("ks,vs", [(2.0 ** -6, 2.0 ** -6), (0.00917, 0.01033)])
+def test_decode_fp8_ring(ks, vs):
+    w = synthetic.Workload("t", B=12, Hkv=8, G=8, D=256, W=1024)
+    x = synthetic.sliding_decode(w, seed=24, positions=(0, 5, 100, 1023, 1024, 1500, 2000, 3000, 4000, 5000,
+                                                       6000, 7000))
+    out, ref = decode_case(w, x, oracle.FP8, ks, vs)
+    assert_parity(host_f64(out), ref, "fp8 decode")
+
+
+# ------------------------------------------------------------------ verify
+
+def verify_case(w, x):
+    scale = 1.0 / np.sqrt(w.D)
+    kp, vp, ko, vo = ring_pools(x["k"], x["v"], x["start"], x["n"], w.W)
+    ref = oracle.gqa_verify(kp, vp, ko, vo, w.W, oracle.BF16, 1, 1, x["k_prop"], x["v_prop"], x["q"], x["p0"],
+                            w.Hkv, scale)
+    L = layer(kp, vp, ko, vo, w.W)
+    out = swr.gqa_verify(L, dev_bf16(x["k_prop"]), dev_bf16(x["v_prop"]), dev_bf16(x["q"]), dev_i32(x["p0"]),
+                         scale)
+    torch.cuda.synchronize()
+    return out, ref
+
+
+def test_verify_b8_full_workload():
+    w = synthetic.SWA_VERIFY
+    out, ref = verify_case(w, synthetic.sliding_verify(w))
+    e = assert_parity(host_f64(out), ref, "B=8 verify")
+    print("B=8 verify max-abs %.3e rel-L2 %.3e" % e)
+
+
+@pytest.mark.parametrize("S,G", [(1, 8), (2, 8), (3, 8), (4, 8), (8, 4), (4, 2), (5, 1)])
+def test_verify_proposal_counts(S, G):
+    w = synthetic.Workload("t", B=8, Hkv=2, G=G, D=256, W=128, S=S)
+    x = synthetic.sliding_verify(w, seed=31, positions=(0, 1, 5, 126, 127, 128, 129, 1000))
+    out, ref = verify_case(w, x)
+    assert_parity(host_f64(out), ref, f"verify S={S} G={G}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 512])
+def test_verify_head_dims(D):
+    w = synthetic.Workload("t", B=3, Hkv=2, G=8, D=D, W=64, S=4)
+    out, ref = verify_case(w, synthetic.sliding_verify(w, seed=32, positions=(3, 64, 300)))
+    assert_parity(host_f64(out), ref, f"verify D={D}")
+
+
+# ------------------------------------------------------------------ global
+
+def global_case(w, x, cap):
+    scale = 1.0 / np.sqrt(w.D)
+    kp, vp, ko, vo = global_pools(x["k"], x["v"], x["key_count"], cap)
+    ref = oracle.global_attend(kp, vp, ko, vo, cap, oracle.BF16, 1, 1, x["q"], x["q_pos"], x["key_count"],
+                               w.Hkv, scale)
+    L = layer(kp, vp, ko, vo, cap)
+    out = swr.global_attend(L, dev_bf16(x["q"]), dev_i32(x["q_pos"]), dev_i32(x["key_count"]),
+                            int(x["key_count"].max()), w.Hkv, scale)
+    torch.cuda.synchronize()
+    return out, ref
+
+
+def test_global_verify_6005_keys():
+    w = synthetic.GLOBAL_VERIFY
+    out, ref = global_case(w, synthetic.global_verify(w), 6016)
+    e = assert_parity(host_f64(out), ref, "global verify 6005")
+    print("global verify max-abs %.3e rel-L2 %.3e" % e)
+
+
+def test_global_sweep_subset():
+    """Key counts from the 4000..8192 sweep: 6000..6080, multiples of 64 +-1,
+    the endpoints and random counts; batched as separate requests that share
+    one key history."""
+    g = synthetic.rng(33)
+    counts = sorted(set(list(range(6000, 6081, 4)) + [4000, 8192, 4095, 4096, 4097, 6015, 6016, 6017, 8127,
+                                                      8128, 8129, 5000, 7777] +
+                        list(g.integers(4000, 8193, 8))))
+    w = synthetic.GLOBAL_VERIFY
+    hist = synthetic.global_verify(synthetic.Workload("t", B=1, Hkv=2, G=8, D=512, S=4, key_count=8192), seed=34)
+    for chunk in (counts[:len(counts) // 2], counts[len(counts) // 2:]):
+        B = len(chunk)
+        kc = np.array(chunk, np.int32)
+        x = dict(key_count=kc, q_pos=(kc[:, None] - 4 + np.arange(4, dtype=np.int32)[None, :]).astype(np.int32),
+                 k=np.repeat(hist["k"], B, axis=0), v=np.repeat(hist["v"], B, axis=0),
+                 q=synthetic.normal_bf16(g, (B, 4, 16, 512)))
+        ww = synthetic.Workload("t", B=B, Hkv=2, G=8, D=512, S=4)
+        out, ref = global_case(ww, x, 8192)
+        for b in range(B):
+            assert_parity(host_f64(out)[b], ref[b], f"key_count {chunk[b]}")
+    assert w.key_count == 6005
+
+
+@pytest.mark.parametrize("S,G,D", [(1, 8, 512), (2, 8, 512), (4, 2, 64), (3, 4, 256), (1, 16, 128)])
+def test_global_shapes(S, G, D):
+    kc = np.array([1, 63, 64, 65, 700, 2000], np.int32)
+    w = synthetic.Workload("t", B=kc.size, Hkv=2, G=G, D=D, S=S)
+    g = synthetic.rng(35)
+    x = dict(key_count=kc,
+             q_pos=np.maximum(kc[:, None] - S + np.arange(S, dtype=np.int32)[None, :], 0).astype(np.int32),
+             k=synthetic.normal_bf16(g, (kc.size, 2048, 2, D)), v=synthetic.normal_bf16(g, (kc.size, 2048, 2, D)),
+             q=synthetic.normal_bf16(g, (kc.size, S, w.Hq, D)))
+    out, ref = global_case(w, x, 2048)
+    assert_parity(host_f64(out), ref, f"global S={S} G={G} D={D}")
