@@ -40,19 +40,24 @@
  *     caller's.  Region reads and writes are bounded in hardware to
  *     `cap` slots, so a broken precondition gives wrong numbers, not a fault.
  *
- * KV region layout (one request, one layer; K and V regions separate)
+ * KV region layout (one request, one layer; K and V regions separate; a
+ * region has `cap` slots, cap a multiple of 8)
  *   slot s in [0, cap), KV head g in [0, Hkv), dim d in [0, D):
- *     K element (s, g, d) at element index (s*Hkv + g)*D + d
- *     V element (s, g, d) at element index ((s/8)*Hkv + g)*D*8 + d*8 + (s%8)
+ *     K element (s, g, d) at element index (g*cap + s)*D + d
+ *       i.e. K is [Hkv][cap][D]
+ *     V element (s, g, d) at element index ((g*(cap/8) + s/8)*D + d)*8 + (s%8)
+ *       i.e. V is [Hkv][cap/8][D][8]: blocks of 8 slots
  *   Element size: 2 bytes (SWR_KV_BF16) or 1 byte (SWR_KV_FP8_E4M3).
- *   K rows are token-major so one append writes one row per token; V is kept
- *   in blocks of 8 slots so that the 8 values of a dim for 8 consecutive slots
- *   are contiguous, which is the operand shape of the gfx950 bf16 matrix
- *   instruction along the key axis.  cap is a multiple of 8.  A region is
- *   cap*Hkv*D*element_size bytes (swr_kv_region_bytes).
- *   Ring regions: cap = W, slot = position mod W.  Global regions: slot =
- *   position, and cap >= pad64(key_count) with slots beyond key_count holding
- *   finite values (the pool's zero fill provides this).
+ *   Each (request, KV head) reads one contiguous K stream and one contiguous
+ *   V stream, which is what HBM streams best.  V is kept in blocks of 8 slots
+ *   so that the values of one dim for 8 consecutive slots are contiguous:
+ *   that is the operand shape of the gfx950 bf16 matrix instruction along
+ *   the key axis.  A region is cap*Hkv*D*element_size bytes
+ *   (swr_kv_region_bytes).
+ *   Ring regions: cap = W for every request, slot = position mod W.
+ *   Global regions: slot = position; each region holds >= pad64(key_count)
+ *   slots, those beyond key_count holding finite values (the pool's zero
+ *   fill provides this); regions may differ in capacity (swr_kv.cap_b).
  */
 #ifndef SWR_H
 #define SWR_H
@@ -93,7 +98,11 @@ typedef struct swr_kv {
   void* v_base;          /* device: base of the buffer holding V regions (may equal k_base) */
   const int64_t* k_off;  /* device [B]: byte offset of request b's K region from k_base (16-B aligned) */
   const int64_t* v_off;  /* device [B]: same for V */
-  int32_t cap;           /* slots per region: the window W for rings, the capacity for global regions */
+  const int32_t* cap_b;  /* device [B] per-request slot counts of global regions (multiples of 8,
+                            each <= cap), or NULL when every region has `cap` slots.  Must be
+                            NULL for rings. */
+  int32_t cap;           /* slots per region: the window W for rings; for global regions the
+                            capacity (the largest one when cap_b is given) */
   int32_t dtype;         /* swr_kv_dtype */
   float k_scale;         /* fp8 only: per-tensor scale of K (> 0, finite) */
   float v_scale;         /* fp8 only: per-tensor scale of V (> 0, finite) */
@@ -110,8 +119,9 @@ typedef struct swr_kv {
  *   wrap != 0    : ring, slot = position mod cap.  When n_new > cap only the
  *                  last cap tokens are written, which is what writing them one
  *                  after another leaves behind.
- *   wrap == 0    : global region, slot = position (position < cap; larger
- *                  positions are dropped).
+ *   wrap == 0    : global region, slot = position (position < the region's
+ *                  capacity; larger positions are dropped).
+ *   kv->cap_b must be NULL when wrap != 0.
  *   fp8 regions store the code nearest to value/scale (exact quotient,
  *   ties to even, saturating at +-448; NaN -> 0x7F with its sign).
  * Supported: D in {64, 128, 256, 512}; T >= 1; B >= 0 (B == 0 is a no-op). */

@@ -56,10 +56,10 @@ def _bind(h):
     h.orc_e4m3_encode_n.argtypes = [P, I64, F, P]
     h.orc_region_bytes.argtypes = [I, I, I, I]
     h.orc_region_bytes.restype = I64
-    h.orc_kv_append.argtypes = [P, P, P, P, I, I, F, F, P, P, P, P, I, I, I, I, I]
+    h.orc_kv_append.argtypes = [P, P, P, P, I, P, I, F, F, P, P, P, P, I, I, I, I, I]
     h.orc_swa_decode.argtypes = [P, P, P, P, I, I, D, D, P, P, I, I, I, I, D, P]
     h.orc_gqa_verify.argtypes = [P, P, P, P, I, I, D, D, P, P, P, P, I, I, I, I, I, D, P]
-    h.orc_global_attend.argtypes = [P, P, P, P, I, I, D, D, P, P, P, I, I, I, I, I, I, D, P]
+    h.orc_global_attend.argtypes = [P, P, P, P, I, P, I, D, D, P, P, P, I, I, I, I, I, I, D, P]
     h.orc_num_threads.restype = I
     return h
 
@@ -149,19 +149,6 @@ def region_bytes(cap: int, hkv: int, d: int, dtype: int) -> int:
     return int(n)
 
 
-# ---------------------------------------------------------------- layout helpers
-
-def k_elem_index(slot, g, d, hkv, dd):
-    """Element index of K(slot, g, d): token-major rows."""
-    return (slot * hkv + g) * dd + d
-
-
-def v_elem_index(slot, g, d, hkv, dd):
-    """Element index of V(slot, g, d): 8-slot blocks, the 8 slots of a block
-    contiguous for each (g, d)."""
-    return ((slot // 8 * hkv + g) * dd + d) * 8 + slot % 8
-
-
 # ---------------------------------------------------------------- operations
 
 def _check_rc(rc, what):
@@ -170,13 +157,14 @@ def _check_rc(rc, what):
 
 
 def kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, k_new, v_new, pos0,
-              n_new=None, wrap=True):
+              n_new=None, wrap=True, caps=None):
     """Append tokens to each request's region, in place.
 
     Ring mode (wrap=True): slot = position mod cap ("Announcing Carat", ring
     buffer section; "Improving Decode Throughput on Intel Gaudi 3", "Our
     approach": K and V of a token go to the same slot).  Global mode
-    (wrap=False): slot = position.  k_new, v_new: bf16 bits [B][T][Hkv][D].
+    (wrap=False): slot = position; caps optionally gives each request's
+    region capacity.  k_new, v_new: bf16 bits [B][T][Hkv][D].
     """
     k_new = _c(k_new, np.uint16)
     v_new = _c(v_new, np.uint16)
@@ -186,7 +174,8 @@ def kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, k_new,
     pos0 = _c(pos0, np.int32)
     nn = None if n_new is None else _c(n_new, np.int32)
     assert k_pool.dtype == np.uint8 and v_pool.dtype == np.uint8
-    rc = lib().orc_kv_append(_p(k_pool), _p(v_pool), _p(k_off), _p(v_off), cap, dtype,
+    cp = None if caps is None else _c(caps, np.int32)
+    rc = lib().orc_kv_append(_p(k_pool), _p(v_pool), _p(k_off), _p(v_off), cap, _p(cp), dtype,
                              ctypes.c_float(k_scale), ctypes.c_float(v_scale), _p(k_new), _p(v_new),
                              _p(pos0), _p(nn), B, T, hkv, d, 1 if wrap else 0)
     _check_rc(rc, "kv_append")
@@ -227,20 +216,21 @@ def gqa_verify(k_pool, v_pool, k_off, v_off, W, dtype, k_scale, v_scale, k_prop,
 
 
 def global_attend(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, q, q_pos, key_count,
-                  hkv, scale, padded=True):
+                  hkv, scale, padded=True, caps=None):
     """Global-layer attention over contiguous regions ("Announcing Carat",
     "More FLOPs can be faster": scores over key_count keys, causal softmax by
     query position, weighted sum of values; padded=True contracts over the
     64-padded key range with a masked tail).
 
     q: bf16 bits [B][S][Hq][D]; q_pos: [B][S]; key_count: [B].
-    Returns float64 [B][S][Hq][D].
+    caps: optional per-request region capacities.  Returns float64 [B][S][Hq][D].
     """
     q = _c(q, np.uint16)
     B, S, hq, d = q.shape
     out = np.empty((B, S, hq, d), np.float64)
+    cp = None if caps is None else _c(caps, np.int32)
     rc = lib().orc_global_attend(_p(k_pool), _p(v_pool), _p(_c(k_off, np.int64)),
-                                 _p(_c(v_off, np.int64)), cap, dtype, k_scale, v_scale, _p(q),
+                                 _p(_c(v_off, np.int64)), cap, _p(cp), dtype, k_scale, v_scale, _p(q),
                                  _p(_c(q_pos, np.int32)), _p(_c(key_count, np.int32)),
                                  1 if padded else 0, B, S, hq, hkv, d, scale, _p(out))
     _check_rc(rc, "global_attend")

@@ -41,14 +41,14 @@
  *      saturating to +-448; element value = decode(code) * scale
  *      [Thor "Features": FP8 (e4m3) KV cache].
  *
- * Memory layout of one request's region (the layout the library declares;
- * restated here, not shared):
+ * Memory layout of one request's region of `cap` slots (the layout the
+ * library declares; restated here, not shared):
  *   K region: element (slot s, kv head g, dim d) at element index
- *             (s*Hkv + g)*D + d                      (token-major rows)
+ *             (g*cap + s)*D + d                        ([Hkv][cap][D])
  *   V region: element (s, g, d) at element index
- *             ((s/8)*Hkv + g)*D*8 + d*8 + (s%8)     (8-slot blocks)
+ *             ((g*(cap/8) + s/8)*D + d)*8 + (s%8)      ([Hkv][cap/8][D][8])
  *   element size 2 bytes (bf16 bits) or 1 byte (fp8 e4m3 code).
- *   The number of slots `cap` is a multiple of 8.
+ *   cap is a multiple of 8.  Global regions may have a capacity per request.
  */
 #include <math.h>
 #include <stdint.h>
@@ -132,12 +132,12 @@ uint8_t orc_e4m3_encode(uint16_t x_bits, float scale) {
 /* Region layout                                                       */
 /* ------------------------------------------------------------------ */
 
-static size_t k_index(int64_t s, int g, int d, int Hkv, int D) {
-  return ((size_t)s * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d;
+static size_t k_index(int64_t s, int g, int d, int64_t cap, int D) {
+  return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;
 }
 
-static size_t v_index(int64_t s, int g, int d, int Hkv, int D) {
-  return (((size_t)(s / 8) * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d) * 8 +
+static size_t v_index(int64_t s, int g, int d, int64_t cap, int D) {
+  return (((size_t)g * (size_t)(cap / 8) + (size_t)(s / 8)) * (size_t)D + (size_t)d) * 8 +
          (size_t)(s % 8);
 }
 
@@ -167,34 +167,42 @@ static void write_elem(uint8_t* region, size_t idx, int dtype, float scale, uint
 /* Append (a token's K and V go to the same slot)                      */
 /* ------------------------------------------------------------------ */
 
+/* Slots of request b's region: caps[b] when a per-request array is given
+ * (global regions), else cap. */
+static int64_t region_cap(int cap, const int32_t* caps, int b) { return caps ? caps[b] : cap; }
+
 /* Appends tokens t = 0 .. n_new[b]-1 of request b (n_new == NULL: T) at
  * positions pos0[b] + t, one after another.  wrap != 0: slot = pos mod cap
  * (ring [Carat ring section; Gaudi "Our approach"]); wrap == 0: slot = pos,
- * which must be < cap (contiguous global region).  A later token that maps to
- * the same slot overwrites an earlier one, as sequential appends would.
- * k_new / v_new: bf16 bits [B][T][Hkv][D]. */
+ * which must be < the region's capacity (contiguous global region).  A later
+ * token that maps to the same slot overwrites an earlier one, as sequential
+ * appends would.  caps (global regions only, may be NULL): per-request
+ * capacities.  k_new / v_new: bf16 bits [B][T][Hkv][D]. */
 int orc_kv_append(uint8_t* k_base, uint8_t* v_base, const int64_t* k_off, const int64_t* v_off,
-                  int cap, int dtype, float k_scale, float v_scale, const uint16_t* k_new,
-                  const uint16_t* v_new, const int32_t* pos0, const int32_t* n_new, int B, int T,
-                  int Hkv, int D, int wrap) {
+                  int cap, const int32_t* caps, int dtype, float k_scale, float v_scale,
+                  const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos0,
+                  const int32_t* n_new, int B, int T, int Hkv, int D, int wrap) {
   if (cap <= 0 || cap % 8 != 0 || B < 0 || T < 0 || Hkv <= 0 || D <= 0) return ORC_EINVAL;
+  if (wrap && caps) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int n = n_new ? n_new[b] : T;
-    if (n < 0 || n > T || pos0[b] < 0) return ORC_EINVAL;
-    if (!wrap && (int64_t)pos0[b] + n > cap) return ORC_EINVAL;
+    int64_t cb = region_cap(cap, caps, b);
+    if (n < 0 || n > T || pos0[b] < 0 || cb <= 0 || cb % 8 != 0) return ORC_EINVAL;
+    if (!wrap && (int64_t)pos0[b] + n > cb) return ORC_EINVAL;
   }
   for (int b = 0; b < B; ++b) {
     int n = n_new ? n_new[b] : T;
+    int64_t cb = region_cap(cap, caps, b);
     uint8_t* kr = k_base + k_off[b];
     uint8_t* vr = v_base + v_off[b];
     for (int t = 0; t < n; ++t) {
       int64_t p = (int64_t)pos0[b] + t;
-      int64_t s = wrap ? p % cap : p;
+      int64_t s = wrap ? p % cb : p;
       for (int g = 0; g < Hkv; ++g)
         for (int d = 0; d < D; ++d) {
           size_t src = (((size_t)b * T + t) * Hkv + g) * D + d;
-          write_elem(kr, k_index(s, g, d, Hkv, D), dtype, k_scale, k_new[src]);
-          write_elem(vr, v_index(s, g, d, Hkv, D), dtype, v_scale, v_new[src]);
+          write_elem(kr, k_index(s, g, d, cb, D), dtype, k_scale, k_new[src]);
+          write_elem(vr, v_index(s, g, d, cb, D), dtype, v_scale, v_new[src]);
         }
     }
   }
@@ -220,13 +228,14 @@ typedef struct {
   const uint16_t* k_prop; /* [S][Hkv][D] for this request, or NULL */
   const uint16_t* v_prop;
   int g, Hkv, D;
+  int64_t cap;            /* slots of this request's region */
 } unit_src;
 
 static void load_key(const unit_src* u, key_ref kr, double* kd, double* vd) {
   for (int d = 0; d < u->D; ++d) {
     if (kr.slot >= 0) {
-      kd[d] = read_elem(u->kr, k_index(kr.slot, u->g, d, u->Hkv, u->D), u->dtype, u->k_scale);
-      vd[d] = read_elem(u->vr, v_index(kr.slot, u->g, d, u->Hkv, u->D), u->dtype, u->v_scale);
+      kd[d] = read_elem(u->kr, k_index(kr.slot, u->g, d, u->cap, u->D), u->dtype, u->k_scale);
+      vd[d] = read_elem(u->vr, v_index(kr.slot, u->g, d, u->cap, u->D), u->dtype, u->v_scale);
     } else {
       int64_t i = -(kr.slot + 1);
       size_t idx = ((size_t)i * u->Hkv + u->g) * u->D + d;
@@ -335,7 +344,7 @@ int orc_swa_decode(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
     int b = un / Hkv, g = un % Hkv;
     int64_t p = pos[b];
     int nk = (int)(p + 1 < W ? p + 1 : W); /* slots ever written */
-    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D};
+    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D, W};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)G * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)G * D);
@@ -383,7 +392,7 @@ int orc_gqa_verify(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
     int nr = (int)(p0 < W ? p0 : W); /* committed ring slots */
     int nk = nr + S;
     unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale,
-                  k_prop + (size_t)b * S * Hkv * D, v_prop + (size_t)b * S * Hkv * D, g, Hkv, D};
+                  k_prop + (size_t)b * S * Hkv * D, v_prop + (size_t)b * S * Hkv * D, g, Hkv, D, W};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)rows * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)rows * D);
@@ -418,16 +427,18 @@ int orc_gqa_verify(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
  * query position q_pos[b][i] sees keys j <= q_pos[b][i], j < key_count[b].
  * padded != 0 (the pages' form, R4): keys are visited over
  * 0 .. pad64(key_count)-1, the tail contributing zero-weight terms;
- * padded == 0: keys 0 .. key_count-1 only. */
+ * padded == 0: keys 0 .. key_count-1 only.  caps (may be NULL): per-request
+ * region capacities, else every region has `cap` slots. */
 int orc_global_attend(const uint8_t* k_base, const uint8_t* v_base, const int64_t* k_off,
-                      const int64_t* v_off, int cap, int dtype, double k_scale, double v_scale,
-                      const uint16_t* q, const int32_t* q_pos, const int32_t* key_count,
-                      int padded, int B, int S, int Hq, int Hkv, int D, double scale,
-                      double* out) {
+                      const int64_t* v_off, int cap, const int32_t* caps, int dtype,
+                      double k_scale, double v_scale, const uint16_t* q, const int32_t* q_pos,
+                      const int32_t* key_count, int padded, int B, int S, int Hq, int Hkv, int D,
+                      double scale, double* out) {
   if (check_common(B, S, Hq, Hkv, D) || cap <= 0 || cap % 8 != 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int64_t kc = key_count[b], kp = padded ? (kc + 63) / 64 * 64 : kc;
-    if (kc <= 0 || kp > cap) return ORC_EINVAL;
+    int64_t cb = region_cap(cap, caps, b);
+    if (kc <= 0 || kp > cb || cb % 8 != 0) return ORC_EINVAL;
     for (int i = 0; i < S; ++i)
       if (q_pos[b * S + i] < 0) return ORC_EINVAL;
   }
@@ -437,7 +448,8 @@ int orc_global_attend(const uint8_t* k_base, const uint8_t* v_base, const int64_
     int b = un / Hkv, g = un % Hkv;
     int64_t kc = key_count[b];
     int nk = (int)(padded ? (kc + 63) / 64 * 64 : kc);
-    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D};
+    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D,
+                  region_cap(cap, caps, b)};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)rows * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)rows * D);

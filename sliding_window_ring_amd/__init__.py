@@ -38,7 +38,7 @@ class SwrKV(ctypes.Structure):
     """Mirror of `swr_kv` in include/swr.h."""
     _fields_ = [
         ("k_base", ctypes.c_void_p), ("v_base", ctypes.c_void_p),
-        ("k_off", ctypes.c_void_p), ("v_off", ctypes.c_void_p),
+        ("k_off", ctypes.c_void_p), ("v_off", ctypes.c_void_p), ("cap_b", ctypes.c_void_p),
         ("cap", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
@@ -50,11 +50,11 @@ class SwrError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python sliding_window_ring_amd/build.py` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     KV = ctypes.POINTER(SwrKV)
     sig = {
@@ -116,17 +116,21 @@ class KVLayer:
     v_base: torch.Tensor          # device uint8 buffer holding the V regions
     k_off: torch.Tensor           # device int64 [B]
     v_off: torch.Tensor           # device int64 [B]
-    cap: int                      # slots per region (ring: W)
+    cap: int                      # slots per region (ring: W; global: the largest capacity)
     dtype: int = SWR_KV_BF16
     k_scale: float = 1.0
     v_scale: float = 1.0
+    cap_b: Optional[torch.Tensor] = None  # device int32 [B] per-request capacities (global regions)
     _c: SwrKV = field(default=None, repr=False)
 
     def c(self) -> SwrKV:
         _dev(self.k_off, "k_off", torch.int64)
         _dev(self.v_off, "v_off", torch.int64)
+        if self.cap_b is not None:
+            _dev(self.cap_b, "cap_b", torch.int32)
         self._c = SwrKV(self.k_base.data_ptr(), self.v_base.data_ptr(), self.k_off.data_ptr(),
-                        self.v_off.data_ptr(), self.cap, self.dtype, self.k_scale, self.v_scale)
+                        self.v_off.data_ptr(), None if self.cap_b is None else self.cap_b.data_ptr(),
+                        self.cap, self.dtype, self.k_scale, self.v_scale)
         return self._c
 
 

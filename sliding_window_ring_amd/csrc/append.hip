@@ -58,26 +58,30 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
 
   const int n = p.n_new ? p.n_new[b] : p.T;
   if (t >= n) return;
-  if (p.wrap && t < n - p.cap) return;  // a later token of this call owns the slot
+  // slots of this request's region (global regions may carry their own)
+  const int cap = (!p.wrap && p.cap_b) ? max(min(p.cap_b[b], p.cap), 0) : p.cap;
+  if (p.wrap && t < n - cap) return;  // a later token of this call owns the slot
   const long pos = (long)p.pos0[b] + t;
   if (pos < 0) return;
   long slot;
   if (p.wrap) {
-    slot = pos % p.cap;
+    slot = pos % cap;
   } else {
-    if (pos >= p.cap) return;
+    if (pos >= cap) return;
     slot = pos;
   }
 
   const size_t src = (((size_t)b * p.T + t) * p.Hkv + g) * p.D + (size_t)d8 * 8;
   const u32x4 kbits = *reinterpret_cast<const u32x4*>(p.k_new + src);
   const u32x4 vbits = *reinterpret_cast<const u32x4*>(p.v_new + src);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], p.region_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], p.region_bytes);
   constexpr int ESZ = FP8 ? 1 : 2;
-  const uint32_t koff = (uint32_t)(((size_t)slot * p.Hkv + g) * p.D + (size_t)d8 * 8) * ESZ;
-  // V element (slot, g, d) at ((slot/8)*Hkv + g)*D*8 + d*8 + slot%8
-  const uint32_t vrow = (uint32_t)((((size_t)(slot >> 3) * p.Hkv + g) * p.D + (size_t)d8 * 8) * 8 +
+  const uint32_t region_bytes = (uint32_t)cap * (uint32_t)(p.Hkv * p.D * ESZ);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+  // K element (slot, g, d) at (g*cap + slot)*D + d
+  const uint32_t koff = (uint32_t)(((size_t)g * cap + slot) * p.D + (size_t)d8 * 8) * ESZ;
+  // V element (slot, g, d) at ((g*(cap/8) + slot/8)*D + d)*8 + slot%8
+  const uint32_t vrow = (uint32_t)((((size_t)g * (cap >> 3) + (size_t)(slot >> 3)) * p.D + (size_t)d8 * 8) * 8 +
                                    (size_t)(slot & 7));
   if (!FP8) {
     store16(rk, koff, kbits);

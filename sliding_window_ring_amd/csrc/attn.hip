@@ -31,8 +31,14 @@
 
 namespace swr {
 
-template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
-__global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnParams p) {
+// Slots of request b's region (global regions may carry a capacity each).
+__device__ __forceinline__ int region_cap(const AttnParams& p, int b) {
+  return p.cap_b ? max(min(p.cap_b[b], p.cap), 0) : p.cap;
+}
+
+template <int D, int DS, int NCT, int KW, bool FP8, int MODE, int WPE>
+__global__ void __launch_bounds__(64 * (D / DS) * KW) __attribute__((amdgpu_waves_per_eu(WPE)))
+attn_kernel(const AttnParams p) {
   constexpr int DSPLIT = D / DS;
   constexpr int NCH = DS / 32;  // QK k-chunks of 32 dims
   constexpr int NDT = DS / 16;  // PV tiles of 16 dims
@@ -56,6 +62,7 @@ __global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnPara
   const int d_base = ds * DS;
 
   // ---------------------------------------------------------------- keys
+  const int cap_r = region_cap(p, b);
   int n_keys;      // valid region keys (ring: slots ever written; global: key_count)
   int ring_head = 0;  // verify: slot of the newest committed position
   if (MODE == MODE_DECODE) {
@@ -65,7 +72,7 @@ __global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnPara
     n_keys = min(p0, p.cap);
     ring_head = p0 > 0 ? (p0 - 1) % p.cap : 0;
   } else {
-    n_keys = min(p.key_count[b], p.cap);
+    n_keys = min(p.key_count[b], cap_r);
   }
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
@@ -100,8 +107,9 @@ __global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnPara
     }
   }
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], p.region_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], p.region_bytes);
+  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
 
   f32x4 o[NCT][NDT];
   float m_run[NCT], l_run[NCT];
@@ -113,54 +121,104 @@ __global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnPara
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // K and V operand registers.  The loads for tile t+KW are issued as soon as
+  // tile t has consumed the registers (K after the score product, V after the
+  // value product), so every wave keeps a tile's worth of loads in flight
+  // while it computes.
+  bf16x8 kop[2][NCH];
+  bf16x8 vop[NDT];
+
+  auto load_k = [&](int t) {
+    const int kb = t * 32;
+    const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      // A row lr of sub-tile `sub` holds key 8*(lr/4) + 4*sub + lr%4, so the
+      // C rows lane group lq receives are keys 8*lq + 4*sub + 0..3.
+      const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
+      if (!prop_tile) {
+        const uint32_t base = ((uint32_t)(g * cap_r + kb + e) * D + d_base) * ESZ;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t off = base + (uint32_t)((4 * c + lq) * 8 * ESZ);
+          if (FP8)
+            kop[sub][c] = fp8x8_to_bf16x8(load8(rk, off));
+          else
+            kop[sub][c] = as_bf16x8(load16_stream(rk, off));
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kop[sub][c] = bf16x8{};
+        if (e < S) {
+          const uint16_t* src = p.k_prop + ((size_t)(b * S + e) * Hkv + g) * D + d_base;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) kop[sub][c] = *reinterpret_cast<const bf16x8*>(src + (4 * c + lq) * 8);
+        }
+      }
+    }
+  };
+
+  auto load_v = [&](int t) {
+    const int kb = t * 32;
+    const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
+    if (!prop_tile) {
+      const uint32_t vbase = ((uint32_t)((g * (cap_r >> 3) + (kb >> 3) + lq) * D + d_base + lr)) * 8 * ESZ;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t off = vbase + (uint32_t)(dt * 16 * 8 * ESZ);
+        if (FP8)
+          vop[dt] = fp8x8_to_bf16x8(load8(rv, off));
+        else
+          vop[dt] = as_bf16x8(load16_stream(rv, off));
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = d_base + 16 * dt + lr;
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pi = 8 * lq + e;
+          uint16_t bits = 0;
+          if (pi < S) bits = p.v_prop[((size_t)(b * S + pi) * Hkv + g) * D + d];
+          v[e] = __builtin_bit_cast(__bf16, bits);
+        }
+        vop[dt] = v;
+      }
+    }
+  };
+
+  {
+    const int t0 = t_begin + kw;
+    if (t0 < t_end) {
+      load_k(t0);
+      load_v(t0);
+    }
+  }
+
   for (int it = 0; it < n_it; ++it) {
     const int t = t_begin + kw + it * KW;
     if (t >= t_end) {  // wave-uniform; keeps the barrier count equal across waves
       if (DSPLIT > 1) __syncthreads();
       continue;
     }
+    const int t_next = t + KW;
+    const bool has_next = t_next < t_end;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     const int kb = t * 32;
 
     // ------------------------------------------------ scores = K . Q^T
     f32x4 sc[2][NCT];
-    {
-      bf16x8 kop[2][NCH];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        // A row lr of sub-tile `sub` holds key 8*(lr/4) + 4*sub + lr%4, so the
-        // C rows lane group lq receives are keys 8*lq + 4*sub + 0..3.
-        const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
-        if (!prop_tile) {
-          const uint32_t base = ((uint32_t)((kb + e) * Hkv + g) * D + d_base) * ESZ;
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            const uint32_t off = base + (uint32_t)((4 * c + lq) * 8 * ESZ);
-            if (FP8)
-              kop[sub][c] = fp8x8_to_bf16x8(load8(rk, off));
-            else
-              kop[sub][c] = as_bf16x8(load16(rk, off));
-          }
-        } else {
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) kop[sub][c] = bf16x8{};
-          if (e < S) {
-            const uint16_t* src = p.k_prop + ((size_t)(b * S + e) * Hkv + g) * D + d_base;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) kop[sub][c] = *reinterpret_cast<const bf16x8*>(src + (4 * c + lq) * 8);
-          }
-        }
+        for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
+        sc[sub][ct] = acc;
       }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
-          sc[sub][ct] = acc;
-        }
-    }
+    if (has_next) load_k(t_next);
 
     if (DSPLIT > 1) {  // add the head-dim slices of the scores, in slice order
       float* buf = smem + (size_t)((it & 1) * KW + kw) * DSPLIT * RED * 64;
@@ -236,50 +294,22 @@ __global__ void __launch_bounds__(64 * (D / DS) * KW) attn_kernel(const AttnPara
     }
 
     // ------------------------------------------------ O^T += V^T . P^T
-    {
-      bf16x8 vop[NDT];
-      if (!prop_tile) {
-        const uint32_t vbase =
-            ((uint32_t)((((kb >> 3) + lq) * Hkv + g) * D + d_base + lr)) * 8 * ESZ;
+    if (!prop_tile && kb + 32 > n_keys) {  // last region tile: zero values of keys past the valid range
+      u32x4 keep;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const uint32_t off = vbase + (uint32_t)(dt * 16 * 8 * ESZ);
-          if (FP8)
-            vop[dt] = fp8x8_to_bf16x8(load8(rv, off));
-          else
-            vop[dt] = as_bf16x8(load16(rv, off));
-        }
-        if (kb + 32 > n_keys) {  // last region tile: zero values of keys past the valid range
-          u32x4 keep;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int k0 = kb + 8 * lq + 2 * j;
-            keep[j] = (k0 < n_keys ? 0x0000FFFFu : 0u) | (k0 + 1 < n_keys ? 0xFFFF0000u : 0u);
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            vop[dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[dt]) & keep);
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d = d_base + 16 * dt + lr;
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int pi = 8 * lq + e;
-            uint16_t bits = 0;
-            if (pi < S) bits = p.v_prop[((size_t)(b * S + pi) * Hkv + g) * D + d];
-            v[e] = __builtin_bit_cast(__bf16, bits);
-          }
-          vop[dt] = v;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = kb + 8 * lq + 2 * j;
+        keep[j] = (k0 < n_keys ? 0x0000FFFFu : 0u) | (k0 + 1 < n_keys ? 0xFFFF0000u : 0u);
       }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[dt], pop[ct], o[ct][dt]);
+      for (int dt = 0; dt < NDT; ++dt)
+        vop[dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[dt]) & keep);
     }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[dt], pop[ct], o[ct][dt]);
+    if (has_next) load_v(t_next);
   }
 
 #pragma unroll
@@ -384,7 +414,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D,
   else if (MODE == MODE_VERIFY)
     n_keys = min(p.pos[b], p.cap);
   else
-    n_keys = min(p.key_count[b], p.cap);
+    n_keys = min(p.key_count[b], region_cap(p, b));
   n_keys = max(n_keys, 0);
   const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
   const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
@@ -445,13 +475,16 @@ constexpr int kNumCU = 256;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Decode keeps two workgroups' waves resident per SIMD so that one computes
+// while the other's loads are in flight; the grouped shapes need the registers.
 template <int D, int DS, int NCT, int KW, int MODE>
 hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  constexpr int WPE = (MODE == MODE_DECODE) ? 2 : 1;
   if (pl.fp8)
-    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE>), dim3(pl.units * pl.nsplit),
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE, WPE>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);
   else
-    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, false, MODE>), dim3(pl.units * pl.nsplit),
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, false, MODE, WPE>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);
   return hipGetLastError();
 }

@@ -40,10 +40,6 @@ swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
   return SWR_OK;
 }
 
-uint32_t region_bytes(const swr_kv* kv, int Hkv, int D) {
-  return (uint32_t)((uint64_t)kv->cap * Hkv * D * elem_size(kv->dtype));
-}
-
 swr_status to_status(hipError_t e) { return e == hipSuccess ? SWR_OK : SWR_ERR_LAUNCH; }
 
 // Shared validation and launch of the three attention calls.
@@ -58,6 +54,7 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   swr_status st = check_kv(kv, Hkv, D);
   if (st != SWR_OK) return st;
   if (!q || !out || !pos || !aligned16(q) || !aligned16(out)) return SWR_ERR_INVALID;
+  if (mode != swr::MODE_GLOBAL && kv->cap_b) return SWR_ERR_INVALID;  // rings share one window
   if (mode == swr::MODE_VERIFY && (!k_prop || !v_prop || !aligned16(k_prop) || !aligned16(v_prop)))
     return SWR_ERR_INVALID;
   if (mode == swr::MODE_GLOBAL) {
@@ -76,7 +73,7 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   p.v_base = static_cast<const uint8_t*>(kv->v_base);
   p.k_off = kv->k_off;
   p.v_off = kv->v_off;
-  p.region_bytes = region_bytes(kv, Hkv, D);
+  p.cap_b = kv->cap_b;
   p.cap = kv->cap;
   const double ks = kv->dtype == SWR_KV_FP8_E4M3 ? (double)kv->k_scale : 1.0;
   p.qk_scale = (float)((double)scale * ks * kLog2e);
@@ -115,13 +112,14 @@ swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
   swr_status st = check_kv(kv, Hkv, D);
   if (st != SWR_OK) return st;
   if (!k_new || !v_new || !pos0 || !aligned16(k_new) || !aligned16(v_new)) return SWR_ERR_INVALID;
+  if (wrap && kv->cap_b) return SWR_ERR_INVALID;  // rings share one window
   if (B == 0) return SWR_OK;
   swr::AppendParams p{};
   p.k_base = static_cast<uint8_t*>(kv->k_base);
   p.v_base = static_cast<uint8_t*>(kv->v_base);
   p.k_off = kv->k_off;
   p.v_off = kv->v_off;
-  p.region_bytes = region_bytes(kv, Hkv, D);
+  p.cap_b = kv->cap_b;
   p.cap = kv->cap;
   p.wrap = wrap ? 1 : 0;
   p.k_scale = kv->k_scale;

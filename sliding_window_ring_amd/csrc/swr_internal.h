@@ -16,7 +16,7 @@ struct AttnParams {
   const uint8_t* v_base;
   const int64_t* k_off;
   const int64_t* v_off;
-  uint32_t region_bytes;   // bytes of one K (or V) region: cap*Hkv*D*esize
+  const int32_t* cap_b;    // per-request slots (global regions) or null: every region has cap
   int cap;                 // slots per region (ring: W)
   float qk_scale;          // scale * k_scale * log2(e): scores in the base-2 domain
   float v_scale;           // applied to the normalised output
@@ -60,7 +60,7 @@ struct AppendParams {
   uint8_t* v_base;
   const int64_t* k_off;
   const int64_t* v_off;
-  uint32_t region_bytes;
+  const int32_t* cap_b;
   int cap;
   int wrap;
   float k_scale, v_scale;

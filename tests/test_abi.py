@@ -45,7 +45,7 @@ def test_status_strings():
 
 
 def kv(cap=1024, dtype=0, k_scale=1.0, v_scale=1.0, base=FAKE):
-    return swr.SwrKV(base, base, FAKE, FAKE, cap, dtype, k_scale, v_scale)
+    return swr.SwrKV(base, base, FAKE, FAKE, None, cap, dtype, k_scale, v_scale)
 
 
 def decode(k=None, q=FAKE, out=FAKE, pos=FAKE, B=56, Hq=64, Hkv=8, D=256, scale=0.0625, ws=None, wsb=0):
@@ -71,6 +71,9 @@ def test_decode_validation():
     assert decode(scale=float("inf")) == INVALID
     assert swr.lib.swr_swa_decode(None, FAKE, FAKE, FAKE, 1, 8, 1, 64, 1.0, None, 0, None) == INVALID
     assert decode(k=kv(cap=1 << 22)) == UNSUPPORTED  # region beyond 32-bit offsets
+    withcaps = kv()
+    withcaps.cap_b = FAKE
+    assert decode(k=withcaps) == INVALID           # rings share one window
 
 
 def test_decode_small_batch_needs_workspace():

@@ -323,9 +323,9 @@ def test_nonfinite_tail_shows_why_the_tail_is_zeroed():
     x, (kp, vp, ko, vo, cap), q, _ = check_padded_tail_leaves_output_unchanged()
     vp = vp.copy()
     kc = int(x["key_count"][0])
-    vv = vp.view(np.uint16).reshape(cap // 8, 2, 64, 8)
+    vv = vp.view(np.uint16).reshape(2, cap // 8, 64, 8)  # [Hkv][cap/8][D][8]
     for s in range(kc, cap):
-        vv[s // 8, :, :, s % 8] = 0x7FC0
+        vv[:, s // 8, :, s % 8] = 0x7FC0
     padded = oracle.global_attend(kp, vp, ko, vo, cap, oracle.BF16, 1, 1, q, x["q_pos"],
                                   x["key_count"], 2, 0.125, padded=True)
     exact = oracle.global_attend(kp, vp, ko, vo, cap, oracle.BF16, 1, 1, q, x["q_pos"],

@@ -23,9 +23,11 @@ MISTAKES = [
     ("encode divides by scale twice", "double v = fabs(x) / (double)scale;",
      "double v = fabs(x) / (double)scale / (double)scale;"),
     ("V region not blocked",
-     "return (((size_t)(s / 8) * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d) * 8 +\n         (size_t)(s % 8);",
-     "return ((size_t)s * (size_t)Hkv + (size_t)g) * (size_t)D + (size_t)d;"),
-    ("append slot off by one", "int64_t s = wrap ? p % cap : p;", "int64_t s = wrap ? (p + 1) % cap : p;"),
+     "return (((size_t)g * (size_t)(cap / 8) + (size_t)(s / 8)) * (size_t)D + (size_t)d) * 8 +\n         (size_t)(s % 8);",
+     "return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;"),
+    ("K region token-major", "return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;\n}\n\nstatic size_t v_index",
+     "return ((size_t)s * (size_t)8 + (size_t)g) * (size_t)D + (size_t)d;\n}\n\nstatic size_t v_index"),
+    ("append slot off by one", "int64_t s = wrap ? p % cb : p;", "int64_t s = wrap ? (p + 1) % cb : p;"),
     ("dot product drops the last dim", "for (int d = 0; d < D; ++d) dot += q[(size_t)r * D + d] * kd[d];",
      "for (int d = 0; d < D - 1; ++d) dot += q[(size_t)r * D + d] * kd[d];"),
     ("score scale missing", "s[(size_t)r * nk + k] = scale * dot;", "s[(size_t)r * nk + k] = dot;"),

@@ -5,8 +5,8 @@ is its absolute position modulo the window, and a new token reuses the oldest
 slot without moving the rest.  "Improving Decode Throughput on Intel Gaudi 3"
 (Our approach): K and V of a token are written together, so both rings carry
 the same rotation.  The region layout read back here uses numpy reshapes of
-the declared layout (K rows [slot][Hkv][D]; V in 8-slot blocks
-[slot/8][Hkv][D][8]), not the oracle's own index arithmetic.
+the declared layout (K [Hkv][slot][D]; V in 8-slot blocks
+[Hkv][slot/8][D][8]), not the oracle's own index arithmetic.
 """
 import numpy as np
 import pytest
@@ -17,11 +17,14 @@ from helpers import f64
 
 
 def k_view(pool, off, cap, hkv, d):
-    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(cap, hkv, d)
+    """[slot][Hkv][D] view of a K region laid out [Hkv][cap][D]."""
+    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(hkv, cap, d).transpose(1, 0, 2)
 
 
 def v_view(pool, off, cap, hkv, d):
-    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(cap // 8, hkv, d, 8)
+    """[slot][Hkv][D] view of a V region laid out [Hkv][cap/8][D][8]."""
+    v = pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(hkv, cap // 8, d, 8)
+    return v.transpose(1, 3, 0, 2).reshape(cap, hkv, d)
 
 
 def position_tokens(n, hkv, d, base=0):
@@ -49,7 +52,7 @@ def test_slot_is_position_mod_window_one_by_one():
             cands = [j for j in range(t + 1) if j % W == s]
             want = (max(cands) + 1) if cands else 0
             assert np.all(K[s] == want), (t, s)
-            assert np.all(V[s // 8, :, :, s % 8] == -want), (t, s)
+            assert np.all(V[s] == -want), (t, s)
 
 
 def test_batched_append_equals_sequential_appends():
@@ -97,9 +100,9 @@ def test_fp8_append_stores_encoded_codes():
     kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
     off = np.zeros(1, np.int64)
     oracle.kv_append(kp, vp, off, off, W, oracle.FP8, ks, vs, k, v, np.array([14], np.int32))
-    K = kp.reshape(W, hkv, d)
-    V = vp.reshape(W // 8, hkv, d, 8)
+    K = kp.reshape(hkv, W, d)
+    V = vp.reshape(hkv, W // 8, d, 8)
     for t in range(5):
         s = (14 + t) % W
-        assert np.array_equal(K[s], oracle.e4m3_encode(k[0, t], ks))
-        assert np.array_equal(V[s // 8, :, :, s % 8], oracle.e4m3_encode(v[0, t], vs))
+        assert np.array_equal(K[:, s], oracle.e4m3_encode(k[0, t], ks))
+        assert np.array_equal(V[:, s // 8, :, s % 8], oracle.e4m3_encode(v[0, t], vs))
