@@ -1,16 +1,14 @@
-// attn.hip -- grouped-query attention over per-request K/V regions on gfx950.
+// attn.hip -- grouped-query attention over per-request sliding-window rings
+// on gfx950 (global layers: global.hip).
 //
-// One kernel template serves the three attention entry points:
+// One kernel template serves the two ring entry points:
 //   decode  : one query token per request over its sliding-window ring
 //             ("Announcing Carat", ring buffer section; "Improving Decode
 //             Throughput on Intel Gaudi 3", Our approach: the ring is read in
 //             place, in storage order, with no gather and no un-rotation);
 //   verify  : G heads x S proposals per KV head over the ring plus the
 //             proposals ("Announcing Carat", Doing it all in one kernel can be
-//             slower: the grouped rows share one K/V stream);
-//   global  : the same grouped rows over a contiguous region padded to a
-//             multiple of 64 keys with a masked tail ("Announcing Carat",
-//             More FLOPs can be faster).
+//             slower: the grouped rows share one K/V stream).
 //
 // Work unit: one (request, KV head).  A workgroup takes a range of 32-key
 // tiles of one unit (split-K across workgroups when the batch is small); its
@@ -63,16 +61,14 @@ attn_kernel(const AttnParams p) {
 
   // ---------------------------------------------------------------- keys
   const int cap_r = region_cap(p, b);
-  int n_keys;      // valid region keys (ring: slots ever written; global: key_count)
+  int n_keys;         // ring slots ever written
   int ring_head = 0;  // verify: slot of the newest committed position
   if (MODE == MODE_DECODE) {
     n_keys = min(p.pos[b] + 1, p.cap);
-  } else if (MODE == MODE_VERIFY) {
+  } else {
     const int p0 = p.pos[b];
     n_keys = min(p0, p.cap);
     ring_head = p0 > 0 ? (p0 - 1) % p.cap : 0;
-  } else {
-    n_keys = min(p.key_count[b], cap_r);
   }
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
@@ -86,7 +82,7 @@ attn_kernel(const AttnParams p) {
   // Row r = i*G + h: proposal i, head h of the group (query head g*G + h).
   bool row_ok[NCT];
   int row_i[NCT];
-  int row_lim[NCT];  // verify: largest slot age still in the window; global: last visible key
+  int row_lim[NCT];  // verify: largest slot age still in the window
   bf16x8 qop[NCT][NCH];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -95,8 +91,7 @@ attn_kernel(const AttnParams p) {
     const int i = row_ok[ct] ? row / G : 0;
     const int h = row_ok[ct] ? row - i * G : 0;
     row_i[ct] = i;
-    if (MODE == MODE_VERIFY) row_lim[ct] = p.cap - 2 - i;
-    if (MODE == MODE_GLOBAL) row_lim[ct] = min(p.pos[b * S + i], n_keys - 1);
+    row_lim[ct] = p.cap - 2 - i;
     const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -256,17 +251,13 @@ attn_kernel(const AttnParams p) {
           bool vis;
           if (MODE == MODE_DECODE) {
             vis = key < n_keys;
-          } else if (MODE == MODE_VERIFY) {
-            if (prop_tile) {
-              const int pi = 8 * lq + e;  // proposal index
-              vis = pi < S && pi <= row_i[ct];
-            } else {
-              int age = ring_head - key;  // positions back from the newest committed one
-              if (age < 0) age += p.cap;
-              vis = key < n_keys && age <= row_lim[ct];
-            }
+          } else if (prop_tile) {
+            const int pi = 8 * lq + e;  // proposal index
+            vis = pi < S && pi <= row_i[ct];
           } else {
-            vis = key <= row_lim[ct];
+            int age = ring_head - key;  // positions back from the newest committed one
+            if (age < 0) age += p.cap;
+            vis = key < n_keys && age <= row_lim[ct];
           }
           vis = vis && row_ok[ct];
           s[e] = vis ? sc[sub][ct][r] * p.qk_scale : -INFINITY;
@@ -411,10 +402,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D,
   int n_keys;
   if (MODE == MODE_DECODE)
     n_keys = min(p.pos[b] + 1, p.cap);
-  else if (MODE == MODE_VERIFY)
-    n_keys = min(p.pos[b], p.cap);
   else
-    n_keys = min(p.key_count[b], region_cap(p, b));
+    n_keys = min(p.pos[b], p.cap);
   n_keys = max(n_keys, 0);
   const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
   const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
@@ -520,6 +509,11 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
 
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
                     AttnPlan* pl) {
+  if (mode == MODE_GLOBAL) {
+    if (!plan_global(B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
+    pl->fp8 = fp8 ? 1 : 0;
+    return true;
+  }
   if (B < 0 || S < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || cap_or_max_keys < 1) return false;
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
   const int G = Hq / Hkv;
@@ -569,23 +563,16 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
   switch (pl.mode) {
     case MODE_DECODE: e = launch_mode<MODE_DECODE>(pl, p, s); break;
     case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
-    case MODE_GLOBAL: e = launch_mode<MODE_GLOBAL>(pl, p, s); break;
+    case MODE_GLOBAL: return launch_global(pl, p, s);
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || pl.nsplit == 1) return e;
   const long total = (long)pl.units * pl.rows * (pl.D / 4);
   const int blocks = ceil_div(total, 256);
-  switch (pl.mode) {
-    case MODE_DECODE:
-      hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
-      break;
-    case MODE_VERIFY:
-      hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
-      break;
-    default:
-      hipLaunchKernelGGL(combine_kernel<MODE_GLOBAL>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
-      break;
-  }
+  if (pl.mode == MODE_DECODE)
+    hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+  else
+    hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
   return hipGetLastError();
 }
 
