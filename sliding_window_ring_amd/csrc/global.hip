@@ -75,31 +75,12 @@ __global__ void __launch_bounds__(64 * (D / DS)) score_kernel(const AttnParams p
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
   const int cap_r = region_slots(p, b);
-  const int n_keys = unit_keys(p, b);
-  const int nt = (n_keys + 31) >> 5;
-  if (t0 >= nt) return;
   const int d_base = ds * DS;
 
-  bool row_ok[NCT];
-  int row_lim[NCT];  // last key the row may see
-  bf16x8 qop[NCT][NCH];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int row = ct * 16 + lr;
-    row_ok[ct] = row < p.rows;
-    const int i = row_ok[ct] ? row / G : 0;
-    const int h = row_ok[ct] ? row - i * G : 0;
-    row_lim[ct] = min(p.pos[b * S + i], n_keys - 1);
-    const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      qop[ct][c] = row_ok[ct] ? *reinterpret_cast<const bf16x8*>(qrow + (4 * c + lq) * 8) : bf16x8{};
-  }
-
+  // Every load is issued before the key count is known: tiles past the keys
+  // read zeros or slots of the region that are never stored as scores.
   const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
-  // all K loads of the workgroup's tiles up front (tiles past the keys read
-  // zeros or another head's slots; their scores are never stored)
   bf16x8 kop[T][2][NCH];
 #pragma unroll
   for (int u = 0; u < T; ++u)
@@ -115,6 +96,26 @@ __global__ void __launch_bounds__(64 * (D / DS)) score_kernel(const AttnParams p
         kop[u][sub][c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
       }
     }
+  bool row_ok[NCT];
+  int row_i[NCT];
+  bf16x8 qop[NCT][NCH];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int row = ct * 16 + lr;
+    row_ok[ct] = row < p.rows;
+    const int i = row_ok[ct] ? row / G : 0;
+    const int h = row_ok[ct] ? row - i * G : 0;
+    row_i[ct] = i;
+    const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      qop[ct][c] = row_ok[ct] ? *reinterpret_cast<const bf16x8*>(qrow + (4 * c + lq) * 8) : bf16x8{};
+  }
+  const int n_keys = unit_keys(p, b);
+  if (t0 >= ((n_keys + 31) >> 5)) return;
+  int row_lim[NCT];  // last key the row may see
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) row_lim[ct] = min(p.pos[b * S + row_i[ct]], n_keys - 1);
   f32x4 sc[T][2][NCT];
 #pragma unroll
   for (int u = 0; u < T; ++u)
@@ -213,13 +214,11 @@ __global__ void __launch_bounds__(64 * kPvWaves) pv_kernel(const AttnParams p, i
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
   const int cap_r = region_slots(p, b);
-  const int n_keys = unit_keys(p, b);
-  const int nt = (n_keys + 31) >> 5;
-  const int nvalid = (nt + CT - 1) / CT;
-  if (chunk >= nvalid) return;
   const int d0 = ds * DSL;
 
-  // ---- every load of this wave up front
+  // ---- every load of this wave up front, before the key count is known
+  // (scores past the keys are read but never used; the score buffer is
+  // padded to whole chunks, so the reads stay inside the workspace)
   const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
   f32x4 sv[TPW][NCT][2];
@@ -227,7 +226,6 @@ __global__ void __launch_bounds__(64 * kPvWaves) pv_kernel(const AttnParams p, i
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int t = chunk * CT + kw + i * KW;
-    if (t >= nt) continue;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int row = min(ct * 16 + lr, p.rows - 1);
@@ -242,6 +240,10 @@ __global__ void __launch_bounds__(64 * kPvWaves) pv_kernel(const AttnParams p, i
       vv[i][dt] = FP8 ? fp8x8_to_bf16x8(load8(rv, off)) : as_bf16x8(load16_stream(rv, off));
     }
   }
+  const int n_keys = unit_keys(p, b);
+  const int nt = (n_keys + 31) >> 5;
+  const int nvalid = (nt + CT - 1) / CT;
+  if (chunk >= nvalid) return;
 
   // ---- online softmax over the chunk and O^T += V^T . P^T
   f32x4 o[NCT][NDT];
@@ -374,17 +376,38 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int D) {
   const int nvalid = (nt + kChunkTiles - 1) / kChunkTiles;
   if (nvalid <= 1) return;
   const size_t base = (size_t)slice * p.nchunk * p.rows + row;
-  float M = -INFINITY;
-  for (int c = 0; c < nvalid; ++c) M = fmaxf(M, p.ws_pml[(base + (size_t)c * p.rows) * 2]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  // Chunks are merged 16 at a time with every load of a group in flight
+  // together; the running (M, L, O) is rescaled between groups.  The order
+  // of the sums is the chunk order.
+  constexpr int GRP = 16;
+  float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int c = 0; c < nvalid; ++c) {
-    const size_t part = base + (size_t)c * p.rows;
-    const float w = fast_exp2(p.ws_pml[part * 2] - M_use);
-    L += p.ws_pml[part * 2 + 1] * w;
-    O += *reinterpret_cast<const f32x4*>(p.ws_part + part * p.dsl + d4) * w;
+  for (int c0 = 0; c0 < nvalid; c0 += GRP) {
+    float m[GRP], l[GRP];
+    f32x4 o[GRP];
+#pragma unroll
+    for (int k = 0; k < GRP; ++k) {
+      const size_t part = base + (size_t)min(c0 + k, nvalid - 1) * p.rows;
+      m[k] = p.ws_pml[part * 2];
+      l[k] = p.ws_pml[part * 2 + 1];
+      o[k] = *reinterpret_cast<const f32x4*>(p.ws_part + part * p.dsl + d4);
+    }
+    float Mg = M;
+#pragma unroll
+    for (int k = 0; k < GRP; ++k)
+      if (c0 + k < nvalid) Mg = fmaxf(Mg, m[k]);
+    const float M_use = (Mg == -INFINITY) ? 0.f : Mg;
+    const float a = fast_exp2(M - M_use);
+    L *= a;
+    O *= a;
+#pragma unroll
+    for (int k = 0; k < GRP; ++k) {
+      if (c0 + k >= nvalid) break;
+      const float w = fast_exp2(m[k] - M_use);
+      L += l[k] * w;
+      O += o[k] * w;
+    }
+    M = Mg;
   }
   const float inv = L > 0.f ? p.v_scale / L : 0.f;
   const int i = row / p.G, h = row - (row / p.G) * p.G;
@@ -459,7 +482,7 @@ bool plan_global(int B, int S, int Hq, int Hkv, int D, int max_keys, AttnPlan* p
   pl->nds = D / pl->dsl;
   pl->nchunk = cdiv(pl->max_tiles, kChunkTiles);
   pl->grid2 = cdiv((long)pl->units * pl->nchunk, 8) * 8 * pl->nds;
-  const size_t kpad = (size_t)pl->max_tiles * 32;
+  const size_t kpad = (size_t)pl->nchunk * kChunkTiles * 32;  // whole chunks
   size_t off = 0;
   pl->off_scores = off;
   off = align256(off + (size_t)pl->units * rows * kpad * sizeof(float));
@@ -477,7 +500,7 @@ hipError_t launch_global(const AttnPlan& pl, const AttnParams& p0, hipStream_t s
   if (pl.units == 0) return hipSuccess;
   AttnParams p = p0;
   p.max_tiles = pl.max_tiles;
-  p.kpad = pl.max_tiles * 32;
+  p.kpad = pl.nchunk * kChunkTiles * 32;
   p.nchunk = pl.nchunk;
   p.nds = pl.nds;
   p.dsl = pl.dsl;
