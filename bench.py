@@ -146,12 +146,185 @@ def cpu_baseline(seconds: float = 12.0):
                       f"8 KV heads x 256) + the 6005-key global verify; binary64 C oracle, {el:.1f} s"}
 
 
+def _timed(torch, fn, reps, sets):
+    """Average us per call of fn(i) over `reps` calls cycling through `sets`,
+    with events on the current stream around the whole loop."""
+    for i in range(2):
+        fn(i % sets)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i % sets)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def other_workloads(swr, torch):
+    """The remaining workloads, each timed on its own (us per call, GB/s of
+    algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the mixed
+    16-request step (bf16 and fp8, rings and global regions in one pool), and
+    the global verify over every key count 4000..8192."""
+    import synthetic
+
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1003)
+    res = {}
+
+    def randn(*shape):
+        return torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+
+    # --- sliding verify: B=8, W=1024, S=4 proposals, 32 rows per KV head
+    w = synthetic.SWA_VERIFY
+    sets = []
+    for _ in range(8):
+        rb = swr.region_bytes(w.W, w.Hkv, w.D)
+        kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
+        vb = torch.empty_like(kb)
+        off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+        L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
+        p0 = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+        swr.kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
+        q = randn(w.B, w.S, w.Hq, w.D)
+        sets.append((L, randn(w.B, w.S, w.Hkv, w.D), randn(w.B, w.S, w.Hkv, w.D), q, p0, torch.empty_like(q)))
+    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, w.B, w.S, w.Hq, w.Hkv, w.D, w.W)),
+                     dtype=torch.uint8, device=dev)
+    us = _timed(torch, lambda i: swr.gqa_verify(sets[i][0], sets[i][1], sets[i][2], sets[i][3], sets[i][4],
+                                                w.D ** -0.5, out=sets[i][5], ws=ws), 100, len(sets))
+    nbytes = w.B * w.Hkv * w.W * w.D * 4 + 2 * w.B * w.S * w.Hkv * w.D * 2 + 2 * w.B * w.S * w.Hq * w.D * 2
+    res["sliding_verify_b8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                "algorithmic_bytes": nbytes}
+    del sets, ws
+
+    # --- fp8 sliding decode, B=56
+    w = synthetic.SWA_DECODE
+    sets = []
+    for _ in range(3):
+        rb = swr.region_bytes(w.W, w.Hkv, w.D, swr.SWR_KV_FP8_E4M3)
+        kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
+        vb = torch.empty_like(kb)
+        off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+        L = swr.KVLayer(kb, vb, off, off.clone(), w.W, swr.SWR_KV_FP8_E4M3, 4.5 / 448, 4.5 / 448)
+        pos = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+        for half in range(2):
+            swr.kv_append(L, randn(w.B, w.W // 2, w.Hkv, w.D), randn(w.B, w.W // 2, w.Hkv, w.D),
+                          (pos - w.W + 1 + half * (w.W // 2)).to(torch.int32))
+        q = randn(w.B, w.Hq, w.D)
+        sets.append((L, q, pos, torch.empty_like(q)))
+    us = _timed(torch, lambda i: swr.swa_decode(sets[i][0], sets[i][1], sets[i][2], w.Hkv, w.D ** -0.5,
+                                                out=sets[i][3]), 60, len(sets))
+    nbytes = w.B * w.Hkv * w.W * w.D * 2 + 2 * w.B * w.Hq * w.D * 2
+    res["sliding_decode_b56_fp8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                     "algorithmic_bytes": nbytes}
+    del sets
+
+    # --- mixed step: 16 requests, contexts log-uniform [512, 65536], one pool
+    ctx = [int(c) for c in synthetic.mixed_contexts()]
+    B = len(ctx)
+    ws_s, ws_g = synthetic.MIXED_SLIDING, synthetic.MIXED_GLOBAL
+    for dtype, name in ((swr.SWR_KV_BF16, "mixed_step_bf16"), (swr.SWR_KV_FP8_E4M3, "mixed_step_fp8")):
+        esz = 2 if dtype == swr.SWR_KV_BF16 else 1
+        rb_s = swr.region_bytes(ws_s.W, ws_s.Hkv, ws_s.D, dtype)
+        caps = [(c + 1 + 63) // 64 * 64 for c in ctx]
+        total = 2 * B * rb_s + 2 * sum(swr.region_bytes(c, ws_g.Hkv, ws_g.D, dtype) for c in caps) + (1 << 24)
+        pool = swr.Pool(total)
+        rk, rv, gk, gv, gc = [], [], [], [], []
+        for c in ctx:
+            k_off, v_off, _ = pool.alloc_kv(ws_s.W, ws_s.Hkv, ws_s.D, dtype)
+            rk.append(k_off)
+            rv.append(v_off)
+            k_off, v_off, cap = pool.alloc_kv(c + 1, ws_g.Hkv, ws_g.D, dtype, global_layer=True)
+            gk.append(k_off)
+            gv.append(v_off)
+            gc.append(cap)
+        sc = 4.5 / 448 if dtype else 1.0
+        sl = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor(rk, device=dev), torch.tensor(rv, device=dev), ws_s.W,
+                         dtype, sc, sc)
+        gl = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor(gk, device=dev), torch.tensor(gv, device=dev),
+                         max(gc), dtype, sc, sc, cap_b=torch.tensor(gc, device=dev, dtype=torch.int32))
+        pos = torch.tensor(ctx, device=dev, dtype=torch.int32)
+        n_ring = min(ws_s.W, min(ctx) + 1)
+        for b, c in enumerate(ctx):
+            one = torch.tensor([b], device=dev)
+            n = min(c + 1, ws_s.W)
+            ring = swr.KVLayer(pool.buffer, pool.buffer, sl.k_off[one], sl.v_off[one], ws_s.W, dtype, sc, sc)
+            swr.kv_append(ring, randn(1, n, ws_s.Hkv, ws_s.D), randn(1, n, ws_s.Hkv, ws_s.D),
+                          torch.tensor([c - n + 1], device=dev, dtype=torch.int32))
+            glob1 = swr.KVLayer(pool.buffer, pool.buffer, gl.k_off[one], gl.v_off[one], gc[b], dtype, sc, sc)
+            for s0 in range(0, c + 1, 8192):
+                n2 = min(8192, c + 1 - s0)
+                swr.kv_append(glob1, randn(1, n2, ws_g.Hkv, ws_g.D), randn(1, n2, ws_g.Hkv, ws_g.D),
+                              torch.tensor([s0], device=dev, dtype=torch.int32), wrap=False)
+        qs = randn(B, ws_s.Hq, ws_s.D)
+        qg = randn(B, 1, ws_g.Hq, ws_g.D)
+        kc = pos + 1
+        dws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, ws_s.Hq, ws_s.Hkv, ws_s.D,
+                                                      ws_s.W)), dtype=torch.uint8, device=dev)
+        gws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv, ws_g.D,
+                                                      max(ctx) + 1)), dtype=torch.uint8, device=dev)
+        outs, outg = torch.empty_like(qs), torch.empty_like(qg)
+        torch.cuda.synchronize()
+
+        def mixed(_i):
+            swr.swa_decode(sl, qs, pos, ws_s.Hkv, ws_s.D ** -0.5, out=outs, ws=dws)
+            swr.global_attend(gl, qg, pos.view(B, 1), kc, max(ctx) + 1, ws_g.Hkv, ws_g.D ** -0.5, out=outg, ws=gws)
+
+        us = _timed(torch, mixed, 30, 1)
+        nbytes = sum(min(c + 1, ws_s.W) for c in ctx) * ws_s.Hkv * ws_s.D * esz * 2 + \
+            sum(c + 1 for c in ctx) * ws_g.Hkv * ws_g.D * esz * 2 + \
+            2 * B * (ws_s.Hq * ws_s.D + ws_g.Hq * ws_g.D) * 2
+        res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
+                     "contexts": ctx}
+        del pool, sl, gl, dws, gws
+        torch.cuda.synchronize()
+
+    # --- global verify over every key count 4000..8192 (one region of 8192 slots)
+    lo, hi = synthetic.GLOBAL_SWEEP
+    cap = 8192
+    rb = swr.region_bytes(cap, GHKV, GD)
+    kb = torch.zeros(rb, dtype=torch.uint8, device=dev)
+    vb = torch.zeros_like(kb)
+    off = torch.zeros(1, device=dev, dtype=torch.int64)
+    L = swr.KVLayer(kb, vb, off, off.clone(), cap)
+    swr.kv_append(L, randn(1, hi, GHKV, GD), randn(1, hi, GHKV, GD), torch.zeros(1, device=dev, dtype=torch.int32),
+                  wrap=False)
+    counts = torch.arange(lo, hi + 1, device=dev, dtype=torch.int32)
+    qpos = (counts.view(-1, 1) - GS + torch.arange(GS, device=dev, dtype=torch.int32).view(1, -1)).contiguous()
+    q = randn(1, GS, GHKV * GG, GD)
+    out = torch.empty_like(q)
+    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, hi), dtype=torch.uint8,
+                     device=dev)
+    n = counts.numel()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    for i in range(3):
+        swr.global_attend(L, q, qpos[i:i + 1], counts[i:i + 1], hi, GHKV, GD ** -0.5, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        swr.global_attend(L, q, qpos[i:i + 1], counts[i:i + 1], lo + i, GHKV, GD ** -0.5, out=out, ws=ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+    ts = sorted(t)
+    at64 = [t[i] for i in range(n) if (lo + i) % 64 == 0]
+    off64 = [t[i] for i in range(n) if (lo + i) % 64 != 0]
+    res["global_verify_sweep_4000_8192"] = {
+        "counts": n, "us_min": round(ts[0], 2), "us_median": round(ts[n // 2], 2), "us_p99": round(ts[int(n * 0.99)], 2),
+        "us_max": round(ts[-1], 2), "us_mean_at_multiples_of_64": round(sum(at64) / len(at64), 2),
+        "us_mean_elsewhere": round(sum(off64) / len(off64), 2),
+        "note": "one region reused (warm in cache), eager launches: shows the shape is flat in the key count"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -288,6 +461,8 @@ def main():
         },
         "host_wall_s": round(wall, 3),
     }
+    if not args.no_extra:
+        result["other_workloads"] = other_workloads(swr, torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result))

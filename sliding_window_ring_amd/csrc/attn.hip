@@ -464,11 +464,12 @@ constexpr int kNumCU = 256;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Decode keeps two workgroups' waves resident per SIMD so that one computes
-// while the other's loads are in flight; the grouped shapes need the registers.
+// Decode (head dim <= 256) keeps two waves resident per SIMD so that one
+// computes while the other's loads are in flight; the grouped shapes and the
+// 512-dim decode need the registers.
 template <int D, int DS, int NCT, int KW, int MODE>
 hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  constexpr int WPE = (MODE == MODE_DECODE) ? 2 : 1;
+  constexpr int WPE = (MODE == MODE_DECODE && D <= 256) ? 2 : 1;
   if (pl.fp8)
     hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE, WPE>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);

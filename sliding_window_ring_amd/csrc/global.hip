@@ -96,6 +96,8 @@ __global__ void __launch_bounds__(64 * (D / DS)) score_kernel(const AttnParams p
         kop[u][sub][c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
       }
     }
+  // Q rows: loaded unconditionally from a valid row (no divergent branch
+  // between the loads), rows past G*S zeroed by select.
   bool row_ok[NCT];
   int row_i[NCT];
   bf16x8 qop[NCT][NCH];
@@ -103,13 +105,16 @@ __global__ void __launch_bounds__(64 * (D / DS)) score_kernel(const AttnParams p
   for (int ct = 0; ct < NCT; ++ct) {
     const int row = ct * 16 + lr;
     row_ok[ct] = row < p.rows;
-    const int i = row_ok[ct] ? row / G : 0;
-    const int h = row_ok[ct] ? row - i * G : 0;
+    const int rr = row_ok[ct] ? row : 0;
+    const int i = rr / G;
+    const int h = rr - i * G;
     row_i[ct] = i;
     const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      qop[ct][c] = row_ok[ct] ? *reinterpret_cast<const bf16x8*>(qrow + (4 * c + lq) * 8) : bf16x8{};
+    for (int c = 0; c < NCH; ++c) {
+      const u32x4 bits = *reinterpret_cast<const u32x4*>(qrow + (4 * c + lq) * 8);
+      qop[ct][c] = as_bf16x8(row_ok[ct] ? bits : u32x4{0u, 0u, 0u, 0u});
+    }
   }
   const int n_keys = unit_keys(p, b);
   if (t0 >= ((n_keys + 31) >> 5)) return;
@@ -219,8 +224,6 @@ __global__ void __launch_bounds__(64 * kPvWaves) pv_kernel(const AttnParams p, i
   // ---- every load of this wave up front, before the key count is known
   // (scores past the keys are read but never used; the score buffer is
   // padded to whole chunks, so the reads stay inside the workspace)
-  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
   f32x4 sv[TPW][NCT][2];
   bf16x8 vv[TPW][NDT];
 #pragma unroll
@@ -233,6 +236,12 @@ __global__ void __launch_bounds__(64 * kPvWaves) pv_kernel(const AttnParams p, i
       sv[i][ct][0] = *reinterpret_cast<const f32x4*>(src);
       sv[i][ct][1] = *reinterpret_cast<const f32x4*>(src + 4);
     }
+  }
+  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = chunk * CT + kw + i * KW;
     const uint32_t vbase = ((uint32_t)((g * (cap_r >> 3) + t * 4 + lq) * D + d0 + lr)) * 8 * ESZ;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -372,40 +381,49 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int D) {
   const int ds = slice - unit * p.nds;
   const int b = unit / p.Hkv;
   const int g = unit - b * p.Hkv;
-  const int nt = (unit_keys(p, b) + 31) >> 5;
-  const int nvalid = (nt + kChunkTiles - 1) / kChunkTiles;
-  if (nvalid <= 1) return;
   const size_t base = (size_t)slice * p.nchunk * p.rows + row;
-  // Chunks are merged 16 at a time with every load of a group in flight
-  // together; the running (M, L, O) is rescaled between groups.  The order
-  // of the sums is the chunk order.
+  // Chunks are merged 16 at a time, every load of a group in flight together
+  // and issued before the key count is known (addresses are clamped to the
+  // launch's chunk count; chunks past this request's keys are dropped by
+  // select, never multiplied, so whatever they hold cannot leak in).  The
+  // running (M, L, O) is rescaled between groups; sums run in chunk order.
   constexpr int GRP = 16;
   float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nvalid; c0 += GRP) {
+  int nvalid = -1;
+  for (int c0 = 0; c0 < p.nchunk; c0 += GRP) {
     float m[GRP], l[GRP];
     f32x4 o[GRP];
 #pragma unroll
     for (int k = 0; k < GRP; ++k) {
-      const size_t part = base + (size_t)min(c0 + k, nvalid - 1) * p.rows;
+      const size_t part = base + (size_t)min(c0 + k, p.nchunk - 1) * p.rows;
       m[k] = p.ws_pml[part * 2];
       l[k] = p.ws_pml[part * 2 + 1];
       o[k] = *reinterpret_cast<const f32x4*>(p.ws_part + part * p.dsl + d4);
     }
+    if (nvalid < 0) {
+      const int nt = (unit_keys(p, b) + 31) >> 5;
+      nvalid = (nt + kChunkTiles - 1) / kChunkTiles;
+      if (nvalid <= 1) return;  // pass 2 wrote this request's output
+    }
+    if (c0 >= nvalid) break;
     float Mg = M;
 #pragma unroll
-    for (int k = 0; k < GRP; ++k)
-      if (c0 + k < nvalid) Mg = fmaxf(Mg, m[k]);
+    for (int k = 0; k < GRP; ++k) Mg = fmaxf(Mg, c0 + k < nvalid ? m[k] : -INFINITY);
     const float M_use = (Mg == -INFINITY) ? 0.f : Mg;
     const float a = fast_exp2(M - M_use);
     L *= a;
     O *= a;
 #pragma unroll
     for (int k = 0; k < GRP; ++k) {
-      if (c0 + k >= nvalid) break;
+      const bool ok = c0 + k < nvalid;
       const float w = fast_exp2(m[k] - M_use);
-      L += l[k] * w;
-      O += o[k] * w;
+      L += ok ? l[k] * w : 0.f;
+      const f32x4 t = o[k] * w;
+      O[0] += ok ? t[0] : 0.f;
+      O[1] += ok ? t[1] : 0.f;
+      O[2] += ok ? t[2] : 0.f;
+      O[3] += ok ? t[3] : 0.f;
     }
     M = Mg;
   }
