@@ -1,14 +1,18 @@
 // attn.hip -- grouped-query attention over per-request sliding-window rings
 // on gfx950 (global layers: global.hip).
 //
-// One kernel template serves the two ring entry points:
+// One kernel template serves the two ring entry points and long global calls:
 //   decode  : one query token per request over its sliding-window ring
 //             ("Announcing Carat", ring buffer section; "Improving Decode
 //             Throughput on Intel Gaudi 3", Our approach: the ring is read in
 //             place, in storage order, with no gather and no un-rotation);
 //   verify  : G heads x S proposals per KV head over the ring plus the
 //             proposals ("Announcing Carat", Doing it all in one kernel can be
-//             slower: the grouped rows share one K/V stream).
+//             slower: the grouped rows share one K/V stream);
+//   gstream : a global layer over contiguous regions (keys 0 .. key_count-1,
+//             causal by query position) when the regions are long enough that
+//             one streaming pass with a split-K merge beats the three-pass
+//             form of global.hip.
 //
 // Work unit: one (request, KV head).  A workgroup takes a range of 32-key
 // tiles of one unit (split-K across workgroups when the batch is small); its
@@ -61,14 +65,16 @@ attn_kernel(const AttnParams p) {
 
   // ---------------------------------------------------------------- keys
   const int cap_r = region_cap(p, b);
-  int n_keys;         // ring slots ever written
+  int n_keys;         // ring slots ever written; global: keys of the request
   int ring_head = 0;  // verify: slot of the newest committed position
   if (MODE == MODE_DECODE) {
     n_keys = min(p.pos[b] + 1, p.cap);
-  } else {
+  } else if (MODE == MODE_VERIFY) {
     const int p0 = p.pos[b];
     n_keys = min(p0, p.cap);
     ring_head = p0 > 0 ? (p0 - 1) % p.cap : 0;
+  } else {
+    n_keys = min(p.key_count[b], cap_r);
   }
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
@@ -82,7 +88,7 @@ attn_kernel(const AttnParams p) {
   // Row r = i*G + h: proposal i, head h of the group (query head g*G + h).
   bool row_ok[NCT];
   int row_i[NCT];
-  int row_lim[NCT];  // verify: largest slot age still in the window
+  int row_lim[NCT];  // verify: largest slot age still in the window; global: last visible key
   bf16x8 qop[NCT][NCH];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -91,7 +97,7 @@ attn_kernel(const AttnParams p) {
     const int i = row_ok[ct] ? row / G : 0;
     const int h = row_ok[ct] ? row - i * G : 0;
     row_i[ct] = i;
-    row_lim[ct] = p.cap - 2 - i;
+    row_lim[ct] = (MODE == MODE_GSTREAM) ? min(p.pos[b * S + i], n_keys - 1) : p.cap - 2 - i;
     const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -251,6 +257,8 @@ attn_kernel(const AttnParams p) {
           bool vis;
           if (MODE == MODE_DECODE) {
             vis = key < n_keys;
+          } else if (MODE == MODE_GSTREAM) {
+            vis = key <= row_lim[ct];
           } else if (prop_tile) {
             const int pi = 8 * lq + e;  // proposal index
             vis = pi < S && pi <= row_i[ct];
@@ -386,7 +394,12 @@ attn_kernel(const AttnParams p) {
 
 // Split-K merge: out = v_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
 // over the non-empty splits of each (request, KV head).  One thread per four
-// output dims of one row.
+// output dims of one row.  Partials are read sixteen splits at a time, all
+// loads issued before any is used (indices past the last split are clamped
+// to it and their values dropped by selects), so a thread waits for one
+// round trip per sixteen splits instead of one per split.
+constexpr int kCombineBatch = 16;
+
 template <int MODE>
 __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D, int units) {
   const int per_row = D / 4;
@@ -402,22 +415,43 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D,
   int n_keys;
   if (MODE == MODE_DECODE)
     n_keys = min(p.pos[b] + 1, p.cap);
-  else
+  else if (MODE == MODE_VERIFY)
     n_keys = min(p.pos[b], p.cap);
+  else
+    n_keys = min(p.key_count[b], region_cap(p, b));
   n_keys = max(n_keys, 0);
   const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
   const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
 
   const size_t base = (size_t)unit * p.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, p.ws_ml[((base + s) * p.rows + row) * 2]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nvalid; ++s) {
-    const float w = fast_exp2(p.ws_ml[((base + s) * p.rows + row) * 2] - M_use);
-    L += p.ws_ml[((base + s) * p.rows + row) * 2 + 1] * w;
-    O += *reinterpret_cast<const f32x4*>(p.ws_acc + ((base + s) * p.rows + row) * D + d4) * w;
+  for (int s0 = 0; s0 < nvalid; s0 += kCombineBatch) {
+    float m[kCombineBatch], l[kCombineBatch];
+    f32x4 a[kCombineBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const size_t at = (base + min(s0 + j, p.nsplit - 1)) * p.rows + row;
+      m[j] = p.ws_ml[at * 2];
+      l[j] = p.ws_ml[at * 2 + 1];
+      a[j] = *reinterpret_cast<const f32x4*>(p.ws_acc + at * D + d4);
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) mb = (s0 + j < nvalid) ? fmaxf(mb, m[j]) : mb;
+    const float M_new = fmaxf(M, mb);
+    const float M_use = (M_new == -INFINITY) ? 0.f : M_new;
+    const float alpha = fast_exp2(M - M_use);  // 0 while nothing was merged yet
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const bool ok = s0 + j < nvalid;
+      const float w = fast_exp2(m[j] - M_use);
+      L += ok ? l[j] * w : 0.f;
+      O += ok ? a[j] * w : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    M = M_new;
   }
   const float inv = L > 0.f ? p.v_scale / L : 0.f;
   const int i = row / p.G, h = row - (row / p.G) * p.G;
@@ -433,9 +467,11 @@ struct Shape {
   int ds, kw;
 };
 
-// Waves per workgroup: D/ds share each key tile, kw split the tiles.
+// Waves per workgroup: D/ds share each key tile, kw split the tiles.  A
+// global layer streamed in one pass takes the decode shapes for up to 16 rows
+// and the grouped verify shapes above that.
 Shape pick_shape(int mode, int D, int nct) {
-  if (mode == MODE_DECODE) {
+  if (mode == MODE_DECODE || (mode == MODE_GSTREAM && nct == 1)) {
     switch (D) {
       case 64: return {64, 4};
       case 128: return {128, 4};
@@ -464,12 +500,21 @@ constexpr int kNumCU = 256;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Decode (head dim <= 256) keeps two waves resident per SIMD so that one
-// computes while the other's loads are in flight; the grouped shapes and the
-// 512-dim decode need the registers.
+// Two waves stay resident per SIMD, so that one computes while the other's
+// loads are in flight, wherever the kernel then fits the 256 registers of a
+// lane without spilling (per the compiler's resource report): the decode
+// shapes up to 256 dims (128 for a streamed global call, which holds a
+// little more per row), and the grouped shapes with 128-dim slices except
+// the 512-dim verify.  Everything else keeps one wave and all the registers.
+template <int D, int DS, int NCT, int KW, int MODE>
+constexpr int waves_per_simd() {
+  if (NCT == 1) return (KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) ? 2 : 1;
+  return (DS <= 128 && (D <= 256 || MODE != MODE_VERIFY)) ? 2 : 1;
+}
+
 template <int D, int DS, int NCT, int KW, int MODE>
 hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  constexpr int WPE = (MODE == MODE_DECODE && D <= 256) ? 2 : 1;
+  constexpr int WPE = waves_per_simd<D, DS, NCT, KW, MODE>();
   if (pl.fp8)
     hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE, WPE>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);
@@ -479,23 +524,35 @@ hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) 
   return hipGetLastError();
 }
 
+// Decode takes the single-row-tile shapes with key-split waves; verify takes
+// one wave group per tile; a streamed global call takes the decode shapes for
+// up to 16 rows and the grouped shapes above.
 template <int MODE>
 hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  if (MODE == MODE_DECODE) {
-    switch (pl.D) {
-      case 64: return launch_fixed<64, 64, 1, 4, MODE>(pl, p, s);
-      case 128: return launch_fixed<128, 128, 1, 4, MODE>(pl, p, s);
-      case 256: return launch_fixed<256, 256, 1, 4, MODE>(pl, p, s);
-      case 512: return launch_fixed<512, 256, 1, 2, MODE>(pl, p, s);
+  const bool decode_shape = MODE == MODE_DECODE || (MODE == MODE_GSTREAM && pl.nct == 1);
+  if constexpr (MODE != MODE_VERIFY) {
+    if (decode_shape) {
+      switch (pl.D) {
+        case 64: return launch_fixed<64, 64, 1, 4, MODE>(pl, p, s);
+        case 128: return launch_fixed<128, 128, 1, 4, MODE>(pl, p, s);
+        case 256: return launch_fixed<256, 256, 1, 4, MODE>(pl, p, s);
+        case 512: return launch_fixed<512, 256, 1, 2, MODE>(pl, p, s);
+      }
+      return hipErrorInvalidValue;
     }
-  } else if (pl.nct == 1) {
-    switch (pl.D) {
-      case 64: return launch_fixed<64, 64, 1, 1, MODE>(pl, p, s);
-      case 128: return launch_fixed<128, 128, 1, 1, MODE>(pl, p, s);
-      case 256: return launch_fixed<256, 256, 1, 1, MODE>(pl, p, s);
-      case 512: return launch_fixed<512, 256, 1, 1, MODE>(pl, p, s);
+  }
+  if constexpr (MODE == MODE_VERIFY) {
+    if (pl.nct == 1) {
+      switch (pl.D) {
+        case 64: return launch_fixed<64, 64, 1, 1, MODE>(pl, p, s);
+        case 128: return launch_fixed<128, 128, 1, 1, MODE>(pl, p, s);
+        case 256: return launch_fixed<256, 256, 1, 1, MODE>(pl, p, s);
+        case 512: return launch_fixed<512, 256, 1, 1, MODE>(pl, p, s);
+      }
+      return hipErrorInvalidValue;
     }
-  } else {
+  }
+  if constexpr (MODE != MODE_DECODE) {
     switch (pl.D) {
       case 64: return launch_fixed<64, 64, 2, 1, MODE>(pl, p, s);
       case 128: return launch_fixed<128, 128, 2, 1, MODE>(pl, p, s);
@@ -508,12 +565,24 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
 
 }  // namespace
 
+// A global call streams in one pass when the K/V of all its units spans at
+// least this many 32-key tiles: the split-K partials are then a small
+// fraction of the bytes read, and there are enough splits to fill the chip.
+constexpr long kStreamTiles = 2048;
+// Tiles per split of a streamed global call: short enough that the splits of
+// unequal requests balance across the compute units.
+constexpr int kStreamSplitTiles = 16;
+
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
                     AttnPlan* pl) {
   if (mode == MODE_GLOBAL) {
-    if (!plan_global(B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
-    pl->fp8 = fp8 ? 1 : 0;
-    return true;
+    if (B < 0 || Hkv < 1 || cap_or_max_keys < 1) return false;
+    if ((long)B * Hkv * ceil_div(cap_or_max_keys, 32) < kStreamTiles) {
+      if (!plan_global(B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
+      pl->fp8 = fp8 ? 1 : 0;
+      return true;
+    }
+    mode = MODE_GSTREAM;
   }
   if (B < 0 || S < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || cap_or_max_keys < 1) return false;
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
@@ -540,7 +609,11 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
 
   // Split-K across workgroups only when the units alone do not fill the chip.
   int tps = pl->max_tiles;
-  if (pl->units > 0 && pl->units < kNumCU) {
+  if (mode == MODE_GSTREAM) {
+    tps = std::min(std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU)),
+                   kStreamSplitTiles);
+    tps = std::min(tps, pl->max_tiles);
+  } else if (pl->units > 0 && pl->units < kNumCU) {
     if (mode == MODE_DECODE)
       tps = std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU));
     else
@@ -565,6 +638,7 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
     case MODE_DECODE: e = launch_mode<MODE_DECODE>(pl, p, s); break;
     case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
     case MODE_GLOBAL: return launch_global(pl, p, s);
+    case MODE_GSTREAM: e = launch_mode<MODE_GSTREAM>(pl, p, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || pl.nsplit == 1) return e;
@@ -572,8 +646,10 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
   const int blocks = ceil_div(total, 256);
   if (pl.mode == MODE_DECODE)
     hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
-  else
+  else if (pl.mode == MODE_VERIFY)
     hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+  else
+    hipLaunchKernelGGL(combine_kernel<MODE_GSTREAM>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
   return hipGetLastError();
 }
 

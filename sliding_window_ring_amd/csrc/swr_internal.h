@@ -8,7 +8,10 @@
 
 namespace swr {
 
-enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2 };
+// MODE_GLOBAL is what a global-layer call asks for; the planner runs it either
+// as three passes (global.hip) or, for long regions, as MODE_GSTREAM: the
+// single-pass split-K kernel of the ring calls over a contiguous region.
+enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3 };
 
 // Everything an attention launch reads, by value.
 struct AttnParams {
@@ -22,7 +25,7 @@ struct AttnParams {
   float v_scale;           // applied to the normalised output
   const uint16_t* q;       // bf16 [B][S][Hq][D]
   uint16_t* out;           // bf16 [B][S][Hq][D]
-  const int32_t* pos;      // decode: pos[B]; verify: pos0[B]; global: q_pos[B][S]
+  const int32_t* pos;      // decode: pos[B]; verify: pos0[B]; global (both forms): q_pos[B][S]
   const int32_t* key_count;  // global: [B]
   const uint16_t* k_prop;  // verify: bf16 [B][S][Hkv][D]
   const uint16_t* v_prop;

@@ -199,3 +199,45 @@ def test_global_shapes(S, G, D):
              q=synthetic.normal_bf16(g, (kc.size, S, w.Hq, D)))
     out, ref = global_case(w, x, 2048)
     assert_parity(host_f64(out), ref, f"global S={S} G={G} D={D}")
+
+
+# A global call whose units span at least 2048 tiles of 32 keys in all
+# (B * Hkv * ceil(max_key_count / 32)) runs as one streaming split-K pass
+# instead of the three-pass form; these cases sit above that bound, with
+# ragged key counts and query positions that stop short of the last key.
+STREAM_COUNTS = np.array([1, 63, 64, 65, 700, 2000, 4099, 5000], np.int32)
+
+
+def streamed_inputs(S, G, D, seed):
+    kc = STREAM_COUNTS
+    g = synthetic.rng(seed)
+    base = kc[:, None] - S + np.arange(S, dtype=np.int32)[None, :]
+    early = base // 2 + np.arange(kc.size, dtype=np.int32)[:, None] % 3  # causal cut well inside the keys
+    q_pos = np.where((np.arange(kc.size) % 2 == 1)[:, None], early, base)
+    q_pos = np.clip(q_pos, 0, kc[:, None] - 1).astype(np.int32)
+    kmax = int(kc.max())
+    return dict(key_count=kc, q_pos=q_pos, k=synthetic.normal_bf16(g, (kc.size, kmax, 2, D)),
+                v=synthetic.normal_bf16(g, (kc.size, kmax, 2, D)), q=synthetic.normal_bf16(g, (kc.size, S, 2 * G, D)))
+
+
+@pytest.mark.parametrize("S,G,D", [(4, 8, 512), (1, 8, 512), (1, 8, 256), (4, 2, 64), (3, 4, 128)])
+def test_global_streamed_shapes(S, G, D):
+    x = streamed_inputs(S, G, D, seed=36)
+    assert x["key_count"].size * 2 * -(-int(x["key_count"].max()) // 32) >= 2048
+    w = synthetic.Workload("t", B=x["key_count"].size, Hkv=2, G=G, D=D, S=S)
+    out, ref = global_case(w, x, 5056)
+    assert_parity(host_f64(out), ref, f"streamed global S={S} G={G} D={D}")
+
+
+def test_global_streamed_fp8():
+    S, G, D = 4, 8, 512
+    x = streamed_inputs(S, G, D, seed=37)
+    kc, cap = x["key_count"], 5056
+    ks, vs = 4.2 / 448, 3.9 / 448
+    kp, vp, ko, vo = global_pools(x["k"], x["v"], kc, cap, oracle.FP8, ks, vs)
+    scale = D ** -0.5
+    ref = oracle.global_attend(kp, vp, ko, vo, cap, oracle.FP8, ks, vs, x["q"], x["q_pos"], kc, 2, scale)
+    L = layer(kp, vp, ko, vo, cap, oracle.FP8, ks, vs)
+    out = swr.global_attend(L, dev_bf16(x["q"]), dev_i32(x["q_pos"]), dev_i32(kc), int(kc.max()), 2, scale)
+    torch.cuda.synchronize()
+    assert_parity(host_f64(out), ref, "streamed global fp8")
