@@ -26,6 +26,12 @@
 // holds (row l%16, keys 8*(l/16)+0..7) is exactly the P^T fragment it must
 // supply, and the V^T fragment is one 16-byte load from the 8-slot V blocks
 // of the region layout.  No shuffles sit between the two contractions.
+//
+// fp8 K/V are read 16 bytes per lane like bf16 (not 8): a K load covers two
+// 8-dim k chunks, which is a fixed permutation of the head-dim (k) axis that
+// Q takes too; a V load covers the 8 keys of two adjacent dims, which feed
+// two consecutive value tiles (even and odd dims), and the output stores
+// interleave them back.
 #include <algorithm>
 
 #include "swr_device.h"
@@ -62,6 +68,10 @@ attn_kernel(const AttnParams p) {
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
   const int d_base = ds * DS;
+  // Head dim of k element 8*lq + j of QK chunk c (relative to d_base), and
+  // head dim of A row lr of value tile dt (absolute).
+  auto kdim = [&](int c) { return FP8 ? 64 * (c >> 1) + 16 * lq + 8 * (c & 1) : (4 * c + lq) * 8; };
+  auto vdim = [&](int dt) { return FP8 ? d_base + 32 * (dt >> 1) + 2 * lr + (dt & 1) : d_base + 16 * dt + lr; };
 
   // ---------------------------------------------------------------- keys
   const int cap_r = region_cap(p, b);
@@ -102,7 +112,7 @@ attn_kernel(const AttnParams p) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (row_ok[ct])
-        qop[ct][c] = *reinterpret_cast<const bf16x8*>(qrow + (4 * c + lq) * 8);
+        qop[ct][c] = *reinterpret_cast<const bf16x8*>(qrow + kdim(c));
       else
         qop[ct][c] = bf16x8{};
     }
@@ -139,13 +149,16 @@ attn_kernel(const AttnParams p) {
       const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
       if (!prop_tile) {
         const uint32_t base = ((uint32_t)(g * cap_r + kb + e) * D + d_base) * ESZ;
+        if (FP8) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const uint32_t off = base + (uint32_t)((4 * c + lq) * 8 * ESZ);
-          if (FP8)
-            kop[sub][c] = fp8x8_to_bf16x8(load8(rk, off));
-          else
-            kop[sub][c] = as_bf16x8(load16_stream(rk, off));
+          for (int c = 0; c < NCH; c += 2) {
+            const u32x4 w = load16_stream(rk, base + (uint32_t)kdim(c));
+            kop[sub][c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+            kop[sub][c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) kop[sub][c] = as_bf16x8(load16_stream(rk, base + (uint32_t)(kdim(c) * 2)));
         }
       } else {
 #pragma unroll
@@ -153,39 +166,54 @@ attn_kernel(const AttnParams p) {
         if (e < S) {
           const uint16_t* src = p.k_prop + ((size_t)(b * S + e) * Hkv + g) * D + d_base;
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) kop[sub][c] = *reinterpret_cast<const bf16x8*>(src + (4 * c + lq) * 8);
+          for (int c = 0; c < NCH; ++c) kop[sub][c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
         }
       }
     }
+  };
+
+  // Proposal values (bf16, outside the ring) as the V^T operand of tile dt.
+  // Over an fp8 ring the accumulator holds values in units of v_scale, so a
+  // proposal enters as v / v_scale, split into a bf16 head and (second
+  // pass, lo = true) the bf16 remainder: the pair carries it to ~2^-16.
+  auto prop_v = [&](int dt, bool lo) -> bf16x8 {
+    const int d = vdim(dt);
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pi = 8 * lq + e;
+      uint16_t bits = 0;
+      if (pi < S) bits = p.v_prop[((size_t)(b * S + pi) * Hkv + g) * D + d];
+      if (FP8) {
+        const float x = __builtin_bit_cast(float, (uint32_t)bits << 16) * p.inv_v_scale;
+        const __bf16 hi = (__bf16)x;
+        v[e] = lo ? (__bf16)(x - (float)hi) : hi;
+      } else {
+        v[e] = __builtin_bit_cast(__bf16, bits);
+      }
+    }
+    return v;
   };
 
   auto load_v = [&](int t) {
     const int kb = t * 32;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     if (!prop_tile) {
-      const uint32_t vbase = ((uint32_t)((g * (cap_r >> 3) + (kb >> 3) + lq) * D + d_base + lr)) * 8 * ESZ;
+      const uint32_t vblock = (uint32_t)(g * (cap_r >> 3) + (kb >> 3) + lq) * D;
+      if (FP8) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t off = vbase + (uint32_t)(dt * 16 * 8 * ESZ);
-        if (FP8)
-          vop[dt] = fp8x8_to_bf16x8(load8(rv, off));
-        else
-          vop[dt] = as_bf16x8(load16_stream(rv, off));
+        for (int dt = 0; dt < NDT; dt += 2) {
+          const u32x4 w = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
+          vop[dt] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+          vop[dt + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_bf16x8(load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 16));
       }
     } else {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = d_base + 16 * dt + lr;
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int pi = 8 * lq + e;
-          uint16_t bits = 0;
-          if (pi < S) bits = p.v_prop[((size_t)(b * S + pi) * Hkv + g) * D + d];
-          v[e] = __builtin_bit_cast(__bf16, bits);
-        }
-        vop[dt] = v;
-      }
+      for (int dt = 0; dt < NDT; ++dt) vop[dt] = prop_v(dt, false);
     }
   };
 
@@ -244,6 +272,8 @@ attn_kernel(const AttnParams p) {
     }
 
     // ------------------------------------------------ masked online softmax
+    // (proposal keys are bf16 values: no k_scale folded into their scores)
+    const float qs = (FP8 && prop_tile) ? p.qk_scale_prop : p.qk_scale;
     bf16x8 pop[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -268,7 +298,7 @@ attn_kernel(const AttnParams p) {
             vis = key < n_keys && age <= row_lim[ct];
           }
           vis = vis && row_ok[ct];
-          s[e] = vis ? sc[sub][ct][r] * p.qk_scale : -INFINITY;
+          s[e] = vis ? sc[sub][ct][r] * qs : -INFINITY;
         }
       float tmax = s[0];
 #pragma unroll
@@ -308,11 +338,30 @@ attn_kernel(const AttnParams p) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[dt], pop[ct], o[ct][dt]);
+    if (FP8 && prop_tile) {  // remainder of the scaled proposal values
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 vlo = prop_v(dt, true);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o[ct][dt] = mfma16x16x32(vlo, pop[ct], o[ct][dt]);
+      }
+    }
     if (has_next) load_v(t_next);
   }
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) l_run[ct] = sum4lanes(l_run[ct]);
+
+  // The lane's outputs of row tile ct as NDT groups of four consecutive head
+  // dims: group q starts at dim d_base + qdim(q).  bf16 K/V: group dt is tile
+  // dt (dims 16*dt + 4*lq + r).  fp8: tiles 2t and 2t+1 hold the even and
+  // odd dims of 32*t + 8*lq + 0..7; groups 2t and 2t+1 are its two halves.
+  auto qdim = [&](int q) { return FP8 ? 32 * (q >> 1) + 8 * lq + 4 * (q & 1) : 16 * q + 4 * lq; };
+  auto qval = [&](int ct, int q) -> f32x4 {
+    if (!FP8) return o[ct][q];
+    const int t = q & ~1, h = 2 * (q & 1);
+    return f32x4{o[ct][t][h], o[ct][t + 1][h], o[ct][t][h + 1], o[ct][t + 1][h + 1]};
+  };
 
   const size_t part = (size_t)unit * p.nsplit + split;
   if (KW == 1) {
@@ -324,17 +373,17 @@ attn_kernel(const AttnParams p) {
       const int i = row / G, h = row - (row / G) * G;
       if (p.nsplit == 1) {
         const float inv = l_run[ct] > 0.f ? p.v_scale / l_run[ct] : 0.f;
-        uint16_t* dst = p.out + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base + 4 * lq;
+        uint16_t* dst = p.out + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          bf16x4 w = {(__bf16)(o[ct][dt][0] * inv), (__bf16)(o[ct][dt][1] * inv),
-                      (__bf16)(o[ct][dt][2] * inv), (__bf16)(o[ct][dt][3] * inv)};
-          *reinterpret_cast<bf16x4*>(dst + 16 * dt) = w;
+        for (int q = 0; q < NDT; ++q) {
+          const f32x4 v = qval(ct, q);
+          bf16x4 w = {(__bf16)(v[0] * inv), (__bf16)(v[1] * inv), (__bf16)(v[2] * inv), (__bf16)(v[3] * inv)};
+          *reinterpret_cast<bf16x4*>(dst + qdim(q)) = w;
         }
       } else {
-        float* dst = p.ws_acc + (part * p.rows + row) * D + d_base + 4 * lq;
+        float* dst = p.ws_acc + (part * p.rows + row) * D + d_base;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[ct][dt];
+        for (int q = 0; q < NDT; ++q) *reinterpret_cast<f32x4*>(dst + qdim(q)) = qval(ct, q);
         if (ds == 0 && lq == 0) {
           p.ws_ml[(part * p.rows + row) * 2 + 0] = m_run[ct];
           p.ws_ml[(part * p.rows + row) * 2 + 1] = l_run[ct];
@@ -355,9 +404,8 @@ attn_kernel(const AttnParams p) {
         cml[(kw * p.rows + row) * 2 + 1] = l_run[ct];
       }
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4*>(co + (size_t)(kw * p.rows + row) * RS + d_base + 16 * dt + 4 * lq) =
-            o[ct][dt];
+      for (int q = 0; q < NDT; ++q)
+        *reinterpret_cast<f32x4*>(co + (size_t)(kw * p.rows + row) * RS + d_base + qdim(q)) = qval(ct, q);
     }
     __syncthreads();
     const int nchunk = p.rows * (D / 4);
@@ -505,21 +553,24 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // lane without spilling (per the compiler's resource report): the decode
 // shapes up to 256 dims (128 for a streamed global call, which holds a
 // little more per row), and the grouped shapes with 128-dim slices except
-// the 512-dim verify.  Everything else keeps one wave and all the registers.
-template <int D, int DS, int NCT, int KW, int MODE>
+// the 512-dim verify and the fp8 verify above 64 dims.  Everything else
+// keeps one wave and all the registers.
+template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
 constexpr int waves_per_simd() {
   if (NCT == 1) return (KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) ? 2 : 1;
-  return (DS <= 128 && (D <= 256 || MODE != MODE_VERIFY)) ? 2 : 1;
+  if (MODE == MODE_VERIFY) return (D <= 64 || (D <= 256 && !FP8)) ? 2 : 1;
+  return DS <= 128 ? 2 : 1;
 }
 
 template <int D, int DS, int NCT, int KW, int MODE>
 hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  constexpr int WPE = waves_per_simd<D, DS, NCT, KW, MODE>();
+  constexpr int W8 = waves_per_simd<D, DS, NCT, KW, true, MODE>();
+  constexpr int W16 = waves_per_simd<D, DS, NCT, KW, false, MODE>();
   if (pl.fp8)
-    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE, WPE>), dim3(pl.units * pl.nsplit),
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, true, MODE, W8>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);
   else
-    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, false, MODE, WPE>), dim3(pl.units * pl.nsplit),
+    hipLaunchKernelGGL((attn_kernel<D, DS, NCT, KW, false, MODE, W16>), dim3(pl.units * pl.nsplit),
                        dim3(pl.threads), pl.lds_bytes, s, p);
   return hipGetLastError();
 }

@@ -78,6 +78,8 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   const double ks = kv->dtype == SWR_KV_FP8_E4M3 ? (double)kv->k_scale : 1.0;
   p.qk_scale = (float)((double)scale * ks * kLog2e);
   p.v_scale = kv->dtype == SWR_KV_FP8_E4M3 ? kv->v_scale : 1.0f;
+  p.qk_scale_prop = (float)((double)scale * kLog2e);
+  p.inv_v_scale = (float)(1.0 / (double)p.v_scale);
   p.q = static_cast<const uint16_t*>(q);
   p.out = static_cast<uint16_t*>(out);
   p.pos = pos;

@@ -108,14 +108,22 @@ def test_decode_fp8_ring(ks, vs):
     assert_parity(host_f64(out), ref, "fp8 decode")
 
 
+@pytest.mark.parametrize("D,G", [(64, 2), (128, 16), (512, 8)])
+def test_decode_fp8_head_dims(D, G):
+    w = synthetic.Workload("t", B=5, Hkv=2, G=G, D=D, W=128)
+    x = synthetic.sliding_decode(w, seed=25, positions=(0, 31, 127, 128, 900))
+    out, ref = decode_case(w, x, oracle.FP8, 0.011, 0.0097)
+    assert_parity(host_f64(out), ref, f"fp8 decode D={D}")
+
+
 # ------------------------------------------------------------------ verify
 
-def verify_case(w, x):
+def verify_case(w, x, dtype=oracle.BF16, ks=1.0, vs=1.0):
     scale = 1.0 / np.sqrt(w.D)
-    kp, vp, ko, vo = ring_pools(x["k"], x["v"], x["start"], x["n"], w.W)
-    ref = oracle.gqa_verify(kp, vp, ko, vo, w.W, oracle.BF16, 1, 1, x["k_prop"], x["v_prop"], x["q"], x["p0"],
+    kp, vp, ko, vo = ring_pools(x["k"], x["v"], x["start"], x["n"], w.W, dtype, ks, vs)
+    ref = oracle.gqa_verify(kp, vp, ko, vo, w.W, dtype, ks, vs, x["k_prop"], x["v_prop"], x["q"], x["p0"],
                             w.Hkv, scale)
-    L = layer(kp, vp, ko, vo, w.W)
+    L = layer(kp, vp, ko, vo, w.W, dtype, ks, vs)
     out = swr.gqa_verify(L, dev_bf16(x["k_prop"]), dev_bf16(x["v_prop"]), dev_bf16(x["q"]), dev_i32(x["p0"]),
                          scale)
     torch.cuda.synchronize()
@@ -144,14 +152,24 @@ def test_verify_head_dims(D):
     assert_parity(host_f64(out), ref, f"verify D={D}")
 
 
+@pytest.mark.parametrize("D,S,G", [(64, 4, 8), (256, 4, 8), (512, 4, 8), (256, 2, 4)])
+def test_verify_fp8_ring(D, S, G):
+    """fp8 ring history with bf16 proposals (the proposals are not yet in the
+    ring, so they keep the precision they arrive in)."""
+    w = synthetic.Workload("t", B=4, Hkv=2, G=G, D=D, W=256, S=S)
+    x = synthetic.sliding_verify(w, seed=38, positions=(0, 5, 256, 1000))
+    out, ref = verify_case(w, x, oracle.FP8, 0.0102, 0.0089)
+    assert_parity(host_f64(out), ref, f"fp8 verify D={D} S={S} G={G}")
+
+
 # ------------------------------------------------------------------ global
 
-def global_case(w, x, cap):
+def global_case(w, x, cap, dtype=oracle.BF16, ks=1.0, vs=1.0):
     scale = 1.0 / np.sqrt(w.D)
-    kp, vp, ko, vo = global_pools(x["k"], x["v"], x["key_count"], cap)
-    ref = oracle.global_attend(kp, vp, ko, vo, cap, oracle.BF16, 1, 1, x["q"], x["q_pos"], x["key_count"],
+    kp, vp, ko, vo = global_pools(x["k"], x["v"], x["key_count"], cap, dtype, ks, vs)
+    ref = oracle.global_attend(kp, vp, ko, vo, cap, dtype, ks, vs, x["q"], x["q_pos"], x["key_count"],
                                w.Hkv, scale)
-    L = layer(kp, vp, ko, vo, cap)
+    L = layer(kp, vp, ko, vo, cap, dtype, ks, vs)
     out = swr.global_attend(L, dev_bf16(x["q"]), dev_i32(x["q_pos"]), dev_i32(x["key_count"]),
                             int(x["key_count"].max()), w.Hkv, scale)
     torch.cuda.synchronize()
@@ -163,6 +181,12 @@ def test_global_verify_6005_keys():
     out, ref = global_case(w, synthetic.global_verify(w), 6016)
     e = assert_parity(host_f64(out), ref, "global verify 6005")
     print("global verify max-abs %.3e rel-L2 %.3e" % e)
+
+
+def test_global_verify_6005_keys_fp8():
+    w = synthetic.GLOBAL_VERIFY
+    out, ref = global_case(w, synthetic.global_verify(w, seed=39), 6016, oracle.FP8, 0.0099, 0.0108)
+    assert_parity(host_f64(out), ref, "global verify 6005 fp8")
 
 
 def test_global_sweep_subset():
@@ -232,12 +256,6 @@ def test_global_streamed_shapes(S, G, D):
 def test_global_streamed_fp8():
     S, G, D = 4, 8, 512
     x = streamed_inputs(S, G, D, seed=37)
-    kc, cap = x["key_count"], 5056
-    ks, vs = 4.2 / 448, 3.9 / 448
-    kp, vp, ko, vo = global_pools(x["k"], x["v"], kc, cap, oracle.FP8, ks, vs)
-    scale = D ** -0.5
-    ref = oracle.global_attend(kp, vp, ko, vo, cap, oracle.FP8, ks, vs, x["q"], x["q_pos"], kc, 2, scale)
-    L = layer(kp, vp, ko, vo, cap, oracle.FP8, ks, vs)
-    out = swr.global_attend(L, dev_bf16(x["q"]), dev_i32(x["q_pos"]), dev_i32(kc), int(kc.max()), 2, scale)
-    torch.cuda.synchronize()
+    w = synthetic.Workload("t", B=x["key_count"].size, Hkv=2, G=G, D=D, S=S)
+    out, ref = global_case(w, x, 5056, oracle.FP8, 4.2 / 448, 3.9 / 448)
     assert_parity(host_f64(out), ref, "streamed global fp8")
