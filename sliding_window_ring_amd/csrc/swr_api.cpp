@@ -88,7 +88,6 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   p.v_prop = static_cast<const uint16_t*>(v_prop);
   if (pl.mode == swr::MODE_GLOBAL) {
     uint8_t* w = static_cast<uint8_t*>(ws);
-    p.ws_scores = reinterpret_cast<float*>(w + pl.off_scores);
     p.ws_part = reinterpret_cast<float*>(w + pl.off_part);
     p.ws_pml = reinterpret_cast<float*>(w + pl.off_pml);
   } else if (pl.ws_bytes > 0) {

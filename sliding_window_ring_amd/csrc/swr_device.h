@@ -95,6 +95,35 @@ __device__ __forceinline__ float sum4lanes(float v) {
   return v;
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16k .. 16k+15), every
+// lane receiving the result: swaps within quads, then the half-row mirror
+// (quad 0 <-> 1, 2 <-> 3) and the row mirror (half 0 <-> 1).  Each step pairs
+// lanes symmetrically, so all 16 lanes end with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float max16lanes(float v) {
+  v = fmaxf(v, dpp_move<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp_move<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_move<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kDppRowMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float sum16lanes(float v) {
+  v += dpp_move<kDppQuadSwap1>(v);
+  v += dpp_move<kDppQuadSwap2>(v);
+  v += dpp_move<kDppRowHalfMirror>(v);
+  v += dpp_move<kDppRowMirror>(v);
+  return v;
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

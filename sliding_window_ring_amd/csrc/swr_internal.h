@@ -36,15 +36,10 @@ struct AttnParams {
   int B, S, Hq, Hkv, G, rows;
   int nsplit;              // workgroups per (request, KV head)
   int tiles_per_split;     // 32-key tiles each split covers
-  // global layers (two passes: scores, then softmax x V with a split-K merge)
-  float* ws_scores;        // [units][rows][kpad] masked scores, base-2 domain
-  float* ws_part;          // [units][nds][nchunk][rows][dsl] unnormalised outputs
-  float* ws_pml;           // [units][nds][nchunk][rows][2] (max, sum)
-  int max_tiles;           // 32-key tiles of the longest request
-  int kpad;                // max_tiles * 32
-  int nchunk;              // key chunks per unit (chunk = 16 tiles)
-  int nds;                 // value slices of dsl dims
-  int dsl;
+  // global layers, chunked form (a 64-key chunk per workgroup, then a merge)
+  float* ws_part;          // [units][nchunk][rows][D] unnormalised chunk outputs
+  float* ws_pml;           // [units][nchunk][rows][2] (max, sum) of each chunk
+  int nchunk;              // 64-key chunks per unit (of the longest request)
 };
 
 // Launch geometry chosen on the host for one attention call.
@@ -61,16 +56,12 @@ struct AttnPlan {
   size_t ws_bytes;  // 0 when nsplit == 1 (decode, verify)
   size_t lds_bytes;
   int threads;
-  // global layers
-  int g_ds;        // head dims per wave in the score pass
-  int dsl;         // value dims per workgroup in the second pass
-  int nds;         // D / dsl
-  int nchunk;      // 16-tile key chunks
-  int grid2;       // workgroups of the second pass (a multiple of 8 per value slice)
-  size_t off_scores, off_part, off_pml, off_count;  // off_count: end of the workspace
+  // global layers, chunked form
+  int nchunk;      // 64-key chunks per unit
+  size_t off_part, off_pml;  // workspace offsets
 };
 
-// Two-pass global attention (global.hip).
+// Global attention in chunked form (global.hip): per-chunk attention, then a merge.
 bool plan_global(int B, int S, int Hq, int Hkv, int D, int max_keys, AttnPlan* plan);
 hipError_t launch_global(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
 
