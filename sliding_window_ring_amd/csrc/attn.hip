@@ -1,5 +1,5 @@
 // attn.hip -- grouped-query attention over per-request sliding-window rings
-// on gfx950 (global layers: global.hip).
+// on gfx950 (global layers and small-batch verify in chunked form: chunked.hip).
 //
 // One kernel template serves the two ring entry points and long global calls:
 //   decode  : one query token per request over its sliding-window ring
@@ -11,8 +11,8 @@
 //             slower: the grouped rows share one K/V stream);
 //   gstream : a global layer over contiguous regions (keys 0 .. key_count-1,
 //             causal by query position) when the regions are long enough that
-//             one streaming pass with a split-K merge beats the three-pass
-//             form of global.hip.
+//             one streaming pass with a split-K merge beats the chunked form
+//             of chunked.hip.
 //
 // Work unit: one (request, KV head).  A workgroup takes a range of 32-key
 // tiles of one unit (split-K across workgroups when the batch is small); its
@@ -629,11 +629,19 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   if (mode == MODE_GLOBAL) {
     if (B < 0 || Hkv < 1 || cap_or_max_keys < 1) return false;
     if ((long)B * Hkv * ceil_div(cap_or_max_keys, 32) < kStreamTiles) {
-      if (!plan_global(B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
+      if (!plan_chunked(MODE_GLOBAL, B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
       pl->fp8 = fp8 ? 1 : 0;
       return true;
     }
     mode = MODE_GSTREAM;
+  }
+  // A verify whose (request, KV head) units do not fill the chip runs in
+  // chunked form: every chunk's loads in flight at once, instead of a split
+  // that walks its tiles one after another.
+  if (mode == MODE_VERIFY && B >= 0 && Hkv >= 1 && (long)B * Hkv < kNumCU) {
+    if (!plan_chunked(MODE_VERIFY, B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
+    pl->fp8 = fp8 ? 1 : 0;
+    return true;
   }
   if (B < 0 || S < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || cap_or_max_keys < 1) return false;
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
@@ -648,6 +656,7 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   const Shape sh = pick_shape(mode, D, nct);
   if (sh.ds == 0) return false;
   pl->mode = mode;
+  pl->chunked = 0;
   pl->D = D;
   pl->fp8 = fp8 ? 1 : 0;
   pl->ds = sh.ds;
@@ -684,11 +693,11 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
 
 hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   if (pl.units == 0) return hipSuccess;
+  if (pl.chunked) return launch_chunked(pl, p, s);
   hipError_t e;
   switch (pl.mode) {
     case MODE_DECODE: e = launch_mode<MODE_DECODE>(pl, p, s); break;
     case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
-    case MODE_GLOBAL: return launch_global(pl, p, s);
     case MODE_GSTREAM: e = launch_mode<MODE_GSTREAM>(pl, p, s); break;
     default: return hipErrorInvalidValue;
   }

@@ -1,0 +1,618 @@
+// chunked.hip -- grouped attention in chunked form on gfx950: global layers,
+// and sliding-layer verify when the batch is small.
+//
+// "Announcing Carat" (More FLOPs can be faster; Doing it all in one kernel
+// can be slower): the G query heads that share a KV head, times the S
+// proposed positions, form one group of rows; scores over the keys, a masked
+// softmax and a weighted sum of values.  For a global layer the keys are the
+// key_count = context + proposals keys of a contiguous region, the mask is
+// causal by query position, and the key axis is padded to a multiple of 64
+// with the tail masked; the page computes scores, softmax and the value
+// product as separate matrix operations and stores the scores in between.
+// For a sliding layer the keys are the ring's committed slots (in storage
+// order, "Announcing Carat", ring buffer section) plus the S proposals, and
+// the mask is the window by slot age.
+//
+// On MI355X a job of a few tens of MB (24.6 MB of K/V for a 6005-key global
+// verify, 67 MB for a B=8 sliding verify) must be spread over most of the
+// 256 CUs to stream at HBM speed, and each workgroup must put all of its
+// loads in flight at once: a chain of dependent round trips per workgroup,
+// not bandwidth, is what bounds a job this small.  So a block of keys (two
+// of the page's 64-key pads) becomes the unit of work:
+//   pass 1 (chunk_kernel): one workgroup per (request, KV head, 128 keys)
+//     issues every K, V and Q load on entry, then runs the three products of
+//     the page on its chunk -- scores (bf16 MFMA, fp32), the masked softmax
+//     over the chunk, and P x V (bf16 MFMA, fp32) -- with Q, the scores and
+//     P kept in LDS, and writes the chunk's unnormalised rows with their
+//     (max, sum).  In a verify call chunk 0 of each (request, KV head) holds
+//     the proposals (read from their own buffers) and chunks 1.. the ring.
+//   pass 2: merges the chunk partials, weights 2^(m_c - M), sums in a fixed
+//     order, division by the weighted row sum.  With many chunks per row
+//     (global) one workgroup per (request, KV head, row, quarter of the
+//     head dims) splits the chunks over thread groups (merge_grouped); with
+//     few (verify) one thread per four output dims takes every chunk
+//     (merge_flat).
+// The chunk length trades workgroups (CUs pulling K/V) against partial
+// bytes (rows x D fp32 per chunk, written and read back): at 128 keys and
+// 32 rows the partials are a quarter of the K/V bytes.  A merge done by the
+// last-finishing workgroup of pass 1 instead would need a device-scope
+// release fence per workgroup, which writes back the XCD's L2 and costs about
+// as much as the kernel boundary it would save on this chip.
+#include <algorithm>
+
+#include "swr_device.h"
+#include "swr_internal.h"
+
+namespace swr {
+
+namespace {
+
+// Slots of request b's region.  The per-request capacity is read without a
+// branch (a null cap_b reads an in-bounds word of k_off instead, then
+// ignored), so the loads of k_off[b], v_off[b] and the capacity go out
+// together rather than one after another.
+__device__ __forceinline__ int region_slots(const AttnParams& p, int b) {
+  const int32_t* cb = p.cap_b ? p.cap_b : reinterpret_cast<const int32_t*>(p.k_off);
+  const int raw = cb[b];
+  return p.cap_b ? max(min(raw, p.cap), 0) : p.cap;
+}
+
+// Region keys a (request, KV head) attends to: the global key count, or the
+// ring slots holding committed positions (verify: positions < pos0).
+template <int MODE>
+__device__ __forceinline__ int region_keys(const AttnParams& p, int b) {
+  if (MODE == MODE_VERIFY) return max(min(p.pos[b], p.cap), 0);
+  return max(min(p.key_count[b], region_slots(p, b)), 0);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ pass 1
+
+constexpr int kChunkKeys = 128;                 // keys per workgroup of pass 1
+// V loads go out once the chunk's scores are computed rather than on entry:
+// a smaller first burst of requests across all workgroups streams faster,
+// and the value loads still overlap the softmax.
+constexpr bool kLateV = true;
+constexpr int kChunkWaves = kChunkKeys / 8;     // 16 waves: two per 16-key subtile
+
+// Chunks of one (request, KV head) that pass 1 fills, a prefix of the
+// launch's chunks: the region chunks up to the key count (verify: after the
+// proposal chunk).
+template <int MODE>
+__device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
+  const int n = (region_keys<MODE>(p, b) + kChunkKeys - 1) / kChunkKeys;
+  return min(n + (MODE == MODE_VERIFY ? 1 : 0), p.nchunk);
+}
+
+// One workgroup per (request, KV head, chunk), sixteen waves.  Every K and
+// Q load of the workgroup is issued on entry (Q goes to LDS once), the V
+// loads right after the score products (256 KB of K/V in all at D = 512),
+// the K loads before the key count is read: addresses past the region are
+// bounded by the buffer resource, and a chunk past the request's keys only
+// leaves without using what it loaded.
+//   scores   wave (kq, dh) = (w % 8, w / 8): keys 16*kq .. +15 over head-dim
+//            half dh, bf16 MFMA into fp32; the two halves meet in LDS and
+//            are added in half order
+//   softmax  16 lanes per row, eight keys per lane (rows spread over the
+//            waves); masked, max and sum over the chunk by DPP within the
+//            lanes' row, P rounded to bf16 into LDS; the row's (max, sum) go
+//            to the workspace
+//   values   waves w < PVW: O^T(dims w*DPW .. +DPW, rows) = V^T . P^T over
+//            the chunk, bf16 MFMA into fp32; the unnormalised rows go to the
+//            workspace for pass 2 with streaming stores.
+// Masks: global -- key < key_count and key <= q_pos of the row's position;
+// verify ring chunk -- a committed slot no older than W-2-i positions before
+// pos0-1 for proposal i (position pos0+i sees positions >= pos0+i-W+1);
+// verify proposal chunk -- proposal j <= i.  Over an fp8 ring the proposals
+// are bf16 values: their scores take scale * log2(e) without k_scale, and
+// their accumulated values are divided by v_scale (in fp32) before the
+// store, since pass 2 multiplies every chunk by v_scale.
+template <int D, int NCT>
+struct ChunkSmem {
+  float sbuf[2][16 * NCT][kChunkKeys + 4];
+  __attribute__((aligned(16))) __bf16 pbuf[16 * NCT][kChunkKeys + 8];
+  __attribute__((aligned(16))) __bf16 qbuf[16 * NCT][D + 8];
+};
+
+// One chunk of one (request, KV head); every wave of the workgroup calls it
+// with the same arguments.  Returns early (all waves alike) for a chunk past
+// the request's keys; waves without value work return after the softmax.
+template <int D, int NCT, bool FP8, int MODE>
+__device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT>& sm, int unit, int chunk) {
+  constexpr int CK = kChunkKeys;
+  constexpr int NW = kChunkWaves;
+  constexpr int KQ = CK / 16;                        // 16-key subtiles (score waves per half)
+  constexpr int ROWS = 16 * NCT;
+  constexpr int DH = D / 2;                          // head dims per score wave
+  constexpr int NCH = DH / 32;                       // 32-dim k chunks per score wave
+  constexpr int PVW = D / 16 < NW ? D / 16 : NW;     // value waves
+  constexpr int DPW = D / PVW;                       // value dims per value wave
+  constexpr int NDT = DPW / 16;                      // 16-dim value tiles per value wave
+  constexpr int KS = CK / 32;                        // 32-key k steps of the value product
+  constexpr int ESZ = FP8 ? 1 : 2;
+  constexpr bool KPAIR = FP8 && NCH % 2 == 0;        // 16-byte fp8 K loads (two k chunks)
+  constexpr bool VPAIR = FP8 && NDT % 2 == 0;        // 16-byte fp8 V loads (two adjacent dims)
+  constexpr int KPL = CK / 16;                       // keys per softmax lane
+  static_assert(ROWS <= 4 * NW, "one softmax pass covers the rows");
+  auto& sbuf = sm.sbuf;
+  auto& pbuf = sm.pbuf;
+  auto& qbuf = sm.qbuf;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int Hkv = p.Hkv, G = p.G, S = p.S;
+  const int b = unit / Hkv;
+  const int g = unit - b * Hkv;
+  const bool prop = MODE == MODE_VERIFY && chunk == 0;           // the proposals' chunk
+  const int k0 = (MODE == MODE_VERIFY ? chunk - 1 : chunk) * CK;  // region slot of key 0
+  const int64_t k_off = p.k_off[b], v_off = p.v_off[b];
+  const int cap_r = region_slots(p, b);
+  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + k_off, region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + v_off, region_bytes);
+
+  // Head dim (within the wave's half) of k element 8*lq + j of chunk c; with
+  // paired fp8 loads a lane's 16 bytes cover two chunks (a fixed permutation
+  // of the k axis, applied to Q and to bf16 proposal keys as well).
+  auto kdim = [&](int c) { return KPAIR ? 64 * (c >> 1) + 16 * lq + 8 * (c & 1) : (4 * c + lq) * 8; };
+  // Head dim of A row lr of value tile dt (paired fp8: tiles 2t, 2t+1 take
+  // the even and odd dims of one 32-dim block).
+  const int vw = wave < PVW ? wave : 0;
+  auto vdim = [&](int dt) {
+    return vw * DPW + (VPAIR ? 32 * (dt >> 1) + 2 * lr + (dt & 1) : 16 * dt + lr);
+  };
+
+  // ---------------------------------------------------------- loads
+  const int kq = wave % KQ, dh = wave / KQ;
+  bf16x8 kop[NCH];
+  bf16x8 vop[KS][NDT];
+  auto load_v = [&]() {
+    if (wave >= PVW) return;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t vblock = (uint32_t)(g * (cap_r >> 3) + ((k0 + 32 * ks) >> 3) + lq) * D;
+      if (VPAIR) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt += 2) {
+          const u32x4 w = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
+          vop[ks][dt] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+          vop[ks][dt + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t off = (vblock + (uint32_t)vdim(dt)) * 8 * ESZ;
+          vop[ks][dt] = FP8 ? fp8x8_to_bf16x8(load8(rv, off)) : as_bf16x8(load16_stream(rv, off));
+        }
+      }
+    }
+  };
+  if (!prop) {
+    const uint32_t base = ((uint32_t)(g * cap_r + k0 + 16 * kq + lr) * D + dh * DH) * ESZ;
+    if (KPAIR) {
+#pragma unroll
+      for (int c = 0; c < NCH; c += 2) {
+        const u32x4 w = load16_stream(rk, base + (uint32_t)kdim(c));
+        kop[c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+        kop[c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t off = base + (uint32_t)(kdim(c) * ESZ);
+        kop[c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
+      }
+    }
+    if (!kLateV) load_v();
+  } else {
+    // proposals j = 0..S-1 are keys 0..S-1 of the chunk (subtile 0; value
+    // k step 0, lane group 0); every other operand element is zero
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kop[c] = bf16x8{};
+    if (kq == 0 && lr < S) {
+      const uint16_t* src = p.k_prop + ((size_t)(b * S + lr) * Hkv + g) * D + dh * DH;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vop[ks][dt] = bf16x8{};
+    if (wave < PVW && lq == 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bf16x8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint16_t bits = 0;
+          if (j < S) bits = p.v_prop[((size_t)(b * S + j) * Hkv + g) * D + vdim(dt)];
+          v[j] = __builtin_bit_cast(__bf16, bits);
+        }
+        vop[0][dt] = v;
+      }
+    }
+  }
+  // Q of the group's rows, once per workgroup, into LDS (rows past p.rows
+  // load row 0 and store zeros)
+  constexpr int QPIECES = ROWS * D / 8;
+#pragma unroll
+  for (int k = 0; k < (QPIECES + 64 * NW - 1) / (64 * NW); ++k) {
+    const int idx = threadIdx.x + k * 64 * NW;
+    if (idx < QPIECES) {
+      const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
+      const bool ok = row < p.rows;
+      const int rr = ok ? row : 0;
+      const int i = rr / G, h = rr - (rr / G) * G;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d8);
+      *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = ok ? v : bf16x8{};
+    }
+  }
+  // softmax role: slot wave*4 + lane/16 takes row `srow` (slots past the
+  // rows idle), keys KPL*(lane%16) .. of the chunk; a global row's query
+  // position is fetched with the loads
+  const int srow = wave * 4 + lq;
+  const bool srow_ok = srow < p.rows;
+  const int si = (srow_ok ? srow : 0) / G;  // proposal index of the row
+  const int qp = MODE == MODE_GLOBAL ? p.pos[b * S + si] : 0;
+
+  const int n_keys = region_keys<MODE>(p, b);
+  if (!prop && k0 >= n_keys) return;  // past this request's keys (uniform over the workgroup)
+
+  // ---------------------------------------------------------- scores
+  __syncthreads();  // Q in LDS
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      acc = mfma16x16x32(kop[c], *reinterpret_cast<const bf16x8*>(&qbuf[ct * 16 + lr][dh * DH + kdim(c)]), acc);
+    *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][16 * kq + 4 * lq]) = acc;
+  }
+  if (kLateV && !prop) load_v();
+  __syncthreads();
+
+  // ---------------------------------------------------------- softmax
+  const size_t slot = ((size_t)unit * p.nchunk + chunk) * p.rows;
+  const float qs = (FP8 && prop) ? p.qk_scale_prop : p.qk_scale;
+  if (srow < ROWS) {
+    const int kk = KPL * lr;
+    // verify: slot age of the newest committed position, and the oldest age
+    // row i still sees
+    const int ring_head = (MODE == MODE_VERIFY && p.pos[b] > 0) ? (p.pos[b] - 1) % p.cap : 0;
+    const int age_lim = p.cap - 2 - si;
+    float sv[KPL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e4 = 0; e4 < KPL; e4 += 4) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sbuf[0][srow][kk + e4]);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sbuf[1][srow][kk + e4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = kk + e4 + e;  // key of the chunk
+        bool vis;
+        if (MODE == MODE_GLOBAL) {
+          vis = k0 + j < n_keys && k0 + j <= qp;
+        } else if (prop) {
+          vis = j < S && j <= si;
+        } else {
+          int age = ring_head - (k0 + j);
+          if (age < 0) age += p.cap;
+          vis = k0 + j < n_keys && age <= age_lim;
+        }
+        vis = vis && srow_ok;
+        sv[e4 + e] = vis ? (s0[e] + s1[e]) * qs : -INFINITY;
+        mx = fmaxf(mx, sv[e4 + e]);
+      }
+    }
+    const float m = max16lanes(mx);
+    const float m_use = (m == -INFINITY) ? 0.f : m;
+    float ps = 0.f;
+#pragma unroll
+    for (int e4 = 0; e4 < KPL; e4 += 4) {
+      bf16x4 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = (__bf16)fast_exp2(sv[e4 + e] - m_use);
+        ps += (float)pb[e];
+      }
+      *reinterpret_cast<bf16x4*>(&pbuf[srow][kk + e4]) = pb;
+    }
+    const float l = sum16lanes(ps);
+    if (lr == 0 && srow_ok) {
+      p.ws_pml[(slot + srow) * 2 + 0] = m;
+      p.ws_pml[(slot + srow) * 2 + 1] = l;
+    }
+  }
+  __syncthreads();
+  if (wave >= PVW) return;
+
+  // ---------------------------------------------------------- values
+  if (!prop && k0 + CK > n_keys) {  // last chunk: zero values of keys past the count
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 keep;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + 32 * ks + 8 * lq + 2 * j;
+        keep[j] = (kk < n_keys ? 0x0000FFFFu : 0u) | (kk + 1 < n_keys ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        vop[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[ks][dt]) & keep);
+    }
+  }
+  f32x4 o[NCT][NDT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 pt = *reinterpret_cast<const bf16x8*>(&pbuf[ct * 16 + lr][32 * ks + 8 * lq]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[ks][dt], pt, o[ct][dt]);
+    }
+  }
+  // Lane (lr, lq) holds rows ct*16 + lr; group q of four consecutive dims
+  // starts at qdim(q).  Proposal values are bf16, not codes: divided by
+  // v_scale here so that the merge's v_scale restores them.
+  const float vs = (FP8 && prop) ? p.inv_v_scale : 1.f;
+  auto qdim = [&](int q) { return vw * DPW + (VPAIR ? 32 * (q >> 1) + 8 * lq + 4 * (q & 1) : 16 * q + 4 * lq); };
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int row = ct * 16 + lr;
+    if (row >= p.rows) continue;
+    float* dst = p.ws_part + (slot + row) * D;
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) {
+      f32x4 v;
+      if (VPAIR) {
+        const int t = q & ~1, hh = 2 * (q & 1);
+        v = f32x4{o[ct][t][hh], o[ct][t + 1][hh], o[ct][t][hh + 1], o[ct][t + 1][hh + 1]};
+      } else {
+        v = o[ct][q];
+      }
+      __builtin_nontemporal_store(v * vs, reinterpret_cast<f32x4*>(dst + qdim(q)));
+    }
+  }
+}
+
+// Global: workgroup j takes chunk j % nchunk of unit j / nchunk.  Verify:
+// the ring chunks of every unit come first (workgroup j < units*(nchunk-1)
+// takes ring chunk j % (nchunk-1) of unit j / (nchunk-1)) and the small
+// proposal chunks last.
+// Up to 256 head dims two workgroups stay resident per CU (eight waves per
+// SIMD, 64 registers a lane); 512 dims need more registers and keep one.
+template <int D, int NCT, bool FP8, int MODE>
+__global__ void __launch_bounds__(64 * kChunkWaves) __attribute__((amdgpu_waves_per_eu(D <= 256 ? 8 : 4)))
+chunk_kernel(const AttnParams p) {
+  __shared__ ChunkSmem<D, NCT> sm;
+  if (MODE == MODE_VERIFY) {
+    const int nring = p.nchunk - 1;
+    const int ring_wgs = p.B * p.Hkv * nring;
+    if ((int)blockIdx.x < ring_wgs) {
+      const int unit = blockIdx.x / nring;
+      chunk_item<D, NCT, FP8, MODE>(p, sm, unit, 1 + (blockIdx.x - unit * nring));
+    } else {
+      chunk_item<D, NCT, FP8, MODE>(p, sm, blockIdx.x - ring_wgs, 0);
+    }
+  } else {
+    const int unit = blockIdx.x / p.nchunk;
+    chunk_item<D, NCT, FP8, MODE>(p, sm, unit, blockIdx.x - unit * p.nchunk);
+  }
+}
+
+// ------------------------------------------------------------------ pass 2
+
+// Both merges read every chunk's (max, sum, row) loads of a batch together,
+// issued before the request's chunk count is known (chunks past it but
+// inside the launch's chunk count are dropped by select, never multiplied,
+// so whatever they hold cannot leak in), and keep a running (M, L, O)
+// rescaled between batches.
+// out = v_scale * sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 16;
+constexpr int kMaxChunks = 513;  // 65536 region keys (+ a proposal chunk)
+
+struct RunningRow {
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+};
+
+// Adds chunks c = c0 + j*step (j < kMergeBatch, c < nvalid) of the row at
+// `slot0` (+ c*rows), four dims at `d`.  On the first batch the request's
+// chunk count is read after the batch's loads are issued.
+template <int MODE>
+__device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, size_t slot0, int d, int c0,
+                                            int step, bool first, int& nvalid, RunningRow& r) {
+  float m[kMergeBatch], l[kMergeBatch];
+  f32x4 a[kMergeBatch];
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+    a[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c0 + j * step < p.nchunk) {  // past the launch's chunks: no load at all
+      const size_t at = slot0 + (size_t)(c0 + j * step) * p.rows;
+      m[j] = p.ws_pml[at * 2];
+      l[j] = p.ws_pml[at * 2 + 1];
+      a[j] = *reinterpret_cast<const f32x4*>(p.ws_part + at * D + d);
+    }
+  }
+  if (first) nvalid = valid_chunks<MODE>(p, b);
+  float mb = r.M;
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) mb = (c0 + j * step < nvalid) ? fmaxf(mb, m[j]) : mb;
+  const float m_use = (mb == -INFINITY) ? 0.f : mb;
+  const float alpha = fast_exp2(r.M - m_use);  // 0 while nothing was merged
+  r.L *= alpha;
+  r.O *= alpha;
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+    const bool ok = c0 + j * step < nvalid;
+    const float w = fast_exp2(m[j] - m_use);
+    r.L += ok ? l[j] * w : 0.f;
+    r.O += ok ? a[j] * w : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  r.M = mb;
+}
+
+__device__ __forceinline__ void store_row4(const AttnParams& p, int D, int b, int g, int row, int d, float L,
+                                           f32x4 O) {
+  const float inv = L > 0.f ? p.v_scale / L : 0.f;
+  const int i = row / p.G, h = row - (row / p.G) * p.G;
+  bf16x4 w = {(__bf16)(O[0] * inv), (__bf16)(O[1] * inv), (__bf16)(O[2] * inv), (__bf16)(O[3] * inv)};
+  *reinterpret_cast<bf16x4*>(p.out + ((size_t)(b * p.S + i) * p.Hq + g * p.G + h) * D + d) = w;
+}
+
+// Many chunks per row: one workgroup per (request, KV head, row, quarter of
+// the head dims); thread group k of NG takes chunks k, k+NG, ... for its
+// four dims, and the groups are merged in group order through LDS.
+template <int D, int MODE>
+__global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams p) {
+  constexpr int PART = D / 4;                  // dims per workgroup
+  constexpr int TPG = PART / 4;                // threads per group (4 dims each)
+  constexpr int NG = kMergeThreads / TPG;      // chunk groups
+  __shared__ float gml[NG][2];
+  __shared__ __attribute__((aligned(16))) float obuf[NG][PART];
+
+  const int tid = threadIdx.x;
+  const int quarter = blockIdx.x & 3;
+  const int ur = blockIdx.x >> 2;              // unit * rows + row
+  const int unit = ur / p.rows;
+  const int row = ur - unit * p.rows;
+  const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+  const int grp = tid / TPG;
+  const int d = quarter * PART + (tid - grp * TPG) * 4;
+  const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
+
+  RunningRow r;
+  int nvalid = p.nchunk;
+  for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
+    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r);
+  }
+  if (tid - grp * TPG == 0) {
+    gml[grp][0] = r.M;
+    gml[grp][1] = r.L;
+  }
+  *reinterpret_cast<f32x4*>(&obuf[grp][d - quarter * PART]) = r.O;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = gml[0][0];
+#pragma unroll
+  for (int k = 1; k < NG; ++k) Mt = fmaxf(Mt, gml[k][0]);
+  const float mt_use = (Mt == -INFINITY) ? 0.f : Mt;
+  float Lt = 0.f;
+  f32x4 Ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const float w = fast_exp2(gml[k][0] - mt_use);
+    Lt += gml[k][1] * w;
+    Ot += *reinterpret_cast<const f32x4*>(&obuf[k][d - quarter * PART]) * w;
+  }
+  store_row4(p, D, b, g, row, d, Lt, Ot);
+}
+
+// Few chunks per row: one thread per (request, KV head, row, four dims)
+// takes every chunk in order.
+template <int MODE>
+__global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, int D) {
+  const int per_row = D / 4;
+  const int per_unit = p.rows * per_row;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.B * p.Hkv * per_unit) return;
+  const int unit = idx / per_unit;
+  const int rem = idx - unit * per_unit;
+  const int row = rem / per_row;
+  const int d = (rem - row * per_row) * 4;
+  const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+  const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
+
+  RunningRow r;
+  int nvalid = p.nchunk;
+  for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
+    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r);
+  }
+  store_row4(p, D, b, g, row, d, r.L, r.O);
+}
+
+// ------------------------------------------------------------------ host
+
+namespace {
+
+int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+template <int D, int NCT, int MODE>
+hipError_t launch_chunks(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  const dim3 grid(pl.units * pl.nchunk), block(64 * kChunkWaves);
+  if (pl.fp8)
+    hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((chunk_kernel<D, NCT, false, MODE>), grid, block, 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (pl.nchunk > kMergeBatch)
+    hipLaunchKernelGGL((merge_grouped<D, MODE>), dim3(pl.units * pl.rows * 4), dim3(kMergeThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((merge_flat<MODE>), dim3(cdiv((long)pl.units * pl.rows * (D / 4), kMergeThreads)),
+                       dim3(kMergeThreads), 0, s, p, D);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_chunks_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
+  const bool two = pl.nct == 2;
+  switch (pl.D) {
+    case 64: return two ? launch_chunks<64, 2, MODE>(pl, p, s) : launch_chunks<64, 1, MODE>(pl, p, s);
+    case 128: return two ? launch_chunks<128, 2, MODE>(pl, p, s) : launch_chunks<128, 1, MODE>(pl, p, s);
+    case 256: return two ? launch_chunks<256, 2, MODE>(pl, p, s) : launch_chunks<256, 1, MODE>(pl, p, s);
+    case 512: return two ? launch_chunks<512, 2, MODE>(pl, p, s) : launch_chunks<512, 1, MODE>(pl, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, AttnPlan* pl) {
+  if (mode != MODE_GLOBAL && mode != MODE_VERIFY) return false;
+  if (B < 0 || S < 1 || S > 8 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || keys < 1) return false;
+  if (D != 64 && D != 128 && D != 256 && D != 512) return false;
+  const int rows = (Hq / Hkv) * S;
+  if (rows > 32) return false;
+  const int nchunk = cdiv(keys, kChunkKeys) + (mode == MODE_VERIFY ? 1 : 0);
+  if (nchunk > kMaxChunks) return false;
+  pl->mode = mode;
+  pl->chunked = 1;
+  pl->D = D;
+  pl->nct = rows > 16 ? 2 : 1;
+  pl->rows = rows;
+  pl->units = B * Hkv;
+  pl->threads = 64 * kChunkWaves;
+  pl->max_tiles = cdiv(keys, 32);
+  pl->kw = 1;
+  pl->nsplit = 1;
+  pl->tiles_per_split = pl->max_tiles;
+  pl->nchunk = nchunk;
+  size_t off = 0;
+  pl->off_part = off;
+  off = align256(off + (size_t)pl->units * nchunk * rows * D * sizeof(float));
+  pl->off_pml = off;
+  off = align256(off + (size_t)pl->units * nchunk * rows * 2 * sizeof(float));
+  pl->ws_bytes = pl->units > 0 ? off : 0;
+  pl->lds_bytes = 0;
+  return true;
+}
+
+hipError_t launch_chunked(const AttnPlan& pl, const AttnParams& p0, hipStream_t s) {
+  if (pl.units == 0) return hipSuccess;
+  AttnParams p = p0;
+  p.nchunk = pl.nchunk;
+  return pl.mode == MODE_VERIFY ? launch_chunks_mode<MODE_VERIFY>(pl, p, s)
+                                : launch_chunks_mode<MODE_GLOBAL>(pl, p, s);
+}
+
+}  // namespace swr

@@ -86,7 +86,7 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   p.key_count = key_count;
   p.k_prop = static_cast<const uint16_t*>(k_prop);
   p.v_prop = static_cast<const uint16_t*>(v_prop);
-  if (pl.mode == swr::MODE_GLOBAL) {
+  if (pl.chunked) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     p.ws_part = reinterpret_cast<float*>(w + pl.off_part);
     p.ws_pml = reinterpret_cast<float*>(w + pl.off_pml);

@@ -9,8 +9,9 @@
 namespace swr {
 
 // MODE_GLOBAL is what a global-layer call asks for; the planner runs it either
-// as three passes (global.hip) or, for long regions, as MODE_GSTREAM: the
+// in chunked form (chunked.hip) or, for long regions, as MODE_GSTREAM: the
 // single-pass split-K kernel of the ring calls over a contiguous region.
+// MODE_VERIFY runs in chunked form when the batch is small.
 enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3 };
 
 // Everything an attention launch reads, by value.
@@ -36,10 +37,10 @@ struct AttnParams {
   int B, S, Hq, Hkv, G, rows;
   int nsplit;              // workgroups per (request, KV head)
   int tiles_per_split;     // 32-key tiles each split covers
-  // global layers, chunked form (a 64-key chunk per workgroup, then a merge)
+  // chunked form (a chunk of keys per workgroup, then a merge)
   float* ws_part;          // [units][nchunk][rows][D] unnormalised chunk outputs
   float* ws_pml;           // [units][nchunk][rows][2] (max, sum) of each chunk
-  int nchunk;              // 64-key chunks per unit (of the longest request)
+  int nchunk;              // chunks per unit (of the longest request; verify: + the proposals')
 };
 
 // Launch geometry chosen on the host for one attention call.
@@ -56,14 +57,16 @@ struct AttnPlan {
   size_t ws_bytes;  // 0 when nsplit == 1 (decode, verify)
   size_t lds_bytes;
   int threads;
-  // global layers, chunked form
-  int nchunk;      // 64-key chunks per unit
+  // chunked form
+  int chunked;     // 1: chunk_kernel + merge (chunked.hip)
+  int nchunk;      // chunks per unit
   size_t off_part, off_pml;  // workspace offsets
 };
 
-// Global attention in chunked form (global.hip): per-chunk attention, then a merge.
-bool plan_global(int B, int S, int Hq, int Hkv, int D, int max_keys, AttnPlan* plan);
-hipError_t launch_global(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
+// Chunked form (chunked.hip): per-chunk attention, then a merge.  mode is
+// MODE_GLOBAL (keys = max_key_count) or MODE_VERIFY (keys = ring window W).
+bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, AttnPlan* plan);
+hipError_t launch_chunked(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
 
 // Fills *plan; returns false for shapes outside the compiled set.
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,

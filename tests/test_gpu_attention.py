@@ -152,6 +152,16 @@ def test_verify_head_dims(D):
     assert_parity(host_f64(out), ref, f"verify D={D}")
 
 
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+def test_verify_large_batch(dtype):
+    """B * Hkv >= 256 units fill the chip without splitting: the ring kernel
+    takes the call (smaller batches run in chunked form)."""
+    w = synthetic.Workload("t", B=32, Hkv=8, G=8, D=64, W=96, S=4)
+    x = synthetic.sliding_verify(w, seed=40, positions=synthetic.uniform_int(synthetic.rng(41), 0, 400, 32))
+    out, ref = verify_case(w, x, dtype, *((0.0105, 0.0094) if dtype else (1.0, 1.0)))
+    assert_parity(host_f64(out), ref, "large-batch verify")
+
+
 @pytest.mark.parametrize("D,S,G", [(64, 4, 8), (256, 4, 8), (512, 4, 8), (256, 2, 4)])
 def test_verify_fp8_ring(D, S, G):
     """fp8 ring history with bf16 proposals (the proposals are not yet in the
