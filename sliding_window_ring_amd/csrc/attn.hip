@@ -702,6 +702,9 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || pl.nsplit == 1) return e;
+  // many splits per row (a long streamed global call): spread each row's
+  // splits over thread groups instead of one thread walking them all
+  if (pl.mode == MODE_GSTREAM && pl.nsplit > 16) return launch_split_merge(pl, p, s);
   const long total = (long)pl.units * pl.rows * (pl.D / 4);
   const int blocks = ceil_div(total, 256);
   if (pl.mode == MODE_DECODE)

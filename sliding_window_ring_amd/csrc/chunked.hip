@@ -76,11 +76,16 @@ constexpr int kChunkKeys = 128;                 // keys per workgroup of pass 1
 constexpr bool kLateV = true;
 constexpr int kChunkWaves = kChunkKeys / 8;     // 16 waves: two per 16-key subtile
 
-// Chunks of one (request, KV head) that pass 1 fills, a prefix of the
+// Chunks of one (request, KV head) that pass 1 filled, a prefix of the
 // launch's chunks: the region chunks up to the key count (verify: after the
-// proposal chunk).
+// proposal chunk).  A streamed global call (attn.hip) fills one partial per
+// non-empty split of tiles_per_split 32-key tiles, in the same layout.
 template <int MODE>
 __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
+  if (MODE == MODE_GSTREAM) {
+    const int tiles = (region_keys<MODE_GLOBAL>(p, b) + 31) / 32;
+    return min((tiles + p.tiles_per_split - 1) / p.tiles_per_split, p.nchunk);
+  }
   const int n = (region_keys<MODE>(p, b) + kChunkKeys - 1) / kChunkKeys;
   return min(n + (MODE == MODE_VERIFY ? 1 : 0), p.nchunk);
 }
@@ -576,6 +581,22 @@ hipError_t launch_chunks_mode(const AttnPlan& pl, const AttnParams& p, hipStream
 }
 
 }  // namespace
+
+hipError_t launch_split_merge(const AttnPlan& pl, const AttnParams& p0, hipStream_t s) {
+  AttnParams p = p0;
+  p.ws_part = p0.ws_acc;
+  p.ws_pml = p0.ws_ml;
+  p.nchunk = pl.nsplit;
+  const dim3 grid(pl.units * pl.rows * 4), block(kMergeThreads);
+  switch (pl.D) {
+    case 64: hipLaunchKernelGGL((merge_grouped<64, MODE_GSTREAM>), grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((merge_grouped<128, MODE_GSTREAM>), grid, block, 0, s, p); break;
+    case 256: hipLaunchKernelGGL((merge_grouped<256, MODE_GSTREAM>), grid, block, 0, s, p); break;
+    case 512: hipLaunchKernelGGL((merge_grouped<512, MODE_GSTREAM>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, AttnPlan* pl) {
   if (mode != MODE_GLOBAL && mode != MODE_VERIFY) return false;

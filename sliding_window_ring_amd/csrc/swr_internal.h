@@ -67,6 +67,9 @@ struct AttnPlan {
 // MODE_GLOBAL (keys = max_key_count) or MODE_VERIFY (keys = ring window W).
 bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, AttnPlan* plan);
 hipError_t launch_chunked(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
+// Merge of the split partials of a streamed global call (many splits per
+// row), by the chunked form's grouped merge.
+hipError_t launch_split_merge(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
 
 // Fills *plan; returns false for shapes outside the compiled set.
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
