@@ -37,22 +37,29 @@
  *     bf16 with round-to-nearest-even.
  *   - Values that live in device memory (positions, key counts) cannot be
  *     checked on the host; the preconditions stated for them are the
- *     caller's.  Region reads and writes are bounded in hardware to
- *     `cap` slots, so a broken precondition gives wrong numbers, not a fault.
+ *     caller's.  Region reads and writes are bounded in hardware to the
+ *     region, so a broken precondition gives wrong numbers, not a fault.
  *
  * KV region layout (one request, one layer; K and V regions separate; a
- * region has `cap` slots, cap a multiple of 8)
- *   slot s in [0, cap), KV head g in [0, Hkv), dim d in [0, D):
- *     K element (s, g, d) at element index (g*cap + s)*D + d
- *       i.e. K is [Hkv][cap][D]
- *     V element (s, g, d) at element index ((g*(cap/8) + s/8)*D + d)*8 + (s%8)
- *       i.e. V is [Hkv][cap/8][D][8]: blocks of 8 slots
- *   Element size: 2 bytes (SWR_KV_BF16) or 1 byte (SWR_KV_FP8_E4M3).
+ * region has `cap` slots, cap a multiple of 8, and stores S = cap rounded up
+ * to a multiple of 32 slots per KV head)
+ *   slot s in [0, cap), KV head g in [0, Hkv), dim d in [0, D); element size
+ *   e = 2 bytes (SWR_KV_BF16) or 1 byte (SWR_KV_FP8_E4M3); a granule is 16
+ *   bytes = R dims of one slot (R = 8 bf16, 16 fp8):
+ *     K: slot s = 32t + k lies in tile t, half h = (k/4)%2, row
+ *       r = 4*(k/8) + k%4; each half holds its 16 rows granule-major.
+ *       Byte offset of (s, g, d):
+ *         ((g*S + 32t)*D + h*16*D)*e + (d/R)*256 + r*16 + (d%R)*e
+ *       i.e. K is [Hkv][S/32][2][D/R][16][R]
+ *     V element (s, g, d) at element index ((g*(S/8) + s/8)*D + d)*8 + (s%8)
+ *       i.e. V is [Hkv][S/8][D][8]: blocks of 8 slots
  *   Each (request, KV head) reads one contiguous K stream and one contiguous
- *   V stream, which is what HBM streams best.  V is kept in blocks of 8 slots
- *   so that the values of one dim for 8 consecutive slots are contiguous:
- *   that is the operand shape of the gfx950 bf16 matrix instruction along
- *   the key axis.  A region is cap*Hkv*D*element_size bytes
+ *   V stream, which is what HBM streams best.  The K row order inside a tile
+ *   is the key order of the gfx950 bf16 matrix instruction's operand in the
+ *   kernels, and the granule-major halves make each operand load of a lane
+ *   group one contiguous kilobyte.  V is kept in blocks of 8 slots so that
+ *   the values of one dim for 8 consecutive slots are contiguous: the
+ *   operand shape along the key axis.  A region is S*Hkv*D*e bytes
  *   (swr_kv_region_bytes).
  *   Ring regions: cap = W for every request, slot = position mod W.
  *   Global regions: slot = position; each region holds >= pad64(key_count)
@@ -202,7 +209,8 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
  * ranges.  Thread-safe. */
 typedef struct swr_pool swr_pool;
 
-/* Bytes of one K (or V) region of `cap` slots (-1 if the shape is invalid). */
+/* Bytes of one K (or V) region of `cap` slots: (cap rounded up to 32) *
+ * Hkv * D * element size (-1 if the shape is invalid). */
 int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype);
 
 swr_status swr_pool_create(size_t bytes, swr_pool** pool);

@@ -42,12 +42,18 @@
  *      [Thor "Features": FP8 (e4m3) KV cache].
  *
  * Memory layout of one request's region of `cap` slots (the layout the
- * library declares; restated here, not shared):
- *   K region: element (slot s, kv head g, dim d) at element index
- *             (g*cap + s)*D + d                        ([Hkv][cap][D])
+ * library declares; restated here, not shared).  A region stores
+ * S = cap rounded up to a multiple of 32 slots per KV head; an element is
+ * 2 bytes (bf16 bits) or 1 byte (fp8 e4m3 code), and a granule is 16 bytes:
+ * R = 8 bf16 or 16 fp8 consecutive dims of one slot.
+ *   K region: slots in tiles of 32; slot s = 32t + k of head g, dim d, at
+ *             element index
+ *               (g*S + 32t)*D + h*16*D + (d/R)*16*R + r*R + (d%R)
+ *             with h = (k/4)%2 and r = 4*(k/8) + k%4: each tile is two
+ *             halves h of 16 rows r, each half stored granule-major
+ *             ([Hkv][S/32][2][D/R][16][R]).
  *   V region: element (s, g, d) at element index
- *             ((g*(cap/8) + s/8)*D + d)*8 + (s%8)      ([Hkv][cap/8][D][8])
- *   element size 2 bytes (bf16 bits) or 1 byte (fp8 e4m3 code).
+ *             ((g*(S/8) + s/8)*D + d)*8 + (s%8)        ([Hkv][S/8][D][8])
  *   cap is a multiple of 8.  Global regions may have a capacity per request.
  */
 #include <math.h>
@@ -132,21 +138,28 @@ uint8_t orc_e4m3_encode(uint16_t x_bits, float scale) {
 /* Region layout                                                       */
 /* ------------------------------------------------------------------ */
 
-static size_t k_index(int64_t s, int g, int d, int64_t cap, int D) {
-  return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;
+static int elem_size(int dtype) { return dtype == ORC_FP8 ? 1 : 2; }
+
+/* Slots stored per KV head for a region of `cap` slots. */
+static int64_t stored_slots(int64_t cap) { return (cap + 31) / 32 * 32; }
+
+static size_t k_index(int64_t s, int g, int d, int64_t cap, int D, int dtype) {
+  const int64_t S = stored_slots(cap);
+  const int64_t R = 16 / elem_size(dtype); /* dims per 16-byte granule */
+  const int64_t t = s / 32, k = s % 32;
+  const int64_t h = (k / 4) % 2, r = 4 * (k / 8) + k % 4;
+  return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D + (d / R) * 16 * R + r * R + d % R);
 }
 
 static size_t v_index(int64_t s, int g, int d, int64_t cap, int D) {
-  return (((size_t)g * (size_t)(cap / 8) + (size_t)(s / 8)) * (size_t)D + (size_t)d) * 8 +
-         (size_t)(s % 8);
+  const int64_t S = stored_slots(cap);
+  return (size_t)((((int64_t)g * (S / 8) + s / 8) * D + d) * 8 + s % 8);
 }
-
-static int elem_size(int dtype) { return dtype == ORC_FP8 ? 1 : 2; }
 
 /* Bytes of one K (or V) region holding `cap` slots. */
 int64_t orc_region_bytes(int cap, int Hkv, int D, int dtype) {
   if (cap <= 0 || cap % 8 != 0 || Hkv <= 0 || D <= 0) return -1;
-  return (int64_t)cap * Hkv * D * elem_size(dtype);
+  return stored_slots(cap) * Hkv * D * elem_size(dtype);
 }
 
 static double read_elem(const uint8_t* region, size_t idx, int dtype, double scale) {
@@ -201,7 +214,7 @@ int orc_kv_append(uint8_t* k_base, uint8_t* v_base, const int64_t* k_off, const 
       for (int g = 0; g < Hkv; ++g)
         for (int d = 0; d < D; ++d) {
           size_t src = (((size_t)b * T + t) * Hkv + g) * D + d;
-          write_elem(kr, k_index(s, g, d, cb, D), dtype, k_scale, k_new[src]);
+          write_elem(kr, k_index(s, g, d, cb, D, dtype), dtype, k_scale, k_new[src]);
           write_elem(vr, v_index(s, g, d, cb, D), dtype, v_scale, v_new[src]);
         }
     }
@@ -234,7 +247,7 @@ typedef struct {
 static void load_key(const unit_src* u, key_ref kr, double* kd, double* vd) {
   for (int d = 0; d < u->D; ++d) {
     if (kr.slot >= 0) {
-      kd[d] = read_elem(u->kr, k_index(kr.slot, u->g, d, u->cap, u->D), u->dtype, u->k_scale);
+      kd[d] = read_elem(u->kr, k_index(kr.slot, u->g, d, u->cap, u->D, u->dtype), u->dtype, u->k_scale);
       vd[d] = read_elem(u->vr, v_index(kr.slot, u->g, d, u->cap, u->D), u->dtype, u->v_scale);
     } else {
       int64_t i = -(kr.slot + 1);

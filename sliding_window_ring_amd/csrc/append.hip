@@ -8,8 +8,9 @@
 // one rotation.  Global regions use slot = position.
 //
 // One thread moves 8 consecutive head dims of one (request, token, KV head):
-// one 16-byte read of K and of V, one 16-byte (bf16) or 8-byte (fp8) K row
-// store, and eight 2-byte / 1-byte V stores into the 8-slot V blocks.
+// one 16-byte read of K and of V, one 16-byte (bf16) or 8-byte (fp8) store
+// into the slot's K granule, and eight 2-byte / 1-byte V stores into the
+// 8-slot V blocks (region layout: swr_device.h).
 // Stores go through bounded buffer resources: a slot outside the region is
 // dropped by the hardware instead of written.
 #include "swr_device.h"
@@ -75,13 +76,17 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
   const u32x4 kbits = *reinterpret_cast<const u32x4*>(p.k_new + src);
   const u32x4 vbits = *reinterpret_cast<const u32x4*>(p.v_new + src);
   constexpr int ESZ = FP8 ? 1 : 2;
-  const uint32_t region_bytes = (uint32_t)cap * (uint32_t)(p.Hkv * p.D * ESZ);
+  const int S = stored_slots(cap);
+  const uint32_t region_bytes = (uint32_t)S * (uint32_t)(p.Hkv * p.D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
-  // K element (slot, g, d) at (g*cap + slot)*D + d
-  const uint32_t koff = (uint32_t)(((size_t)g * cap + slot) * p.D + (size_t)d8 * 8) * ESZ;
-  // V element (slot, g, d) at ((g*(cap/8) + slot/8)*D + d)*8 + slot%8
-  const uint32_t vrow = (uint32_t)((((size_t)g * (cap >> 3) + (size_t)(slot >> 3)) * p.D + (size_t)d8 * 8) * 8 +
+  // K: this thread's 8 dims are one bf16 granule, or half an fp8 granule
+  const int k32 = (int)(slot & 31);
+  const uint32_t koff = k_half_base(g, S, (int)(slot & ~31L), (k32 >> 2) & 1, p.D, ESZ) +
+                        (uint32_t)((FP8 ? d8 >> 1 : d8) * 256 + (4 * (k32 >> 3) + (k32 & 3)) * 16 +
+                                   (FP8 ? (d8 & 1) * 8 : 0));
+  // V element (slot, g, d) at ((g*(S/8) + slot/8)*D + d)*8 + slot%8
+  const uint32_t vrow = (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * p.D + (size_t)d8 * 8) * 8 +
                                    (size_t)(slot & 7));
   if (!FP8) {
     store16(rk, koff, kbits);

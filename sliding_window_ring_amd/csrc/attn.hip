@@ -25,7 +25,9 @@
 // Keys are laid out on the MFMA k axis so that the score fragment a lane
 // holds (row l%16, keys 8*(l/16)+0..7) is exactly the P^T fragment it must
 // supply, and the V^T fragment is one 16-byte load from the 8-slot V blocks
-// of the region layout.  No shuffles sit between the two contractions.
+// of the region layout.  No shuffles sit between the two contractions.  K
+// is stored in that same key order (swr_device.h), so each K operand load of
+// a lane group is 1 KB of contiguous memory.
 //
 // fp8 K/V are read 16 bytes per lane like bf16 (not 8): a K load covers two
 // 8-dim k chunks, which is a fixed permutation of the head-dim (k) axis that
@@ -118,7 +120,8 @@ attn_kernel(const AttnParams p) {
     }
   }
 
-  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
+  const int S_r = stored_slots(cap_r);  // slots stored per KV head (region layout: swr_device.h)
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(Hkv * D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
 
@@ -145,20 +148,24 @@ attn_kernel(const AttnParams p) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       // A row lr of sub-tile `sub` holds key 8*(lr/4) + 4*sub + lr%4, so the
-      // C rows lane group lq receives are keys 8*lq + 4*sub + 0..3.
+      // C rows lane group lq receives are keys 8*lq + 4*sub + 0..3.  In the
+      // region that key is row lr of half `sub` of the tile: the lane reads
+      // 16 bytes of granule (d_base + kdim(c)) / R of that row.
       const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
       if (!prop_tile) {
-        const uint32_t base = ((uint32_t)(g * cap_r + kb + e) * D + d_base) * ESZ;
+        constexpr int R = FP8 ? 16 : 8;  // dims per 16-byte granule
+        const uint32_t hb = k_half_base(g, S_r, kb, sub, D, ESZ) + (uint32_t)(lr * 16);
         if (FP8) {
 #pragma unroll
           for (int c = 0; c < NCH; c += 2) {
-            const u32x4 w = load16_stream(rk, base + (uint32_t)kdim(c));
+            const u32x4 w = load16_stream(rk, hb + (uint32_t)((d_base + kdim(c)) / R) * 256);
             kop[sub][c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
             kop[sub][c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) kop[sub][c] = as_bf16x8(load16_stream(rk, base + (uint32_t)(kdim(c) * 2)));
+          for (int c = 0; c < NCH; ++c)
+            kop[sub][c] = as_bf16x8(load16_stream(rk, hb + (uint32_t)((d_base + kdim(c)) / R) * 256));
         }
       } else {
 #pragma unroll
@@ -199,7 +206,7 @@ attn_kernel(const AttnParams p) {
     const int kb = t * 32;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     if (!prop_tile) {
-      const uint32_t vblock = (uint32_t)(g * (cap_r >> 3) + (kb >> 3) + lq) * D;
+      const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + (kb >> 3) + lq) * D;
       if (FP8) {
 #pragma unroll
         for (int dt = 0; dt < NDT; dt += 2) {
@@ -553,12 +560,12 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // lane without spilling (per the compiler's resource report): the decode
 // shapes up to 256 dims (128 for a streamed global call, which holds a
 // little more per row), and the grouped shapes with 128-dim slices except
-// the 512-dim verify and the fp8 verify above 64 dims.  Everything else
-// keeps one wave and all the registers.
+// the verify above 128 dims (bf16) or 64 dims (fp8).  Everything else keeps
+// one wave and all the registers.
 template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
 constexpr int waves_per_simd() {
   if (NCT == 1) return (KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) ? 2 : 1;
-  if (MODE == MODE_VERIFY) return (D <= 64 || (D <= 256 && !FP8)) ? 2 : 1;
+  if (MODE == MODE_VERIFY) return (D <= 64 || (D <= 128 && !FP8)) ? 2 : 1;
   return DS <= 128 ? 2 : 1;
 }
 

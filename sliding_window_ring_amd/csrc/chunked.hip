@@ -96,9 +96,11 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 // the K loads before the key count is read: addresses past the region are
 // bounded by the buffer resource, and a chunk past the request's keys only
 // leaves without using what it loaded.
-//   scores   wave (kq, dh) = (w % 8, w / 8): keys 16*kq .. +15 over head-dim
-//            half dh, bf16 MFMA into fp32; the two halves meet in LDS and
-//            are added in half order
+//   scores   wave (kq, dh) = (w % 8, w / 8): the 16 keys of half kq%2 of
+//            the chunk's 32-slot tile kq/2 (row r = key 8*(r/4) + 4*(kq%2)
+//            + r%4 of the tile, as stored) over head-dim half dh, bf16 MFMA
+//            into fp32; the two halves meet in LDS (in key order) and are
+//            added in half order
 //   softmax  16 lanes per row, eight keys per lane (rows spread over the
 //            waves); masked, max and sum over the chunk by DPP within the
 //            lanes' row, P rounded to bf16 into LDS; the row's (max, sum) go
@@ -155,7 +157,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int k0 = (MODE == MODE_VERIFY ? chunk - 1 : chunk) * CK;  // region slot of key 0
   const int64_t k_off = p.k_off[b], v_off = p.v_off[b];
   const int cap_r = region_slots(p, b);
-  const uint32_t region_bytes = (uint32_t)cap_r * (uint32_t)(Hkv * D * ESZ);
+  const int S_r = stored_slots(cap_r);  // slots stored per KV head (region layout: swr_device.h)
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(Hkv * D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + k_off, region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + v_off, region_bytes);
 
@@ -178,7 +181,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (wave >= PVW) return;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t vblock = (uint32_t)(g * (cap_r >> 3) + ((k0 + 32 * ks) >> 3) + lq) * D;
+      const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + ((k0 + 32 * ks) >> 3) + lq) * D;
       if (VPAIR) {
 #pragma unroll
         for (int dt = 0; dt < NDT; dt += 2) {
@@ -196,29 +199,35 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     }
   };
   if (!prop) {
-    const uint32_t base = ((uint32_t)(g * cap_r + k0 + 16 * kq + lr) * D + dh * DH) * ESZ;
+    // row lr of half kq%2 of tile kq/2; granule (dh*DH + kdim(c)) / R of it
+    constexpr int R = FP8 ? 16 : 8;
+    const uint32_t hb = k_half_base(g, S_r, k0 + 32 * (kq >> 1), kq & 1, D, ESZ) + (uint32_t)(lr * 16);
     if (KPAIR) {
 #pragma unroll
       for (int c = 0; c < NCH; c += 2) {
-        const u32x4 w = load16_stream(rk, base + (uint32_t)kdim(c));
+        const u32x4 w = load16_stream(rk, hb + (uint32_t)((dh * DH + kdim(c)) / R) * 256);
         kop[c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
         kop[c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
       }
     } else {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint32_t off = base + (uint32_t)(kdim(c) * ESZ);
+        const int dim = dh * DH + kdim(c);
+        const uint32_t off = hb + (uint32_t)(dim / R) * 256 + (uint32_t)((dim % R) * ESZ);
         kop[c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
       }
     }
     if (!kLateV) load_v();
   } else {
-    // proposals j = 0..S-1 are keys 0..S-1 of the chunk (subtile 0; value
-    // k step 0, lane group 0); every other operand element is zero
+    // proposals j = 0..S-1 are keys 0..S-1 of the chunk: row r of the
+    // wave's subtile is key 32*(kq/2) + 8*(r/4) + 4*(kq%2) + r%4 (so j < 8
+    // lands in subtiles 0 and 1), and value k step 0, lane group 0; every
+    // other operand element is zero
+    const int pj = 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kop[c] = bf16x8{};
-    if (kq == 0 && lr < S) {
-      const uint16_t* src = p.k_prop + ((size_t)(b * S + lr) * Hkv + g) * D + dh * DH;
+    if (pj < S) {
+      const uint16_t* src = p.k_prop + ((size_t)(b * S + pj) * Hkv + g) * D + dh * DH;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
     }
@@ -274,7 +283,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       acc = mfma16x16x32(kop[c], *reinterpret_cast<const bf16x8*>(&qbuf[ct * 16 + lr][dh * DH + kdim(c)]), acc);
-    *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][16 * kq + 4 * lq]) = acc;
+    // C rows 4*lq + r are keys 8*lq + 4*(kq%2) + r of tile kq/2
+    *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][32 * (kq >> 1) + 8 * lq + 4 * (kq & 1)]) = acc;
   }
   if (kLateV && !prop) load_v();
   __syncthreads();

@@ -35,7 +35,7 @@ swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
     if (!(kv->k_scale > 0.f) || !std::isfinite(kv->k_scale)) return SWR_ERR_INVALID;
     if (!(kv->v_scale > 0.f) || !std::isfinite(kv->v_scale)) return SWR_ERR_INVALID;
   }
-  const double bytes = (double)kv->cap * Hkv * D * elem_size(kv->dtype);
+  const double bytes = (double)swr::stored_slots(kv->cap) * Hkv * D * elem_size(kv->dtype);
   if (bytes > 4294967295.0) return SWR_ERR_UNSUPPORTED;  // regions are addressed with 32-bit offsets
   return SWR_OK;
 }
@@ -182,7 +182,7 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
 int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype) {
   if (cap <= 0 || cap % 8 != 0 || Hkv <= 0 || D <= 0) return -1;
   if (dtype != SWR_KV_BF16 && dtype != SWR_KV_FP8_E4M3) return -1;
-  return (int64_t)cap * Hkv * D * elem_size(dtype);
+  return (int64_t)swr::stored_slots(cap) * Hkv * D * elem_size(dtype);
 }
 
 swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {

@@ -70,6 +70,26 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Region layout (one request's K or V for one layer).  Per KV head a region
+// stores S = cap rounded up to 32 slots.
+//   K: tiles of 32 slots.  Slot 32t + k sits in half h = (k/4)%2, row
+//      r = 4*(k/8) + k%4 of tile t -- row r of half h is exactly MFMA A row r
+//      of the score sub-tile h (keys 8*(r/4) + 4h + r%4), whose C fragment
+//      is the P^T fragment of the value product.  Each half holds its 16
+//      rows granule-major: D/R granules of 16 rows x 16 bytes (R = 8 bf16 or
+//      16 fp8 dims), so one lane group's operand load (4 granules x 16 rows)
+//      is 1 KB of contiguous memory.
+//        byte offset = ((g*S + 32t)*D + h*16*D)*esize + (d/R)*256 + r*16 + (d%R)*esize
+//   V: blocks of 8 slots, ((g*(S/8) + slot/8)*D + d)*8 + slot%8 elements:
+//      one 16-byte load is 8 consecutive keys of one dim (the V^T operand).
+// (stored_slots: swr_internal.h)
+
+// Byte offset of K granule (slot-half base, granule q, row r): the start of
+// the half is ((g*S + 32t)*D + h*16*D)*esize.
+__device__ __forceinline__ uint32_t k_half_base(int g, int S, int tile_slot0, int half, int D, int esize) {
+  return ((uint32_t)(g * S + tile_slot0) * (uint32_t)D + (uint32_t)(half * 16 * D)) * (uint32_t)esize;
+}
+
 // D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 8
 // k-values of lane group l / 16; lane l receives C rows 4*(l/16) .. +3 of

@@ -14,6 +14,10 @@ namespace swr {
 // MODE_VERIFY runs in chunked form when the batch is small.
 enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3 };
 
+// Slots a region stores per KV head: its capacity rounded up to whole
+// 32-slot K tiles (region layout: swr_device.h).
+__host__ __device__ constexpr int stored_slots(int cap) { return (cap + 31) & ~31; }
+
 // Everything an attention launch reads, by value.
 struct AttnParams {
   const uint8_t* k_base;

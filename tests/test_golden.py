@@ -8,6 +8,7 @@ import pytest
 import oracle
 import synthetic
 from helpers import f64, global_pools
+from test_oracle_ring import k_view
 
 FACTS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
 
@@ -56,5 +57,5 @@ def test_ring_slot_of_position_for_window_1024(pos, slot):
     off = np.zeros(1, np.int64)
     one = synthetic.bf16_bits(np.ones((1, 1, hkv, d), np.float32))
     oracle.kv_append(kp, vp, off, off, W, oracle.BF16, 1, 1, one, one, np.array([pos], np.int32))
-    K = f64(kp.view(np.uint16).reshape(hkv, W, d)[0])[:, None, :]
+    K = f64(k_view(kp, 0, W, hkv, d))  # [slot][Hkv][D] through the declared layout
     assert list(np.nonzero(K[:, 0, 0])[0]) == [slot]

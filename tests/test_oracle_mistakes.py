@@ -23,10 +23,14 @@ MISTAKES = [
     ("encode divides by scale twice", "double v = fabs(x) / (double)scale;",
      "double v = fabs(x) / (double)scale / (double)scale;"),
     ("V region not blocked",
-     "return (((size_t)g * (size_t)(cap / 8) + (size_t)(s / 8)) * (size_t)D + (size_t)d) * 8 +\n         (size_t)(s % 8);",
-     "return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;"),
-    ("K region token-major", "return ((size_t)g * (size_t)cap + (size_t)s) * (size_t)D + (size_t)d;\n}\n\nstatic size_t v_index",
-     "return ((size_t)s * (size_t)8 + (size_t)g) * (size_t)D + (size_t)d;\n}\n\nstatic size_t v_index"),
+     "return (size_t)((((int64_t)g * (S / 8) + s / 8) * D + d) * 8 + s % 8);",
+     "return (size_t)(((int64_t)g * S + s) * D + d);"),
+    ("K tile rows in slot order", "const int64_t h = (k / 4) % 2, r = 4 * (k / 8) + k % 4;",
+     "const int64_t h = k / 16, r = k % 16;"),
+    ("K granule ignores the element size", "const int64_t R = 16 / elem_size(dtype); /* dims per 16-byte granule */",
+     "const int64_t R = 8;"),
+    ("K head stride ignores the tile padding", "return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D",
+     "return (size_t)(((int64_t)g * cap + 32 * t) * D + h * 16 * D"),
     ("append slot off by one", "int64_t s = wrap ? p % cb : p;", "int64_t s = wrap ? (p + 1) % cb : p;"),
     ("dot product drops the last dim", "for (int d = 0; d < D; ++d) dot += q[(size_t)r * D + d] * kd[d];",
      "for (int d = 0; d < D - 1; ++d) dot += q[(size_t)r * D + d] * kd[d];"),

@@ -5,8 +5,10 @@ is its absolute position modulo the window, and a new token reuses the oldest
 slot without moving the rest.  "Improving Decode Throughput on Intel Gaudi 3"
 (Our approach): K and V of a token are written together, so both rings carry
 the same rotation.  The region layout read back here uses numpy reshapes of
-the declared layout (K [Hkv][slot][D]; V in 8-slot blocks
-[Hkv][slot/8][D][8]), not the oracle's own index arithmetic.
+the declared layout, not the oracle's own index arithmetic: S = cap rounded
+up to 32 slots per KV head; K [Hkv][S/32][2][D/R][16][R] with R the dims of
+a 16-byte granule and slot 32t + k in half (k/4)%2, row 4*(k/8) + k%4 of
+tile t; V in 8-slot blocks [Hkv][S/8][D][8].
 """
 import numpy as np
 import pytest
@@ -16,15 +18,27 @@ import synthetic
 from helpers import f64
 
 
-def k_view(pool, off, cap, hkv, d):
-    """[slot][Hkv][D] view of a K region laid out [Hkv][cap][D]."""
-    return pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(hkv, cap, d).transpose(1, 0, 2)
+def stored(cap):
+    return -(-cap // 32) * 32
 
 
-def v_view(pool, off, cap, hkv, d):
-    """[slot][Hkv][D] view of a V region laid out [Hkv][cap/8][D][8]."""
-    v = pool[off:off + cap * hkv * d * 2].view(np.uint16).reshape(hkv, cap // 8, d, 8)
-    return v.transpose(1, 3, 0, 2).reshape(cap, hkv, d)
+def k_view(pool, off, cap, hkv, d, esize=2):
+    """[slot][Hkv][D] view of a K region: tiles of 32 slots, each two halves
+    of 16 rows stored granule-major ([Hkv][S/32][2][D/R][16][R])."""
+    S, R = stored(cap), 16 // esize
+    a = pool[off:off + S * hkv * d * esize].view(np.uint16 if esize == 2 else np.uint8)
+    a = a.reshape(hkv, S // 32, 2, d // R, 16, R)
+    slot = np.arange(cap)
+    t, k = slot // 32, slot % 32
+    half, row = (k // 4) % 2, 4 * (k // 8) + k % 4
+    return a[:, t, half, :, row, :].reshape(cap, hkv, d)
+
+
+def v_view(pool, off, cap, hkv, d, esize=2):
+    """[slot][Hkv][D] view of a V region laid out [Hkv][S/8][D][8]."""
+    S = stored(cap)
+    v = pool[off:off + S * hkv * d * esize].view(np.uint16 if esize == 2 else np.uint8).reshape(hkv, S // 8, d, 8)
+    return v.transpose(1, 3, 0, 2).reshape(S, hkv, d)[:cap]
 
 
 def position_tokens(n, hkv, d, base=0):
@@ -100,9 +114,9 @@ def test_fp8_append_stores_encoded_codes():
     kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
     off = np.zeros(1, np.int64)
     oracle.kv_append(kp, vp, off, off, W, oracle.FP8, ks, vs, k, v, np.array([14], np.int32))
-    K = kp.reshape(hkv, W, d)
-    V = vp.reshape(hkv, W // 8, d, 8)
+    K = k_view(kp, 0, W, hkv, d, esize=1)
+    V = v_view(vp, 0, W, hkv, d, esize=1)
     for t in range(5):
         s = (14 + t) % W
-        assert np.array_equal(K[:, s], oracle.e4m3_encode(k[0, t], ks))
-        assert np.array_equal(V[:, s // 8, :, s % 8], oracle.e4m3_encode(v[0, t], vs))
+        assert np.array_equal(K[s], oracle.e4m3_encode(k[0, t], ks))
+        assert np.array_equal(V[s], oracle.e4m3_encode(v[0, t], vs))
