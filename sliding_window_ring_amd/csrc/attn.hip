@@ -524,14 +524,17 @@ struct Shape {
 
 // Waves per workgroup: D/ds share each key tile, kw split the tiles.  A
 // global layer streamed in one pass takes the decode shapes for up to 16 rows
-// and the grouped verify shapes above that.
+// and the grouped verify shapes above that.  At 512 dims four 128-dim
+// slices share each tile at two waves per SIMD: measured on the 16-request
+// mixed step, 225 us (bf16) and 130 us (fp8) against 241 and 187 us for two
+// 256-dim slices x two key-split waves at one wave per SIMD.
 Shape pick_shape(int mode, int D, int nct) {
   if (mode == MODE_DECODE || (mode == MODE_GSTREAM && nct == 1)) {
     switch (D) {
       case 64: return {64, 4};
       case 128: return {128, 4};
       case 256: return {256, 4};
-      case 512: return {256, 2};
+      case 512: return {128, 1};
     }
   } else if (nct == 1) {
     switch (D) {
@@ -559,12 +562,13 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // loads are in flight, wherever the kernel then fits the 256 registers of a
 // lane without spilling (per the compiler's resource report): the decode
 // shapes up to 256 dims (128 for a streamed global call, which holds a
-// little more per row), and the grouped shapes with 128-dim slices except
-// the verify above 128 dims (bf16) or 64 dims (fp8).  Everything else keeps
-// one wave and all the registers.
+// little more per row) and the 512-dim one (four 128-dim slices per tile),
+// and the grouped shapes with 128-dim slices except the verify above 128
+// dims (bf16) or 64 dims (fp8).  Everything else keeps one wave and all the
+// registers.
 template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
 constexpr int waves_per_simd() {
-  if (NCT == 1) return (KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) ? 2 : 1;
+  if (NCT == 1) return ((KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) || (D == 512 && DS <= 128)) ? 2 : 1;
   if (MODE == MODE_VERIFY) return (D <= 64 || (D <= 128 && !FP8)) ? 2 : 1;
   return DS <= 128 ? 2 : 1;
 }
@@ -594,7 +598,7 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
         case 64: return launch_fixed<64, 64, 1, 4, MODE>(pl, p, s);
         case 128: return launch_fixed<128, 128, 1, 4, MODE>(pl, p, s);
         case 256: return launch_fixed<256, 256, 1, 4, MODE>(pl, p, s);
-        case 512: return launch_fixed<512, 256, 1, 2, MODE>(pl, p, s);
+        case 512: return launch_fixed<512, 128, 1, 1, MODE>(pl, p, s);
       }
       return hipErrorInvalidValue;
     }
