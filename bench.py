@@ -161,7 +161,7 @@ def _timed(torch, fn, reps, sets):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
-def other_workloads(swr, torch):
+def other_workloads(swr, torch, sweep=True):
     """The remaining workloads, each timed on its own (us per call, GB/s of
     algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the mixed
     16-request step (bf16 and fp8, rings and global regions in one pool), and
@@ -280,6 +280,8 @@ def other_workloads(swr, torch):
         del pool, sl, gl, dws, gws
         torch.cuda.synchronize()
 
+    if not sweep:
+        return res
     # --- global verify over every key count 4000..8192 (one region of 8192 slots)
     lo, hi = synthetic.GLOBAL_SWEEP
     cap = 8192
@@ -325,6 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the global key-count sweep of the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -462,7 +465,7 @@ def main():
         "host_wall_s": round(wall, 3),
     }
     if not args.no_extra:
-        result["other_workloads"] = other_workloads(swr, torch)
+        result["other_workloads"] = other_workloads(swr, torch, sweep=not args.no_sweep)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result))
