@@ -396,9 +396,10 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 }
 
 // Global: workgroup j takes chunk j % nchunk of unit j / nchunk.  Verify:
-// the ring chunks of every unit come first (workgroup j < units*(nchunk-1)
-// takes ring chunk j % (nchunk-1) of unit j / (nchunk-1)) and the small
-// proposal chunks last.
+// the ring chunks of every unit come first and the small proposal chunks
+// last.  When the units are a multiple of the 8 XCDs (workgroup j runs on
+// XCD j % 8), all ring chunks of a unit go to one XCD, whose L2 then serves
+// the unit's Q to all of them after one read.
 // Up to 256 head dims two workgroups stay resident per CU (eight waves per
 // SIMD, 64 registers a lane); 512 dims need more registers and keep one.
 template <int D, int NCT, bool FP8, int MODE>
@@ -409,8 +410,16 @@ chunk_kernel(const AttnParams p) {
     const int nring = p.nchunk - 1;
     const int ring_wgs = p.B * p.Hkv * nring;
     if ((int)blockIdx.x < ring_wgs) {
-      const int unit = blockIdx.x / nring;
-      chunk_item<D, NCT, FP8, MODE>(p, sm, unit, 1 + (blockIdx.x - unit * nring));
+      int unit, rc;
+      if ((p.B * p.Hkv) % 8 == 0) {
+        const int x = blockIdx.x & 7, sl = blockIdx.x >> 3;
+        unit = x + 8 * (sl / nring);
+        rc = sl - (sl / nring) * nring;
+      } else {
+        unit = blockIdx.x / nring;
+        rc = blockIdx.x - unit * nring;
+      }
+      chunk_item<D, NCT, FP8, MODE>(p, sm, unit, 1 + rc);
     } else {
       chunk_item<D, NCT, FP8, MODE>(p, sm, blockIdx.x - ring_wgs, 0);
     }
