@@ -131,19 +131,35 @@ def cpu_baseline(seconds: float = 12.0):
     gx = synthetic.global_verify()
     gk, gv, gko, gvo = global_pools(gx["k"], gx["v"], gx["key_count"], 6016)
     per_rep = nb * HKV * W * D * 4 + 2 * nb * HKV * G * D * 2 + algorithmic_bytes()[2]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.swa_decode(kp, vp, ko, vo, W, oracle.BF16, 1, 1, x["q"], x["pos"], HKV, 1 / 16)
-        oracle.global_attend(gk, gv, gko, gvo, 6016, oracle.BF16, 1, 1, gx["q"], gx["q_pos"], gx["key_count"],
-                             GHKV, GD ** -0.5)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+    def run(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.swa_decode(kp, vp, ko, vo, W, oracle.BF16, 1, 1, x["q"], x["pos"], HKV, 1 / 16)
+            oracle.global_attend(gk, gv, gko, gvo, 6016, oracle.BF16, 1, 1, gx["q"], gx["q_pos"], gx["key_count"],
+                                 GHKV, GD ** -0.5)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    cores = oracle.num_threads()
+    reps, el = run(seconds)
+    prev = oracle.set_threads(1)
+    reps1, el1 = run(seconds / 2)
+    oracle.set_threads(prev)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{reps} repetitions of: sliding decode for 16 of the 56 requests (full 1024-key windows, "
-                      f"8 KV heads x 256) + the 6005-key global verify; binary64 C oracle, {el:.1f} s"}
+                      f"8 KV heads x 256) + the 6005-key global verify; binary64 C oracle, {el:.1f} s",
+            "value_1_thread": round(per_rep * reps1 / el1 / 1e9, 4),
+            "sample_1_thread": f"{reps1} repetitions of the same, one OpenMP thread, {el1:.1f} s",
+            "host": {"cpu": cpu, "logical_cpus": os.cpu_count()}}
 
 
 def _timed(torch, fn, reps, sets):
@@ -197,6 +213,28 @@ def other_workloads(swr, torch, sweep=True):
     res["sliding_verify_b8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                                 "algorithmic_bytes": nbytes}
     del sets, ws
+
+    # --- one GPU's share of the B=56 decode under KV-head sharding (8 GPUs, one KV head each)
+    w = synthetic.SWA_DECODE
+    sets = []
+    for _ in range(3):
+        rb = swr.region_bytes(w.W, 1, w.D)
+        kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
+        vb = torch.empty_like(kb)
+        off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+        L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
+        pos = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+        swr.kv_append(L, randn(w.B, w.W, 1, w.D), randn(w.B, w.W, 1, w.D), (pos - w.W + 1).to(torch.int32))
+        q = randn(w.B, w.G, w.D)
+        sets.append((L, q, pos, torch.empty_like(q)))
+    hws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.G, 1, w.D, w.W)),
+                      dtype=torch.uint8, device=dev)
+    us = _timed(torch, lambda i: swr.swa_decode(sets[i][0], sets[i][1], sets[i][2], 1, w.D ** -0.5, out=sets[i][3],
+                                                ws=hws), 60, len(sets))
+    nbytes = w.B * w.W * w.D * 4 + 2 * w.B * w.G * w.D * 2
+    res["sliding_decode_b56_one_kv_head_share"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                                   "algorithmic_bytes": nbytes}
+    del sets, hws
 
     # --- fp8 sliding decode, B=56
     w = synthetic.SWA_DECODE
@@ -414,6 +452,19 @@ def main():
     g1.record()
     torch.cuda.synchronize()
     global_graph_us = g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
+    # ... and the attention calls alone (24 in one graph), without the append
+    agraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(agraph):
+        for g in glob:
+            swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, scale_g, out=g["out"], ws=gws)
+    agraph.replay()
+    torch.cuda.synchronize()
+    g0.record()
+    for _ in range(reps):
+        agraph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    global_attn_graph_us = g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
     b_dec, b_app_s, b_glob, b_app_g = algorithmic_bytes()
     step_bytes = b_dec + b_app_s + b_glob + b_app_g
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -446,6 +497,7 @@ def main():
             "sliding_decode_b56_append": round(append_s, 2),
             "global_verify_6005_append_and_attention": round(global_us, 2),
             "global_verify_6005_in_layer_graph": round(global_graph_us, 2),
+            "global_verify_6005_attention_only_in_graph": round(global_attn_graph_us, 2),
         },
         "layer_gbs": {
             "sliding_decode_b56_attention": round(achieved, 1),

@@ -61,6 +61,8 @@ def _bind(h):
     h.orc_gqa_verify.argtypes = [P, P, P, P, I, I, D, D, P, P, P, P, I, I, I, I, I, D, P]
     h.orc_global_attend.argtypes = [P, P, P, P, I, P, I, D, D, P, P, P, I, I, I, I, I, I, D, P]
     h.orc_num_threads.restype = I
+    h.orc_set_threads.argtypes = [I]
+    h.orc_set_threads.restype = I
     return h
 
 
@@ -112,6 +114,12 @@ def _c(a, dtype):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> int:
+    """Set the oracle's OpenMP threads (for timing on fewer cores); returns
+    the previous count.  Results are the same for any count."""
+    return lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- formats

@@ -499,6 +499,20 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Sets the threads of the parallel loops (n >= 1, for timing on fewer
+ * cores); returns the previous count.  Results do not depend on it: every
+ * unit is computed by one thread in a fixed order. */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+  const int prev = omp_get_max_threads();
+  if (n >= 1) omp_set_num_threads(n);
+  return prev;
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* Array forms of the scalar codecs, for the test suite. */
 void orc_bf16_value_n(const uint16_t* x, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_value(x[i]);
