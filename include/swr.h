@@ -95,7 +95,9 @@ typedef enum swr_kv_dtype {
 typedef enum swr_op {
   SWR_OP_SWA_DECODE = 0,
   SWR_OP_GQA_VERIFY = 1,
-  SWR_OP_GLOBAL_ATTEND = 2
+  SWR_OP_GLOBAL_ATTEND = 2,
+  SWR_OP_SWA_APPEND_DECODE = 3,
+  SWR_OP_GLOBAL_APPEND_ATTEND = 4
 } swr_op;
 
 /* One layer's view of per-request K/V regions inside one or two device
@@ -155,6 +157,22 @@ swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const in
                           int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Append + sliding decode in one call ([Carat] ring section: a decode step
+ * writes the new token into the slot of the oldest one and attends over the
+ * window; [Gaudi] "Our approach": K and V go to the same slot).  Equivalent
+ * to swr_kv_append(ring, k_new, v_new, pos, NULL, B, 1, Hkv, D, 1) followed
+ * by swr_swa_decode(ring, q, out, pos, ...): the ring holds the same bytes
+ * afterwards and the output is the same attention, from one launch (plus
+ * the split merge when B*Hkv is small) instead of two.
+ *   k_new, v_new : device bf16 [B][Hkv][D], the token at position pos[b]
+ *   ring, q, out, pos, scale : as for swr_swa_decode
+ *   ws : >= swr_workspace_bytes(SWR_OP_SWA_APPEND_DECODE, B, 1, Hq, Hkv, D, W)
+ * Supported: as swr_swa_decode. */
+swr_status swr_swa_append_decode(const swr_kv* ring, const void* k_new, const void* v_new,
+                                 const void* q, void* out, const int32_t* pos, int B, int Hq,
+                                 int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------- sliding verify */
 
 /* Speculative verification on a sliding layer ([Carat] "Doing it all in one
@@ -193,6 +211,29 @@ swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const i
                              const int32_t* key_count, int max_key_count, int B, int S, int Hq,
                              int Hkv, int D, float scale, void* ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/* Append + global-layer attention in one call ([Carat] "More FLOPs can be
+ * faster": the proposals join the global KV, key_count = context +
+ * proposals, then the grouped attention).  Writes the S tokens of request b
+ * at positions pos0[b] .. pos0[b]+S-1 (slot = position) and computes the rows
+ * of swr_global_attend with q_pos[b][i] = pos0[b] + i and key_count[b] =
+ * pos0[b] + S.  Equivalent to swr_kv_append(kv, k_new, v_new, pos0, NULL, B,
+ * S, Hkv, D, 0) followed by swr_global_attend: same region bytes, same
+ * attention.  When the K/V of all (request, KV head) pairs spans fewer than
+ * 2048 tiles of 32 keys the call is one chunked pass plus its merge (the
+ * proposals' workgroup stores them while it attends); longer calls run the
+ * append and then the streamed pass.
+ *   k_new, v_new  : device bf16 [B][S][Hkv][D]
+ *   q, out        : device bf16 [B][S][Hq][D]
+ *   pos0          : device int32 [B], pos0[b] >= 0, pos0[b] + S <= max_key_count and
+ *                   <= the region's capacity
+ *   max_key_count : host bound on pos0[b] + S, sizes the launch and workspace
+ *   ws : >= swr_workspace_bytes(SWR_OP_GLOBAL_APPEND_ATTEND, B, S, Hq, Hkv, D, max_key_count)
+ * Supported: as swr_global_attend. */
+swr_status swr_global_append_attend(const swr_kv* kv, const void* k_new, const void* v_new,
+                                    const void* q, void* out, const int32_t* pos0,
+                                    int max_key_count, int B, int S, int Hq, int Hkv, int D,
+                                    float scale, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes an attention call needs (0 when it needs none).  For
  * decode and verify `cap_or_max_keys` is the window W; for global attention it

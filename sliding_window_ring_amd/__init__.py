@@ -23,12 +23,15 @@ SWR_KV_FP8_E4M3 = 1
 SWR_OP_SWA_DECODE = 0
 SWR_OP_GQA_VERIFY = 1
 SWR_OP_GLOBAL_ATTEND = 2
+SWR_OP_SWA_APPEND_DECODE = 3
+SWR_OP_GLOBAL_APPEND_ATTEND = 4
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace missing or too small",
           4: "HIP launch error", 5: "pool exhausted"}
 
 EXPORTS = [
-    "swr_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend", "swr_workspace_bytes",
+    "swr_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
+    "swr_global_append_attend", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
     "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_status_string",
 ]
@@ -60,8 +63,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "swr_kv_append": ([KV, P, P, P, P, I, I, I, I, I, P], I),
         "swr_swa_decode": ([KV, P, P, P, I, I, I, I, F, P, SZ, P], I),
+        "swr_swa_append_decode": ([KV, P, P, P, P, P, I, I, I, I, F, P, SZ, P], I),
         "swr_gqa_verify": ([KV, P, P, P, P, P, I, I, I, I, I, F, P, SZ, P], I),
         "swr_global_attend": ([KV, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
+        "swr_global_append_attend": ([KV, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
         "swr_workspace_bytes": ([I, I, I, I, I, I, I], SZ),
         "swr_kv_region_bytes": ([I, I, I, I], I64),
         "swr_pool_create": ([SZ, ctypes.POINTER(P)], I),
@@ -180,6 +185,25 @@ def swa_decode(ring: KVLayer, q: torch.Tensor, pos: torch.Tensor, hkv: int, scal
     return out
 
 
+def swa_append_decode(ring: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      pos: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """swr_swa_append_decode: k_new, v_new bf16 [B][Hkv][D] (or [B][1][Hkv][D]),
+    q bf16 [B][Hq][D], pos int32 [B] -> out bf16 [B][Hq][D]."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    _dev(pos, "pos", torch.int32)
+    B, hq, d = q.shape
+    hkv = k_new.shape[-2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    ws, wsb = _workspace(SWR_OP_SWA_APPEND_DECODE, B, 1, hq, hkv, d, ring.cap, ws, q.device)
+    _check("swr_swa_append_decode",
+           lib.swr_swa_append_decode(ctypes.byref(ring.c()), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                     _ptr(pos), B, hq, hkv, d, scale, _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
 def gqa_verify(ring: KVLayer, k_prop: torch.Tensor, v_prop: torch.Tensor, q: torch.Tensor,
                pos0: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -213,6 +237,27 @@ def global_attend(kv: KVLayer, q: torch.Tensor, q_pos: torch.Tensor, key_count: 
     _check("swr_global_attend", lib.swr_global_attend(ctypes.byref(kv.c()), _ptr(q), _ptr(out), _ptr(q_pos),
                                                       _ptr(key_count), max_key_count, B, S, hq, hkv, d, scale,
                                                       _ptr(ws), wsb, _stream(stream)))
+    return out
+
+
+def global_append_attend(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                         pos0: torch.Tensor, max_key_count: int, scale: float,
+                         out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """swr_global_append_attend: k_new, v_new bf16 [B][S][Hkv][D], q bf16
+    [B][S][Hq][D], pos0 int32 [B] -> out bf16 [B][S][Hq][D]."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    _dev(pos0, "pos0", torch.int32)
+    B, S, hq, d = q.shape
+    hkv = k_new.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    ws, wsb = _workspace(SWR_OP_GLOBAL_APPEND_ATTEND, B, S, hq, hkv, d, max_key_count, ws, q.device)
+    _check("swr_global_append_attend",
+           lib.swr_global_append_attend(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                        _ptr(pos0), max_key_count, B, S, hq, hkv, d, scale, _ptr(ws), wsb,
+                                        _stream(stream)))
     return out
 
 

@@ -18,32 +18,6 @@
 
 namespace swr {
 
-// OCP E4M3FN code of value/scale: the quotient is formed in binary64 with
-// correct rounding (value is bf16, scale fp32, so the binary64 quotient sits
-// on the same side of every E4M3 rounding midpoint as the exact one), then
-// rounded to nearest, ties to even, on the E4M3 grid (quantum 2^-9 below
-// 2^-6, 2^(e-3) in binade e above), saturating at +-448.
-__device__ __forceinline__ uint8_t e4m3_encode(float value, float scale) {
-  const double v = __ddiv_rn((double)value, (double)scale);
-  const uint8_t sign = __builtin_signbit(v) ? 0x80 : 0x00;
-  const double a = __builtin_fabs(v);
-  if (__builtin_isnan(a)) return sign | 0x7F;
-  if (a >= 448.0) return sign | 0x7E;
-  if (a < 0x1p-6) {
-    // subnormal range: code = round(a / 2^-9); 8 lands on the smallest normal 0x08
-    return sign | (uint8_t)__builtin_rint(a * 512.0);
-  }
-  // binade e (-6 .. 8) from the binary64 exponent field; a * 2^(3-e) is exact
-  int e = (int)((__builtin_bit_cast(uint64_t, a) >> 52) & 0x7FF) - 1023;
-  const double pow2 = __builtin_bit_cast(double, (uint64_t)(1023 + 3 - e) << 52);
-  int m = (int)__builtin_rint(a * pow2);  // 8 .. 16
-  if (m == 16) {
-    m = 8;
-    ++e;
-  }
-  return sign | (uint8_t)(((e + 7) << 3) | (m - 8));
-}
-
 template <bool FP8>
 __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
   const int d8n = p.D / 8;
@@ -80,34 +54,7 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
   const uint32_t region_bytes = (uint32_t)S * (uint32_t)(p.Hkv * p.D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
-  // K: this thread's 8 dims are one bf16 granule, or half an fp8 granule
-  const int k32 = (int)(slot & 31);
-  const uint32_t koff = k_half_base(g, S, (int)(slot & ~31L), (k32 >> 2) & 1, p.D, ESZ) +
-                        (uint32_t)((FP8 ? d8 >> 1 : d8) * 256 + (4 * (k32 >> 3) + (k32 & 3)) * 16 +
-                                   (FP8 ? (d8 & 1) * 8 : 0));
-  // V element (slot, g, d) at ((g*(S/8) + slot/8)*D + d)*8 + slot%8
-  const uint32_t vrow = (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * p.D + (size_t)d8 * 8) * 8 +
-                                   (size_t)(slot & 7));
-  if (!FP8) {
-    store16(rk, koff, kbits);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t bits = (uint16_t)(vbits[e >> 1] >> (16 * (e & 1)));
-      store2(rv, (vrow + 8 * e) * 2, bits);
-    }
-  } else {
-    uint32_t kc[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t kb16 = (kbits[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t vb16 = (vbits[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const float kv = __builtin_bit_cast(float, kb16 << 16);
-      const float vv = __builtin_bit_cast(float, vb16 << 16);
-      kc[e >> 2] |= (uint32_t)e4m3_encode(kv, p.k_scale) << (8 * (e & 3));
-      store1(rv, vrow + 8 * e, e4m3_encode(vv, p.v_scale));
-    }
-    store8(rk, koff, u32x2{kc[0], kc[1]});
-  }
+  store_token_piece<FP8>(rk, rv, (int)slot, g, S, p.D, d8, kbits, vbits, p.k_scale, p.v_scale);
 }
 
 __global__ void __launch_bounds__(256) zero16_kernel(u32x4* dst, size_t n16) {

@@ -55,10 +55,12 @@ attn_kernel(const AttnParams p) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int RED = 2 * NCT * 4;  // score floats per lane per tile
   constexpr int RS = D + 4;         // padded LDS row stride (floats)
+  constexpr bool DEC = MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND;
+  constexpr bool APP = MODE == MODE_DECODE_APPEND;
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   const int ds = wave % DSPLIT;
   const int kw = wave / DSPLIT;
   const int lr = lane & 15;  // row within a 16-row column tile; also key row of the K operand
@@ -79,14 +81,14 @@ attn_kernel(const AttnParams p) {
   const int cap_r = region_cap(p, b);
   int n_keys;         // ring slots ever written; global: keys of the request
   int ring_head = 0;  // verify: slot of the newest committed position
-  if (MODE == MODE_DECODE) {
+  if (DEC) {
     n_keys = min(p.pos[b] + 1, p.cap);
   } else if (MODE == MODE_VERIFY) {
     const int p0 = p.pos[b];
     n_keys = min(p0, p.cap);
     ring_head = p0 > 0 ? (p0 - 1) % p.cap : 0;
   } else {
-    n_keys = min(p.key_count[b], cap_r);
+    n_keys = min(key_count_of(p, b), cap_r);
   }
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
@@ -109,7 +111,7 @@ attn_kernel(const AttnParams p) {
     const int i = row_ok[ct] ? row / G : 0;
     const int h = row_ok[ct] ? row - i * G : 0;
     row_i[ct] = i;
-    row_lim[ct] = (MODE == MODE_GSTREAM) ? min(p.pos[b * S + i], n_keys - 1) : p.cap - 2 - i;
+    row_lim[ct] = (MODE == MODE_GSTREAM) ? min(qpos_of(p, b, i), n_keys - 1) : p.cap - 2 - i;
     const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -224,22 +226,61 @@ attn_kernel(const AttnParams p) {
     }
   };
 
-  {
-    const int t0 = t_begin + kw;
-    if (t0 < t_end) {
-      load_k(t0);
-      load_v(t0);
+  // Fused append (decode): the new token, position pos in slot pos % W, is
+  // stored by the waves that read its tile, each its own head-dim slice, and
+  // that tile is the last one they read: the split walks its tiles in
+  // rotated order, starting after the token's tile.  The stores go out with
+  // the first loads; the wave waits for them once, just before the tile's
+  // loads are issued, so its later loads see them.  No other workgroup reads
+  // the tile.
+  const int nt = t_end - t_begin;
+  int rot = 0;  // local tile index lam is tile t_begin + (lam + rot) mod nt
+  bool writer = false;
+  int t_new = -1, slot_new = 0;
+  if (APP) {
+    slot_new = p.pos[b] % p.cap;
+    t_new = slot_new >> 5;
+    if (t_new >= t_begin && t_new < t_end) {
+      rot = t_new - t_begin + 1;
+      if (rot == nt) rot = 0;
+      writer = kw == (nt - 1) % KW;
     }
+  }
+  auto tile_at = [&](int lam) {
+    int x = lam + rot;
+    if (x >= nt) x -= nt;
+    return t_begin + x;
+  };
+  auto write_new = [&]() {
+    if (lane < DS / 8) {
+      const int d8 = d_base / 8 + lane;
+      const size_t src = ((size_t)b * Hkv + g) * D + (size_t)d8 * 8;
+      const u32x4 kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+      const u32x4 vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+      store_token_piece<FP8>(rk, rv, slot_new, g, S_r, D, d8, kbits, vbits, p.k_scale_store, p.v_scale_store);
+    }
+  };
+
+  if (kw < nt) {
+    const int t0 = tile_at(kw);
+    if (APP && writer && t0 == t_new) {  // the wave's only tile: store, wait, then load
+      write_new();
+      wait_vm_all();
+    }
+    load_k(t0);
+    load_v(t0);
+    if (APP && writer && t0 != t_new) write_new();
   }
 
   for (int it = 0; it < n_it; ++it) {
-    const int t = t_begin + kw + it * KW;
-    if (t >= t_end) {  // wave-uniform; keeps the barrier count equal across waves
+    const int lam = kw + it * KW;
+    if (lam >= nt) {  // wave-uniform; keeps the barrier count equal across waves
       if (DSPLIT > 1) __syncthreads();
       continue;
     }
-    const int t_next = t + KW;
-    const bool has_next = t_next < t_end;
+    const int t = tile_at(lam);
+    const bool has_next = lam + KW < nt;
+    const int t_next = has_next ? tile_at(lam + KW) : 0;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     const int kb = t * 32;
 
@@ -254,7 +295,10 @@ attn_kernel(const AttnParams p) {
         for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
         sc[sub][ct] = acc;
       }
-    if (has_next) load_k(t_next);
+    if (has_next) {
+      if (APP && writer && t_next == t_new) wait_vm_all();
+      load_k(t_next);
+    }
 
     if (DSPLIT > 1) {  // add the head-dim slices of the scores, in slice order
       float* buf = smem + (size_t)((it & 1) * KW + kw) * DSPLIT * RED * 64;
@@ -292,7 +336,7 @@ attn_kernel(const AttnParams p) {
           const int e = 4 * sub + r;     // element of the P^T fragment
           const int key = kb + 8 * lq + e;
           bool vis;
-          if (MODE == MODE_DECODE) {
+          if (DEC) {
             vis = key < n_keys;
           } else if (MODE == MODE_GSTREAM) {
             vis = key <= row_lim[ct];
@@ -468,12 +512,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D,
   const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
 
   int n_keys;
-  if (MODE == MODE_DECODE)
+  if (MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND)
     n_keys = min(p.pos[b] + 1, p.cap);
   else if (MODE == MODE_VERIFY)
     n_keys = min(p.pos[b], p.cap);
   else
-    n_keys = min(p.key_count[b], region_cap(p, b));
+    n_keys = min(key_count_of(p, b), region_cap(p, b));
   n_keys = max(n_keys, 0);
   const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
   const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
@@ -529,7 +573,7 @@ struct Shape {
 // mixed step, 225 us (bf16) and 130 us (fp8) against 241 and 187 us for two
 // 256-dim slices x two key-split waves at one wave per SIMD.
 Shape pick_shape(int mode, int D, int nct) {
-  if (mode == MODE_DECODE || (mode == MODE_GSTREAM && nct == 1)) {
+  if (mode == MODE_DECODE || mode == MODE_DECODE_APPEND || (mode == MODE_GSTREAM && nct == 1)) {
     switch (D) {
       case 64: return {64, 4};
       case 128: return {128, 4};
@@ -568,7 +612,8 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // registers.
 template <int D, int DS, int NCT, int KW, bool FP8, int MODE>
 constexpr int waves_per_simd() {
-  if (NCT == 1) return ((KW > 1 && (D <= 128 || (D == 256 && MODE == MODE_DECODE))) || (D == 512 && DS <= 128)) ? 2 : 1;
+  constexpr bool DEC = MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND;
+  if (NCT == 1) return ((KW > 1 && (D <= 128 || (D == 256 && DEC))) || (D == 512 && DS <= 128)) ? 2 : 1;
   if (MODE == MODE_VERIFY) return (D <= 64 || (D <= 128 && !FP8)) ? 2 : 1;
   return DS <= 128 ? 2 : 1;
 }
@@ -591,7 +636,8 @@ hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) 
 // up to 16 rows and the grouped shapes above.
 template <int MODE>
 hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  const bool decode_shape = MODE == MODE_DECODE || (MODE == MODE_GSTREAM && pl.nct == 1);
+  const bool decode_shape =
+      MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND || (MODE == MODE_GSTREAM && pl.nct == 1);
   if constexpr (MODE != MODE_VERIFY) {
     if (decode_shape) {
       switch (pl.D) {
@@ -614,7 +660,7 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
       return hipErrorInvalidValue;
     }
   }
-  if constexpr (MODE != MODE_DECODE) {
+  if constexpr (MODE != MODE_DECODE && MODE != MODE_DECODE_APPEND) {
     switch (pl.D) {
       case 64: return launch_fixed<64, 64, 2, 1, MODE>(pl, p, s);
       case 128: return launch_fixed<128, 128, 2, 1, MODE>(pl, p, s);
@@ -658,7 +704,8 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
   const int G = Hq / Hkv;
   const int rows = G * S;
-  if (mode == MODE_DECODE) {
+  const bool dec = mode == MODE_DECODE || mode == MODE_DECODE_APPEND;
+  if (dec) {
     if (S != 1 || G > 16) return false;
   } else {
     if (S > 8 || rows > 32) return false;
@@ -685,7 +732,7 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
                    kStreamSplitTiles);
     tps = std::min(tps, pl->max_tiles);
   } else if (pl->units > 0 && pl->units < kNumCU) {
-    if (mode == MODE_DECODE)
+    if (dec)
       tps = std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU));
     else
       tps = std::max(4, ceil_div((long)pl->max_tiles * pl->units, 4 * kNumCU));
@@ -702,12 +749,23 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   return true;
 }
 
+bool plan_global_append(int B, int S, int Hq, int Hkv, int D, int fp8, int max_keys, AttnPlan* pl) {
+  if (B < 0 || S < 1 || Hkv < 1 || max_keys < S) return false;
+  if ((long)B * Hkv * ceil_div(max_keys, 32) < kStreamTiles) {
+    if (!plan_chunked(MODE_VERIFY, B, S, Hq, Hkv, D, std::max(max_keys - S, 1), pl)) return false;
+    pl->fp8 = fp8 ? 1 : 0;
+    return true;
+  }
+  return plan_attention(MODE_GLOBAL, B, S, Hq, Hkv, D, fp8, max_keys, pl);
+}
+
 hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   if (pl.units == 0) return hipSuccess;
   if (pl.chunked) return launch_chunked(pl, p, s);
   hipError_t e;
   switch (pl.mode) {
     case MODE_DECODE: e = launch_mode<MODE_DECODE>(pl, p, s); break;
+    case MODE_DECODE_APPEND: e = launch_mode<MODE_DECODE_APPEND>(pl, p, s); break;
     case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
     case MODE_GSTREAM: e = launch_mode<MODE_GSTREAM>(pl, p, s); break;
     default: return hipErrorInvalidValue;
@@ -718,7 +776,7 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
   if (pl.mode == MODE_GSTREAM && pl.nsplit > 16) return launch_split_merge(pl, p, s);
   const long total = (long)pl.units * pl.rows * (pl.D / 4);
   const int blocks = ceil_div(total, 256);
-  if (pl.mode == MODE_DECODE)
+  if (pl.mode == MODE_DECODE || pl.mode == MODE_DECODE_APPEND)
     hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
   else if (pl.mode == MODE_VERIFY)
     hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);

@@ -58,11 +58,12 @@ __device__ __forceinline__ int region_slots(const AttnParams& p, int b) {
 }
 
 // Region keys a (request, KV head) attends to: the global key count, or the
-// ring slots holding committed positions (verify: positions < pos0).
+// slots holding committed positions (verify: positions < pos0; a ring has
+// W slots, a global region its own capacity and never wraps).
 template <int MODE>
 __device__ __forceinline__ int region_keys(const AttnParams& p, int b) {
-  if (MODE == MODE_VERIFY) return max(min(p.pos[b], p.cap), 0);
-  return max(min(p.key_count[b], region_slots(p, b)), 0);
+  if (MODE == MODE_VERIFY) return max(min(p.pos[b], region_slots(p, b)), 0);
+  return max(min(key_count_of(p, b), region_slots(p, b)), 0);
 }
 
 }  // namespace
@@ -115,6 +116,12 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 // are bf16 values: their scores take scale * log2(e) without k_scale, and
 // their accumulated values are divided by v_scale (in fp32) before the
 // store, since pass 2 multiplies every chunk by v_scale.
+// Fused append (global regions, which never wrap, so every committed key
+// stays visible to every row): the proposal chunk also stores the proposals
+// into slots pos0 .. pos0+S-1, and over an fp8 region it takes their stored
+// codes as operands, exactly as a later call would read them.  The region
+// chunks read only slots below pos0; a store can only meet a read of a slot
+// the chunk masks (its K scores are replaced and its V lanes zeroed).
 template <int D, int NCT>
 struct ChunkSmem {
   float sbuf[2][16 * NCT][kChunkKeys + 4];
@@ -219,6 +226,17 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     }
     if (!kLateV) load_v();
   } else {
+    if (p.append) {  // the proposals into their slots, 8 head dims per thread
+      const int per = D / 8;
+      for (int idx = threadIdx.x; idx < S * per; idx += 64 * NW) {
+        const int j = idx / per, d8 = idx - (idx / per) * per;
+        const int slot = p.pos[b] + j;
+        if (slot < 0 || slot >= cap_r) continue;  // outside the region: dropped, as by the append call
+        const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
+        store_token_piece<FP8>(rk, rv, slot, g, S_r, D, d8, *reinterpret_cast<const u32x4*>(p.k_prop + src),
+                               *reinterpret_cast<const u32x4*>(p.v_prop + src), p.k_scale_store, p.v_scale_store);
+      }
+    }
     // proposals j = 0..S-1 are keys 0..S-1 of the chunk: row r of the
     // wave's subtile is key 32*(kq/2) + 8*(r/4) + 4*(kq%2) + r%4 (so j < 8
     // lands in subtiles 0 and 1), and value k step 0, lane group 0; every
@@ -229,7 +247,10 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (pj < S) {
       const uint16_t* src = p.k_prop + ((size_t)(b * S + pj) * Hkv + g) * D + dh * DH;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
+      for (int c = 0; c < NCH; ++c) {
+        kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
+        if (FP8 && p.append) kop[c] = fp8_stored_values(kop[c], p.k_scale_store);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -244,6 +265,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           uint16_t bits = 0;
           if (j < S) bits = p.v_prop[((size_t)(b * S + j) * Hkv + g) * D + vdim(dt)];
           v[j] = __builtin_bit_cast(__bf16, bits);
+          if (FP8 && p.append) v[j] = fp8_stored_value(v[j], p.v_scale_store);
         }
         vop[0][dt] = v;
       }
@@ -270,7 +292,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int srow = wave * 4 + lq;
   const bool srow_ok = srow < p.rows;
   const int si = (srow_ok ? srow : 0) / G;  // proposal index of the row
-  const int qp = MODE == MODE_GLOBAL ? p.pos[b * S + si] : 0;
+  const int qp = MODE == MODE_GLOBAL ? qpos_of(p, b, si) : 0;
 
   const int n_keys = region_keys<MODE>(p, b);
   if (!prop && k0 >= n_keys) return;  // past this request's keys (uniform over the workgroup)
@@ -291,7 +313,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // ---------------------------------------------------------- softmax
   const size_t slot = ((size_t)unit * p.nchunk + chunk) * p.rows;
-  const float qs = (FP8 && prop) ? p.qk_scale_prop : p.qk_scale;
+  const bool bf16_prop = FP8 && prop && !p.append;  // proposals as bf16 values, not codes
+  const float qs = bf16_prop ? p.qk_scale_prop : p.qk_scale;
   if (srow < ROWS) {
     const int kk = KPL * lr;
     // verify: slot age of the newest committed position, and the oldest age
@@ -374,7 +397,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // Lane (lr, lq) holds rows ct*16 + lr; group q of four consecutive dims
   // starts at qdim(q).  Proposal values are bf16, not codes: divided by
   // v_scale here so that the merge's v_scale restores them.
-  const float vs = (FP8 && prop) ? p.inv_v_scale : 1.f;
+  const float vs = bf16_prop ? p.inv_v_scale : 1.f;
   auto qdim = [&](int q) { return vw * DPW + (VPAIR ? 32 * (q >> 1) + 8 * lq + 4 * (q & 1) : 16 * q + 4 * lq); };
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {

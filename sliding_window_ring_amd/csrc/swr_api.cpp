@@ -42,11 +42,38 @@ swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
 
 swr_status to_status(hipError_t e) { return e == hipSuccess ? SWR_OK : SWR_ERR_LAUNCH; }
 
-// Shared validation and launch of the three attention calls.
-swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const int32_t* pos,
-                  const int32_t* key_count, const void* k_prop, const void* v_prop,
-                  int cap_or_max_keys, int B, int S, int Hq, int Hkv, int D, float scale, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
+// Launch of the append kernel for an already validated call.
+swr_status append_tokens(const swr_kv* kv, const void* k_new, const void* v_new, const int32_t* pos0,
+                         int B, int T, int Hkv, int D, int wrap, hipStream_t stream) {
+  swr::AppendParams p{};
+  p.k_base = static_cast<uint8_t*>(kv->k_base);
+  p.v_base = static_cast<uint8_t*>(kv->v_base);
+  p.k_off = kv->k_off;
+  p.v_off = kv->v_off;
+  p.cap_b = kv->cap_b;
+  p.cap = kv->cap;
+  p.wrap = wrap ? 1 : 0;
+  p.k_scale = kv->k_scale;
+  p.v_scale = kv->v_scale;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.pos0 = pos0;
+  p.n_new = nullptr;
+  p.B = B;
+  p.T = T;
+  p.Hkv = Hkv;
+  p.D = D;
+  return to_status(swr::launch_append(p, kv->dtype == SWR_KV_FP8_E4M3, stream));
+}
+
+// Shared validation and launch of the attention calls.  mode is what the
+// caller asked for (decode, verify, global); `append` fuses the append of the
+// tokens in k_prop / v_prop (decode: the new token at pos; global: S tokens
+// at pos0 .. pos0+S-1).
+swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* out,
+                  const int32_t* pos, const int32_t* key_count, const void* k_prop,
+                  const void* v_prop, int cap_or_max_keys, int B, int S, int Hq, int Hkv, int D,
+                  float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || D < 1) return SWR_ERR_INVALID;
   if (Hq % Hkv != 0) return SWR_ERR_INVALID;
   if (!std::isfinite(scale)) return SWR_ERR_INVALID;
@@ -55,16 +82,24 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   if (st != SWR_OK) return st;
   if (!q || !out || !pos || !aligned16(q) || !aligned16(out)) return SWR_ERR_INVALID;
   if (mode != swr::MODE_GLOBAL && kv->cap_b) return SWR_ERR_INVALID;  // rings share one window
-  if (mode == swr::MODE_VERIFY && (!k_prop || !v_prop || !aligned16(k_prop) || !aligned16(v_prop)))
+  if ((mode == swr::MODE_VERIFY || append) &&
+      (!k_prop || !v_prop || !aligned16(k_prop) || !aligned16(v_prop)))
     return SWR_ERR_INVALID;
   if (mode == swr::MODE_GLOBAL) {
-    if (!key_count || cap_or_max_keys < 1) return SWR_ERR_INVALID;
+    if ((!append && !key_count) || cap_or_max_keys < 1) return SWR_ERR_INVALID;
+    if (append && cap_or_max_keys < S) return SWR_ERR_INVALID;
     // the padded contraction reads pad64(key_count) slots of every region
     if ((long)(cap_or_max_keys + 63) / 64 * 64 > kv->cap) return SWR_ERR_INVALID;
   }
+  const int fp8 = kv->dtype == SWR_KV_FP8_E4M3;
   AttnPlan pl;
-  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, kv->dtype == SWR_KV_FP8_E4M3, cap_or_max_keys, &pl))
-    return SWR_ERR_UNSUPPORTED;
+  bool planned;
+  if (mode == swr::MODE_GLOBAL && append)
+    planned = swr::plan_global_append(B, S, Hq, Hkv, D, fp8, cap_or_max_keys, &pl);
+  else
+    planned = swr::plan_attention(append ? swr::MODE_DECODE_APPEND : mode, B, S, Hq, Hkv, D, fp8,
+                                  cap_or_max_keys, &pl);
+  if (!planned) return SWR_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes || !aligned16(ws))) return SWR_ERR_WORKSPACE;
   if (B == 0) return SWR_OK;
 
@@ -86,6 +121,19 @@ swr_status attend(int mode, const swr_kv* kv, const void* q, void* out, const in
   p.key_count = key_count;
   p.k_prop = static_cast<const uint16_t*>(k_prop);
   p.v_prop = static_cast<const uint16_t*>(v_prop);
+  p.k_scale_store = kv->k_scale;
+  p.v_scale_store = kv->v_scale;
+  if (mode == swr::MODE_GLOBAL && append) {
+    if (pl.chunked) {
+      p.append = 1;  // the proposals' chunk stores them
+    } else {
+      // long call: the append kernel first, then the streamed pass with the
+      // positions and key counts derived from pos0
+      const swr_status st2 = append_tokens(kv, k_prop, v_prop, pos, B, S, Hkv, D, 0, stream);
+      if (st2 != SWR_OK) return st2;
+      p.qpos_from_pos0 = 1;
+    }
+  }
   if (pl.chunked) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     p.ws_part = reinterpret_cast<float*>(w + pl.off_part);
@@ -145,7 +193,16 @@ swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const in
                           int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   if (!ring) return SWR_ERR_INVALID;
-  return attend(swr::MODE_DECODE, ring, q, out, pos, nullptr, nullptr, nullptr, ring->cap, B, 1, Hq,
+  return attend(swr::MODE_DECODE, 0, ring, q, out, pos, nullptr, nullptr, nullptr, ring->cap, B, 1,
+                Hq, Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+swr_status swr_swa_append_decode(const swr_kv* ring, const void* k_new, const void* v_new,
+                                 const void* q, void* out, const int32_t* pos, int B, int Hq,
+                                 int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!ring) return SWR_ERR_INVALID;
+  return attend(swr::MODE_DECODE, 1, ring, q, out, pos, nullptr, k_new, v_new, ring->cap, B, 1, Hq,
                 Hkv, D, scale, ws, ws_bytes, stream);
 }
 
@@ -154,16 +211,24 @@ swr_status swr_gqa_verify(const swr_kv* ring, const void* k_prop, const void* v_
                           int Hkv, int D, float scale, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   if (!ring) return SWR_ERR_INVALID;
-  return attend(swr::MODE_VERIFY, ring, q, out, pos0, nullptr, k_prop, v_prop, ring->cap, B, S, Hq,
-                Hkv, D, scale, ws, ws_bytes, stream);
+  return attend(swr::MODE_VERIFY, 0, ring, q, out, pos0, nullptr, k_prop, v_prop, ring->cap, B, S,
+                Hq, Hkv, D, scale, ws, ws_bytes, stream);
 }
 
 swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const int32_t* q_pos,
                              const int32_t* key_count, int max_key_count, int B, int S, int Hq,
                              int Hkv, int D, float scale, void* ws, size_t ws_bytes,
                              hipStream_t stream) {
-  return attend(swr::MODE_GLOBAL, kv, q, out, q_pos, key_count, nullptr, nullptr, max_key_count, B,
-                S, Hq, Hkv, D, scale, ws, ws_bytes, stream);
+  return attend(swr::MODE_GLOBAL, 0, kv, q, out, q_pos, key_count, nullptr, nullptr, max_key_count,
+                B, S, Hq, Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+swr_status swr_global_append_attend(const swr_kv* kv, const void* k_new, const void* v_new,
+                                    const void* q, void* out, const int32_t* pos0,
+                                    int max_key_count, int B, int S, int Hq, int Hkv, int D,
+                                    float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return attend(swr::MODE_GLOBAL, 1, kv, q, out, pos0, nullptr, k_new, v_new, max_key_count, B, S,
+                Hq, Hkv, D, scale, ws, ws_bytes, stream);
 }
 
 size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap_or_max_keys) {
@@ -172,6 +237,12 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
     case SWR_OP_SWA_DECODE: mode = swr::MODE_DECODE; S = 1; break;
     case SWR_OP_GQA_VERIFY: mode = swr::MODE_VERIFY; break;
     case SWR_OP_GLOBAL_ATTEND: mode = swr::MODE_GLOBAL; break;
+    case SWR_OP_SWA_APPEND_DECODE: mode = swr::MODE_DECODE_APPEND; S = 1; break;
+    case SWR_OP_GLOBAL_APPEND_ATTEND: {
+      AttnPlan pl;
+      if (!swr::plan_global_append(B, S, Hq, Hkv, D, 0, cap_or_max_keys, &pl)) return 0;
+      return pl.ws_bytes;
+    }
     default: return 0;
   }
   AttnPlan pl;

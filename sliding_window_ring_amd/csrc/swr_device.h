@@ -90,6 +90,85 @@ __device__ __forceinline__ uint32_t k_half_base(int g, int S, int tile_slot0, in
   return ((uint32_t)(g * S + tile_slot0) * (uint32_t)D + (uint32_t)(half * 16 * D)) * (uint32_t)esize;
 }
 
+// OCP E4M3FN code of value/scale: the quotient is formed in binary64 with
+// correct rounding (value is bf16, scale fp32, so the binary64 quotient sits
+// on the same side of every E4M3 rounding midpoint as the exact one), then
+// rounded to nearest, ties to even, on the E4M3 grid (quantum 2^-9 below
+// 2^-6, 2^(e-3) in binade e above), saturating at +-448.
+__device__ __forceinline__ uint8_t e4m3_encode(float value, float scale) {
+  const double v = __ddiv_rn((double)value, (double)scale);
+  const uint8_t sign = __builtin_signbit(v) ? 0x80 : 0x00;
+  const double a = __builtin_fabs(v);
+  if (__builtin_isnan(a)) return sign | 0x7F;
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < 0x1p-6) {
+    // subnormal range: code = round(a / 2^-9); 8 lands on the smallest normal 0x08
+    return sign | (uint8_t)__builtin_rint(a * 512.0);
+  }
+  // binade e (-6 .. 8) from the binary64 exponent field; a * 2^(3-e) is exact
+  int e = (int)((__builtin_bit_cast(uint64_t, a) >> 52) & 0x7FF) - 1023;
+  const double pow2 = __builtin_bit_cast(double, (uint64_t)(1023 + 3 - e) << 52);
+  int m = (int)__builtin_rint(a * pow2);  // 8 .. 16
+  if (m == 16) {
+    m = 8;
+    ++e;
+  }
+  return sign | (uint8_t)(((e + 7) << 3) | (m - 8));
+}
+
+// Writes head dims 8*d8 .. 8*d8+7 of one token's K and V (bf16 bits, two
+// per word) into slot `slot` of KV head g of a region storing S slots per
+// head: one K granule store (16 bytes bf16, 8 bytes fp8) and eight V element
+// stores into the slot's 8-slot V blocks.  fp8 regions take the E4M3 codes
+// of value/scale.  The buffer resources bound the stores to the region.
+template <bool FP8>
+__device__ __forceinline__ void store_token_piece(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int slot,
+                                                  int g, int S, int D, int d8, u32x4 kbits, u32x4 vbits,
+                                                  float k_scale, float v_scale) {
+  constexpr int ESZ = FP8 ? 1 : 2;
+  const int k32 = slot & 31;
+  const uint32_t koff = k_half_base(g, S, slot & ~31, (k32 >> 2) & 1, D, ESZ) +
+                        (uint32_t)((FP8 ? d8 >> 1 : d8) * 256 + (4 * (k32 >> 3) + (k32 & 3)) * 16 +
+                                   (FP8 ? (d8 & 1) * 8 : 0));
+  // V element (slot, g, d) at ((g*(S/8) + slot/8)*D + d)*8 + slot%8
+  const uint32_t vrow = (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * D + (size_t)d8 * 8) * 8 +
+                                   (size_t)(slot & 7));
+  if (!FP8) {
+    store16(rk, koff, kbits);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store2(rv, (vrow + 8 * e) * 2, (uint16_t)(vbits[e >> 1] >> (16 * (e & 1))));
+  } else {
+    uint32_t kc[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t kb16 = (kbits[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t vb16 = (vbits[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      kc[e >> 2] |= (uint32_t)e4m3_encode(__builtin_bit_cast(float, kb16 << 16), k_scale) << (8 * (e & 3));
+      store1(rv, vrow + 8 * e, e4m3_encode(__builtin_bit_cast(float, vb16 << 16), v_scale));
+    }
+    store8(rk, koff, u32x2{kc[0], kc[1]});
+  }
+}
+
+// The bf16 values an fp8 region holds for bf16 x after a store: the E4M3
+// codes of x/scale, decoded (in units of scale).
+__device__ __forceinline__ __bf16 fp8_stored_value(__bf16 x, float scale) {
+  return fp8x8_to_bf16x8(u32x2{(uint32_t)e4m3_encode((float)x, scale), 0u})[0];
+}
+
+__device__ __forceinline__ bf16x8 fp8_stored_values(bf16x8 x, float scale) {
+  u32x2 c = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e >> 2] |= (uint32_t)e4m3_encode((float)x[e], scale) << (8 * (e & 3));
+  return fp8x8_to_bf16x8(c);
+}
+
+// Waits until every vector memory access the wave has issued is complete,
+// stores included (on gfx9-family parts the vector memory counter covers
+// loads and stores), so that a later load by the wave sees what it stored.
+// The memory clobber keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 8
 // k-values of lane group l / 16; lane l receives C rows 4*(l/16) .. +3 of

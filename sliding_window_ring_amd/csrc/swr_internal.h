@@ -12,7 +12,9 @@ namespace swr {
 // in chunked form (chunked.hip) or, for long regions, as MODE_GSTREAM: the
 // single-pass split-K kernel of the ring calls over a contiguous region.
 // MODE_VERIFY runs in chunked form when the batch is small.
-enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3 };
+// MODE_DECODE_APPEND is a decode that first writes the new token into its
+// ring slot (the fused append + decode call).
+enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3, MODE_DECODE_APPEND = 4 };
 
 // Slots a region stores per KV head: its capacity rounded up to whole
 // 32-slot K tiles (region layout: swr_device.h).
@@ -34,8 +36,12 @@ struct AttnParams {
   uint16_t* out;           // bf16 [B][S][Hq][D]
   const int32_t* pos;      // decode: pos[B]; verify: pos0[B]; global (both forms): q_pos[B][S]
   const int32_t* key_count;  // global: [B]
-  const uint16_t* k_prop;  // verify: bf16 [B][S][Hkv][D]
+  const uint16_t* k_prop;  // verify: proposals; fused append: the tokens to store.  bf16 [B][S][Hkv][D]
   const uint16_t* v_prop;
+  int append;              // chunked verify over global regions: also store the proposals at pos0 + j
+  int qpos_from_pos0;      // streamed global: pos is pos0[B]; q_pos[b][i] = pos0[b] + i, key_count = pos0[b] + S
+  float k_scale_store;     // fp8 regions: the scales a stored token's K and V are divided by
+  float v_scale_store;
   float* ws_acc;           // split partials: [units][nsplit][rows][D]
   float* ws_ml;            // split partials: [units][nsplit][rows][2] (max, sum)
   int B, S, Hq, Hkv, G, rows;
@@ -46,6 +52,16 @@ struct AttnParams {
   float* ws_pml;           // [units][nchunk][rows][2] (max, sum) of each chunk
   int nchunk;              // chunks per unit (of the longest request; verify: + the proposals')
 };
+
+// Global calls: the key count of request b and the position of its query i,
+// from the arrays, or derived from pos0 when the call appended its S tokens
+// at pos0 .. pos0+S-1 itself.
+__device__ __forceinline__ int key_count_of(const AttnParams& p, int b) {
+  return p.qpos_from_pos0 ? p.pos[b] + p.S : p.key_count[b];
+}
+__device__ __forceinline__ int qpos_of(const AttnParams& p, int b, int i) {
+  return p.qpos_from_pos0 ? p.pos[b] + i : p.pos[b * p.S + i];
+}
 
 // Launch geometry chosen on the host for one attention call.
 struct AttnPlan {
@@ -80,6 +96,12 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
                     AttnPlan* plan);
 
 hipError_t launch_attention(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
+
+// Plan of a global call that appends its S tokens itself (max_keys bounds
+// pos0 + S): chunked verify over the regions, whose proposal chunk stores the
+// tokens, or for long calls the streamed global pass (run after the append
+// kernel, positions derived from pos0).
+bool plan_global_append(int B, int S, int Hq, int Hkv, int D, int fp8, int max_keys, AttnPlan* plan);
 
 struct AppendParams {
   uint8_t* k_base;

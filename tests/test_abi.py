@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_boundary_calls():
     names = declared_functions()
     for n in ["swr_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend",
-              "swr_workspace_bytes", "swr_status_string"]:
+              "swr_swa_append_decode", "swr_global_append_attend", "swr_workspace_bytes",
+              "swr_status_string"]:
         assert n in names
 
 
@@ -98,6 +99,46 @@ def test_verify_and_global_validation():
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6017, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 0, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == WORKSPACE
+
+
+def test_fused_append_decode_validation():
+    f = swr.lib.swr_swa_append_decode
+
+    def call(k=None, kn=FAKE, vn=FAKE, q=FAKE, out=FAKE, pos=FAKE, B=56, Hq=64, Hkv=8, D=256, ws=None, wsb=0):
+        r = kv() if k is None else k
+        return f(ctypes.byref(r), kn, vn, q, out, pos, B, Hq, Hkv, D, 0.0625, ws, wsb, None)
+
+    assert call(kn=None) == INVALID
+    assert call(vn=None) == INVALID
+    assert call(vn=FAKE + 2) == INVALID            # misaligned
+    assert call(pos=None) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    withcaps = kv()
+    withcaps.cap_b = FAKE
+    assert call(k=withcaps) == INVALID             # rings share one window
+    need = swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, 16, 1, 64, 8, 256, 1024)
+    assert need == swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, 16, 1, 64, 8, 256, 1024) > 0
+    assert call(B=16) == WORKSPACE
+    assert call(B=0) == OK
+
+
+def test_fused_global_append_validation():
+    g = swr.lib.swr_global_append_attend
+    rg = kv(cap=6016)
+
+    def call(kn=FAKE, vn=FAKE, pos0=FAKE, mk=6005, S=4, Hq=16, ws=None, wsb=0):
+        return g(ctypes.byref(rg), kn, vn, FAKE, FAKE, pos0, mk, 1, S, Hq, 2, 512, 0.04, ws, wsb, None)
+
+    assert call(kn=None) == INVALID
+    assert call(vn=FAKE + 8) == INVALID
+    assert call(pos0=None) == INVALID
+    assert call(mk=3) == INVALID                   # fewer keys than the tokens it appends
+    assert call(mk=6017) == INVALID                # padded contraction past the capacity
+    assert call(S=9) == UNSUPPORTED
+    need = swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 1, 4, 16, 2, 512, 6005)
+    assert need > 0
+    assert call() == WORKSPACE
+    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
 
 
 def test_append_validation():
