@@ -4,7 +4,10 @@
 One step = one sliding-window layer of the B=56 decode batch (append the new
 token into each request's 1024-slot ring, then GQA decode over the ring) plus
 one global layer of the 6005-key speculative verify (append the 4 proposals,
-then the grouped 32-row attention over the 64-padded region).  Every step
+then the grouped 32-row attention over the 64-padded region).  Each layer is
+one library call that does both (swr_swa_append_decode,
+swr_global_append_attend); the separate append and attention calls are timed
+beside it.  Every step
 uses the K/V of a different layer (3 sliding layers x 470 MB, 24 global
 layers x 24.6 MB, all carved from one pool), so the K/V stream comes from
 HBM and not from the 256 MB Infinity Cache.
@@ -105,7 +108,9 @@ def build_layers(swr, torch, pool):
 
 def algorithmic_bytes():
     """Bytes each operation must move (K/V read at the exact key count, new
-    tokens read and written, queries read, outputs written)."""
+    tokens read and written, queries read, outputs written), the same for the
+    fused calls as for the separate ones: the fused sliding call moves decode
+    + append_s, the fused global call glob + append_g."""
     decode = B * HKV * W * D * 2 * 2 + 2 * B * HKV * G * D * 2
     append_s = B * HKV * D * 2 * 2 * 2
     glob = KC * GHKV * GD * 2 * 2 + 2 * GS * GHKV * GG * GD * 2
@@ -250,12 +255,18 @@ def other_workloads(swr, torch, sweep=True):
             swr.kv_append(L, randn(w.B, w.W // 2, w.Hkv, w.D), randn(w.B, w.W // 2, w.Hkv, w.D),
                           (pos - w.W + 1 + half * (w.W // 2)).to(torch.int32))
         q = randn(w.B, w.Hq, w.D)
-        sets.append((L, q, pos, torch.empty_like(q)))
+        sets.append((L, q, pos, torch.empty_like(q), randn(w.B, w.Hkv, w.D), randn(w.B, w.Hkv, w.D)))
     us = _timed(torch, lambda i: swr.swa_decode(sets[i][0], sets[i][1], sets[i][2], w.Hkv, w.D ** -0.5,
                                                 out=sets[i][3]), 60, len(sets))
     nbytes = w.B * w.Hkv * w.W * w.D * 2 + 2 * w.B * w.Hq * w.D * 2
     res["sliding_decode_b56_fp8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                                      "algorithmic_bytes": nbytes}
+    # the same layer with its append (bf16 tokens in, fp8 codes stored)
+    us = _timed(torch, lambda i: swr.swa_append_decode(sets[i][0], sets[i][4], sets[i][5], sets[i][1], sets[i][2],
+                                                       w.D ** -0.5, out=sets[i][3]), 60, len(sets))
+    nbytes += w.B * w.Hkv * w.D * (2 + 1) * 2
+    res["sliding_decode_b56_fp8_append_and_attention"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                                          "algorithmic_bytes": nbytes}
     del sets
 
     # --- mixed step: 16 requests, contexts log-uniform [512, 65536], one pool
@@ -315,7 +326,23 @@ def other_workloads(swr, torch, sweep=True):
             2 * B * (ws_s.Hq * ws_s.D + ws_g.Hq * ws_g.D) * 2
         res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
                      "contexts": ctx}
-        del pool, sl, gl, dws, gws
+
+        # the same step with each layer appending its token first (the token
+        # at position ctx, already in the regions above, is written again)
+        kn_s, vn_s = randn(B, ws_s.Hkv, ws_s.D), randn(B, ws_s.Hkv, ws_s.D)
+        kn_g, vn_g = randn(B, 1, ws_g.Hkv, ws_g.D), randn(B, 1, ws_g.Hkv, ws_g.D)
+        fws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv,
+                                                      ws_g.D, max(ctx) + 1)), dtype=torch.uint8, device=dev)
+
+        def mixed_fused(_i):
+            swr.swa_append_decode(sl, kn_s, vn_s, qs, pos, ws_s.D ** -0.5, out=outs, ws=dws)
+            swr.global_append_attend(gl, kn_g, vn_g, qg, pos, max(ctx) + 1, ws_g.D ** -0.5, out=outg, ws=fws)
+
+        us = _timed(torch, mixed_fused, 30, 1)
+        nbytes += B * (ws_s.Hkv * ws_s.D + ws_g.Hkv * ws_g.D) * (2 + esz) * 2
+        res[name + "_append_and_attention"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                               "algorithmic_bytes": nbytes}
+        del pool, sl, gl, dws, gws, fws
         torch.cuda.synchronize()
 
     if not sweep:
@@ -391,15 +418,23 @@ def main():
         N_GLOBAL_SETS * 2 * swr.region_bytes(6016, GHKV, GD) + (1 << 20)
     pool = swr.Pool(per_layer_pool)
     sliding, glob = build_layers(swr, torch, pool)
-    gws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC), 16),
+    gws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC),
+                          swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC), 16),
                       dtype=torch.uint8, device="cuda")
-    dws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, HKV * G, HKV, D, W), 16),
+    dws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W), 16),
                       dtype=torch.uint8, device="cuda")
     scale_s, scale_g = D ** -0.5, GD ** -0.5
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
-    def global_layer(g):
+    def sliding_layer(s):  # append the token at pos into the ring, then decode
+        swr.swa_append_decode(s["L"], s["k_new"], s["v_new"], s["q"], s["pos"], scale_s, out=s["out"], ws=dws)
+
+    def global_layer(g):  # append the 4 proposals at ctx .. ctx+3, then the grouped verify
+        swr.global_append_attend(g["L"], g["k_prop"], g["v_prop"], g["q"], g["ctx"], KC, scale_g, out=g["out"],
+                                 ws=gws)
+
+    def global_separate(g):
         swr.kv_append(g["L"], g["k_prop"], g["v_prop"], g["ctx"], wrap=False)
         swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, scale_g, out=g["out"], ws=gws)
 
@@ -408,15 +443,12 @@ def main():
         g = glob[i % N_GLOBAL_SETS]
         if events:
             events[0].record()
-        swr.kv_append(s["L"], s["k_new"], s["v_new"], s["pos"])
+        sliding_layer(s)
         if events:
             events[1].record()
-        swr.swa_decode(s["L"], s["q"], s["pos"], HKV, scale_s, out=s["out"], ws=dws)
-        if events:
-            events[2].record()
         global_layer(g)
         if events:
-            events[3].record()
+            events[2].record()
 
     for i in range(args.warmup):
         step(i)
@@ -432,44 +464,46 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    append_s = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e3
-    decode_us = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e3
-    global_us = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps * 1e3
+    sliding_us = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e3
+    global_us = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e3
+
+    # The separate calls, each timed back to back over the same layer sets:
+    # the decode without its append, and the append alone.
+    decode_only_us = _timed(torch, lambda i: swr.swa_decode(sliding[i]["L"], sliding[i]["q"], sliding[i]["pos"], HKV,
+                                                            scale_s, out=sliding[i]["out"], ws=dws),
+                            30, N_SLIDING_SETS)
+    append_only_us = _timed(torch, lambda i: swr.kv_append(sliding[i]["L"], sliding[i]["k_new"], sliding[i]["v_new"],
+                                                           sliding[i]["pos"]), 30, N_SLIDING_SETS)
 
     # The global layer's launches are short: also time them the way a serving
-    # loop issues them, captured in one HIP graph holding all 24 global layers.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for g in glob:
-            global_layer(g)
-    graph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    g0.record()
-    for _ in range(reps):
+    # loop issues them, captured in one HIP graph holding all 24 global layers
+    # -- the fused call, the separate append + attention, and the attention
+    # call alone.
+    def graph_us(layer_fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for g in glob:
+                layer_fn(g)
         graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    global_graph_us = g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
-    # ... and the attention calls alone (24 in one graph), without the append
-    agraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(agraph):
-        for g in glob:
-            swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, scale_g, out=g["out"], ws=gws)
-    agraph.replay()
-    torch.cuda.synchronize()
-    g0.record()
-    for _ in range(reps):
-        agraph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    global_attn_graph_us = g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
+
+    global_graph_us = graph_us(global_layer)
+    global_sep_graph_us = graph_us(global_separate)
+    global_attn_graph_us = graph_us(lambda g: swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV,
+                                                                scale_g, out=g["out"], ws=gws))
     b_dec, b_app_s, b_glob, b_app_g = algorithmic_bytes()
     step_bytes = b_dec + b_app_s + b_glob + b_app_g
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = b_dec / (decode_us * 1e-6) / 1e9
-    traffic = measured_traffic(b_dec)
+    achieved = (b_dec + b_app_s) / (sliding_us * 1e-6) / 1e9
+    traffic = measured_traffic(b_dec + b_app_s)
 
     result = {
         "metric": "attention KV GB/s & % HBM peak; us/layer, sliding decode B=56 + global verify",
@@ -493,26 +527,29 @@ def main():
         },
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "us_per_layer": {
-            "sliding_decode_b56_attention": round(decode_us, 2),
-            "sliding_decode_b56_append": round(append_s, 2),
+            "sliding_decode_b56_append_and_attention": round(sliding_us, 2),
+            "sliding_decode_b56_attention_only": round(decode_only_us, 2),
+            "sliding_decode_b56_separate_append": round(append_only_us, 2),
             "global_verify_6005_append_and_attention": round(global_us, 2),
             "global_verify_6005_in_layer_graph": round(global_graph_us, 2),
+            "global_verify_6005_separate_append_and_attention_in_graph": round(global_sep_graph_us, 2),
             "global_verify_6005_attention_only_in_graph": round(global_attn_graph_us, 2),
         },
         "layer_gbs": {
-            "sliding_decode_b56_attention": round(achieved, 1),
+            "sliding_decode_b56_append_and_attention": round(achieved, 1),
+            "sliding_decode_b56_attention_only": round(b_dec / (decode_only_us * 1e-6) / 1e9, 1),
             "global_verify_6005": round((b_glob + b_app_g) / (global_us * 1e-6) / 1e9, 1),
             "global_verify_6005_in_layer_graph": round((b_glob + b_app_g) / (global_graph_us * 1e-6) / 1e9, 1),
         },
         "roofline": {
-            "kernel": "attn_kernel<256,256,1,4,bf16,decode> (swr_swa_decode, B=56)",
+            "kernel": "attn_kernel<256,256,1,4,bf16,decode+append> (swr_swa_append_decode, B=56)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": b_dec,
+            "algorithmic_bytes_per_launch": b_dec + b_app_s,
         },
         "host_wall_s": round(wall, 3),
     }

@@ -227,12 +227,21 @@ attn_kernel(const AttnParams p) {
   };
 
   // Fused append (decode): the new token, position pos in slot pos % W, is
-  // stored by the waves that read its tile, each its own head-dim slice, and
-  // that tile is the last one they read: the split walks its tiles in
-  // rotated order, starting after the token's tile.  The stores go out with
-  // the first loads; the wave waits for them once, just before the tile's
-  // loads are issued, so its later loads see them.  No other workgroup reads
-  // the tile.
+  // written by the waves that read its tile, each its own head-dim slice; no
+  // other workgroup reads the tile.  The split walks its tiles in rotated
+  // order, starting after the token's tile, so that this tile comes last
+  // (the writes then fall at the end of the read stream).
+  //  bf16: the wave loads the tile as it is (the slot still holds the token
+  //   it evicts), puts the new token into its operand registers, and stores
+  //   back every cache line of the tile that holds a byte of the slot, whole:
+  //   a line left partly written costs its next reader a merge with memory,
+  //   which over a batch's 64 lines per (request, KV head) measured about as
+  //   much as a separate append launch.
+  //  fp8 (the registers hold decoded values, not the stored codes): the
+  //   stores go out with the first loads and the wave waits for them once,
+  //   before the tile's loads.
+  constexpr bool SUBST = APP && !FP8;
+  constexpr bool FIRST = APP && FP8;
   const int nt = t_end - t_begin;
   int rot = 0;  // local tile index lam is tile t_begin + (lam + rot) mod nt
   bool writer = false;
@@ -252,7 +261,7 @@ attn_kernel(const AttnParams p) {
     return t_begin + x;
   };
   auto write_new = [&]() {
-    if (lane < DS / 8) {
+    if (FIRST && lane < DS / 8) {
       const int d8 = d_base / 8 + lane;
       const size_t src = ((size_t)b * Hkv + g) * D + (size_t)d8 * 8;
       const u32x4 kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
@@ -261,15 +270,26 @@ attn_kernel(const AttnParams p) {
     }
   };
 
+  // bf16: the wave's slice of the new token, staged in LDS until its tile
+  // comes round (K granules and V values by head dim)
+  __shared__ __attribute__((aligned(16))) __bf16 stage_k[SUBST ? D : 8], stage_v[SUBST ? D : 8];
+  const int k32_new = slot_new & 31;
+  const int h_new = (k32_new >> 2) & 1, r_new = 4 * (k32_new >> 3) + (k32_new & 3);
+
   if (kw < nt) {
     const int t0 = tile_at(kw);
-    if (APP && writer && t0 == t_new) {  // the wave's only tile: store, wait, then load
+    if (FIRST && writer && t0 == t_new) {  // the wave's only tile: store, wait, then load
       write_new();
       wait_vm_all();
     }
     load_k(t0);
     load_v(t0);
-    if (APP && writer && t0 != t_new) write_new();
+    if (FIRST && writer && t0 != t_new) write_new();
+    if (SUBST && writer && lane < DS / 8) {
+      const size_t src = ((size_t)b * Hkv + g) * D + d_base + (size_t)lane * 8;
+      *reinterpret_cast<u32x4*>(&stage_k[d_base + lane * 8]) = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+      *reinterpret_cast<u32x4*>(&stage_v[d_base + lane * 8]) = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+    }
   }
 
   for (int it = 0; it < n_it; ++it) {
@@ -283,6 +303,40 @@ attn_kernel(const AttnParams p) {
     const int t_next = has_next ? tile_at(lam + KW) : 0;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     const int kb = t * 32;
+    const bool subst = SUBST && writer && t == t_new;  // wave-uniform
+
+    if (subst) {
+      // K: row r_new of half h_new is the new token; the lanes of the 8-row
+      // group holding it store their granules back (4 whole lines per chunk)
+      const uint32_t hb = k_half_base(g, S_r, kb, h_new, D, ESZ) + (uint32_t)(lr * 16);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (sub != h_new) continue;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (lr == r_new) kop[sub][c] = *reinterpret_cast<const bf16x8*>(&stage_k[d_base + kdim(c)]);
+          if ((lr >> 3) == (r_new >> 3))
+            store16(rk, hb + (uint32_t)((d_base + kdim(c)) / 8) * 256, __builtin_bit_cast(u32x4, kop[sub][c]));
+        }
+      }
+      // V: lane group k32/8 holds the slot's 8-key blocks; element k32%8 of
+      // each is the new token; the 16 lanes of the group store 256 bytes
+      if (lq == (k32_new >> 3)) {
+        const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + (kb >> 3) + lq) * D;
+        const int e = k32_new & 7;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          u32x4 w = __builtin_bit_cast(u32x4, vop[dt]);
+          const uint32_t nv = __builtin_bit_cast(uint16_t, stage_v[vdim(dt)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j == (e >> 1)) w[j] = (e & 1) ? ((w[j] & 0x0000FFFFu) | (nv << 16)) : ((w[j] & 0xFFFF0000u) | nv);
+          }
+          vop[dt] = __builtin_bit_cast(bf16x8, w);
+          store16(rv, (vblock + (uint32_t)vdim(dt)) * 16, w);
+        }
+      }
+    }
 
     // ------------------------------------------------ scores = K . Q^T
     f32x4 sc[2][NCT];
@@ -296,7 +350,7 @@ attn_kernel(const AttnParams p) {
         sc[sub][ct] = acc;
       }
     if (has_next) {
-      if (APP && writer && t_next == t_new) wait_vm_all();
+      if (FIRST && writer && t_next == t_new) wait_vm_all();
       load_k(t_next);
     }
 
