@@ -47,17 +47,18 @@
  *   e = 2 bytes (SWR_KV_BF16) or 1 byte (SWR_KV_FP8_E4M3); a granule is 16
  *   bytes = R dims of one slot (R = 8 bf16, 16 fp8):
  *     K: slot s = 32t + k lies in tile t, half h = (k/4)%2, row
- *       r = 4*(k/8) + k%4; each half holds its 16 rows granule-major.
- *       Byte offset of (s, g, d):
- *         ((g*S + 32t)*D + h*16*D)*e + (d/R)*256 + r*16 + (d%R)*e
- *       i.e. K is [Hkv][S/32][2][D/R][16][R]
+ *       r = 4*(k/8) + k%4; each half holds its 16 rows in 1 KB blocks of
+ *       four granules per row (granule q = d/R).  Byte offset of (s, g, d):
+ *         ((g*S + 32t)*D + h*16*D)*e + (q/4)*1024 + r*64 + (q%4)*16 + (d%R)*e
+ *       i.e. K is [Hkv][S/32][2][D/(4R)][16][4][R]; D is a multiple of 4R
  *     V element (s, g, d) at element index ((g*(S/8) + s/8)*D + d)*8 + (s%8)
  *       i.e. V is [Hkv][S/8][D][8]: blocks of 8 slots
  *   Each (request, KV head) reads one contiguous K stream and one contiguous
  *   V stream, which is what HBM streams best.  The K row order inside a tile
  *   is the key order of the gfx950 bf16 matrix instruction's operand in the
- *   kernels, and the granule-major halves make each operand load of a lane
- *   group one contiguous kilobyte.  V is kept in blocks of 8 slots so that
+ *   kernels; a lane group's operand load (16 rows x 4 granules) is one
+ *   contiguous 1 KB block, and a row's four granules are 64 contiguous
+ *   bytes, so a token written on its own touches few cache lines.  V is kept in blocks of 8 slots so that
  *   the values of one dim for 8 consecutive slots are contiguous: the
  *   operand shape along the key axis.  A region is S*Hkv*D*e bytes
  *   (swr_kv_region_bytes).

@@ -143,12 +143,17 @@ static int elem_size(int dtype) { return dtype == ORC_FP8 ? 1 : 2; }
 /* Slots stored per KV head for a region of `cap` slots. */
 static int64_t stored_slots(int64_t cap) { return (cap + 31) / 32 * 32; }
 
+/* K blocks hold four granules of each of 16 rows: D must be a multiple of
+ * four granules (32 bf16 dims, 64 fp8 dims). */
+static int k_layout_ok(int D, int dtype) { return D > 0 && D % (4 * (16 / elem_size(dtype))) == 0; }
+
 static size_t k_index(int64_t s, int g, int d, int64_t cap, int D, int dtype) {
   const int64_t S = stored_slots(cap);
   const int64_t R = 16 / elem_size(dtype); /* dims per 16-byte granule */
   const int64_t t = s / 32, k = s % 32;
   const int64_t h = (k / 4) % 2, r = 4 * (k / 8) + k % 4;
-  return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D + (d / R) * 16 * R + r * R + d % R);
+  const int64_t q = d / R; /* granule; four granules of a row sit together */
+  return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D + (q / 4) * 64 * R + r * 4 * R + (q % 4) * R + d % R);
 }
 
 static size_t v_index(int64_t s, int g, int d, int64_t cap, int D) {
@@ -195,7 +200,7 @@ int orc_kv_append(uint8_t* k_base, uint8_t* v_base, const int64_t* k_off, const 
                   int cap, const int32_t* caps, int dtype, float k_scale, float v_scale,
                   const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos0,
                   const int32_t* n_new, int B, int T, int Hkv, int D, int wrap) {
-  if (cap <= 0 || cap % 8 != 0 || B < 0 || T < 0 || Hkv <= 0 || D <= 0) return ORC_EINVAL;
+  if (cap <= 0 || cap % 8 != 0 || B < 0 || T < 0 || Hkv <= 0 || !k_layout_ok(D, dtype)) return ORC_EINVAL;
   if (wrap && caps) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int n = n_new ? n_new[b] : T;
@@ -348,7 +353,7 @@ int orc_swa_decode(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
                    const int64_t* v_off, int W, int dtype, double k_scale, double v_scale,
                    const uint16_t* q, const int32_t* pos, int B, int Hq, int Hkv, int D,
                    double scale, double* out) {
-  if (check_common(B, 1, Hq, Hkv, D) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, 1, Hq, Hkv, D) || !k_layout_ok(D, dtype) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b)
     if (pos[b] < 0) return ORC_EINVAL;
   int G = Hq / Hkv, rc = ORC_OK;
@@ -394,7 +399,7 @@ int orc_gqa_verify(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
                    const uint16_t* k_prop, const uint16_t* v_prop, const uint16_t* q,
                    const int32_t* pos0, int B, int S, int Hq, int Hkv, int D, double scale,
                    double* out) {
-  if (check_common(B, S, Hq, Hkv, D) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, S, Hq, Hkv, D) || !k_layout_ok(D, dtype) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b)
     if (pos0[b] < 0) return ORC_EINVAL;
   int G = Hq / Hkv, rows = G * S, rc = ORC_OK;
@@ -447,7 +452,7 @@ int orc_global_attend(const uint8_t* k_base, const uint8_t* v_base, const int64_
                       double k_scale, double v_scale, const uint16_t* q, const int32_t* q_pos,
                       const int32_t* key_count, int padded, int B, int S, int Hq, int Hkv, int D,
                       double scale, double* out) {
-  if (check_common(B, S, Hq, Hkv, D) || cap <= 0 || cap % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, S, Hq, Hkv, D) || !k_layout_ok(D, dtype) || cap <= 0 || cap % 8 != 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int64_t kc = key_count[b], kp = padded ? (kc + 63) / 64 * 64 : kc;
     int64_t cb = region_cap(cap, caps, b);

@@ -156,18 +156,18 @@ attn_kernel(const AttnParams p) {
       const int e = 8 * (lr >> 2) + 4 * sub + (lr & 3);
       if (!prop_tile) {
         constexpr int R = FP8 ? 16 : 8;  // dims per 16-byte granule
-        const uint32_t hb = k_half_base(g, S_r, kb, sub, D, ESZ) + (uint32_t)(lr * 16);
+        const uint32_t hb = k_half_base(g, S_r, kb, sub, D, ESZ);
         if (FP8) {
 #pragma unroll
           for (int c = 0; c < NCH; c += 2) {
-            const u32x4 w = load16_stream(rk, hb + (uint32_t)((d_base + kdim(c)) / R) * 256);
+            const u32x4 w = load16_stream(rk, hb + k_granule_offset((d_base + kdim(c)) / R, lr));
             kop[sub][c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
             kop[sub][c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
           }
         } else {
 #pragma unroll
           for (int c = 0; c < NCH; ++c)
-            kop[sub][c] = as_bf16x8(load16_stream(rk, hb + (uint32_t)((d_base + kdim(c)) / R) * 256));
+            kop[sub][c] = as_bf16x8(load16_stream(rk, hb + k_granule_offset((d_base + kdim(c)) / R, lr)));
         }
       } else {
 #pragma unroll
@@ -306,17 +306,18 @@ attn_kernel(const AttnParams p) {
     const bool subst = SUBST && writer && t == t_new;  // wave-uniform
 
     if (subst) {
-      // K: row r_new of half h_new is the new token; the lanes of the 8-row
-      // group holding it store their granules back (4 whole lines per chunk)
-      const uint32_t hb = k_half_base(g, S_r, kb, h_new, D, ESZ) + (uint32_t)(lr * 16);
+      // K: row r_new of half h_new is the new token; the lanes of the two
+      // rows sharing its lines store their granules back (one whole 128-byte
+      // line per chunk)
+      const uint32_t hb = k_half_base(g, S_r, kb, h_new, D, ESZ);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (sub != h_new) continue;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           if (lr == r_new) kop[sub][c] = *reinterpret_cast<const bf16x8*>(&stage_k[d_base + kdim(c)]);
-          if ((lr >> 3) == (r_new >> 3))
-            store16(rk, hb + (uint32_t)((d_base + kdim(c)) / 8) * 256, __builtin_bit_cast(u32x4, kop[sub][c]));
+          if ((lr >> 1) == (r_new >> 1))
+            store16(rk, hb + k_granule_offset((d_base + kdim(c)) / 8, lr), __builtin_bit_cast(u32x4, kop[sub][c]));
         }
       }
       // V: lane group k32/8 holds the slot's 8-key blocks; element k32%8 of

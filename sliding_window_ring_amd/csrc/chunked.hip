@@ -208,11 +208,11 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   if (!prop) {
     // row lr of half kq%2 of tile kq/2; granule (dh*DH + kdim(c)) / R of it
     constexpr int R = FP8 ? 16 : 8;
-    const uint32_t hb = k_half_base(g, S_r, k0 + 32 * (kq >> 1), kq & 1, D, ESZ) + (uint32_t)(lr * 16);
+    const uint32_t hb = k_half_base(g, S_r, k0 + 32 * (kq >> 1), kq & 1, D, ESZ);
     if (KPAIR) {
 #pragma unroll
       for (int c = 0; c < NCH; c += 2) {
-        const u32x4 w = load16_stream(rk, hb + (uint32_t)((dh * DH + kdim(c)) / R) * 256);
+        const u32x4 w = load16_stream(rk, hb + k_granule_offset((dh * DH + kdim(c)) / R, lr));
         kop[c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
         kop[c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
       }
@@ -220,7 +220,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int dim = dh * DH + kdim(c);
-        const uint32_t off = hb + (uint32_t)(dim / R) * 256 + (uint32_t)((dim % R) * ESZ);
+        const uint32_t off = hb + k_granule_offset(dim / R, lr) + (uint32_t)((dim % R) * ESZ);
         kop[c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
       }
     }

@@ -75,19 +75,26 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 //   K: tiles of 32 slots.  Slot 32t + k sits in half h = (k/4)%2, row
 //      r = 4*(k/8) + k%4 of tile t -- row r of half h is exactly MFMA A row r
 //      of the score sub-tile h (keys 8*(r/4) + 4h + r%4), whose C fragment
-//      is the P^T fragment of the value product.  Each half holds its 16
-//      rows granule-major: D/R granules of 16 rows x 16 bytes (R = 8 bf16 or
-//      16 fp8 dims), so one lane group's operand load (4 granules x 16 rows)
-//      is 1 KB of contiguous memory.
-//        byte offset = ((g*S + 32t)*D + h*16*D)*esize + (d/R)*256 + r*16 + (d%R)*esize
+//      is the P^T fragment of the value product.  A granule is 16 bytes of
+//      one row (R = 8 bf16 or 16 fp8 dims); each half holds its 16 rows in
+//      1 KB blocks of four granules, row-major in the block: one lane
+//      group's operand load (4 granules x 16 rows) is one contiguous block,
+//      and a row's four granules are 64 contiguous bytes (a token written
+//      alone touches half as many lines, a quarter as many as granule-major).
+//        byte offset = ((g*S + 32t)*D + h*16*D)*esize + (q/4)*1024 + r*64 + (q%4)*16 + (d%R)*esize,
+//        q = d/R
 //   V: blocks of 8 slots, ((g*(S/8) + slot/8)*D + d)*8 + slot%8 elements:
 //      one 16-byte load is 8 consecutive keys of one dim (the V^T operand).
 // (stored_slots: swr_internal.h)
 
-// Byte offset of K granule (slot-half base, granule q, row r): the start of
-// the half is ((g*S + 32t)*D + h*16*D)*esize.
+// Byte offset of the start of a K tile half: ((g*S + 32t)*D + h*16*D)*esize.
 __device__ __forceinline__ uint32_t k_half_base(int g, int S, int tile_slot0, int half, int D, int esize) {
   return ((uint32_t)(g * S + tile_slot0) * (uint32_t)D + (uint32_t)(half * 16 * D)) * (uint32_t)esize;
+}
+
+// Byte offset, within a K tile half, of granule q of row r.
+__device__ __forceinline__ uint32_t k_granule_offset(int q, int r) {
+  return (uint32_t)((q >> 2) * 1024 + r * 64 + (q & 3) * 16);
 }
 
 // OCP E4M3FN code of value/scale: the quotient is formed in binary64 with
@@ -128,8 +135,8 @@ __device__ __forceinline__ void store_token_piece(__amdgpu_buffer_rsrc_t rk, __a
   constexpr int ESZ = FP8 ? 1 : 2;
   const int k32 = slot & 31;
   const uint32_t koff = k_half_base(g, S, slot & ~31, (k32 >> 2) & 1, D, ESZ) +
-                        (uint32_t)((FP8 ? d8 >> 1 : d8) * 256 + (4 * (k32 >> 3) + (k32 & 3)) * 16 +
-                                   (FP8 ? (d8 & 1) * 8 : 0));
+                        k_granule_offset(FP8 ? d8 >> 1 : d8, 4 * (k32 >> 3) + (k32 & 3)) +
+                        (uint32_t)(FP8 ? (d8 & 1) * 8 : 0);
   // V element (slot, g, d) at ((g*(S/8) + slot/8)*D + d)*8 + slot%8
   const uint32_t vrow = (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * D + (size_t)d8 * 8) * 8 +
                                    (size_t)(slot & 7));

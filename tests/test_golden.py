@@ -34,7 +34,7 @@ def test_padded_contraction_length_is_6016_for_6005_keys():
     g = FACTS["global_key_count"]
     kc, padded = g["value"], g["padded_to"]
     assert padded - kc == g["extra_columns"] and padded % g["pad_multiple"] == 0
-    hkv, d = 1, 8
+    hkv, d = 1, 32
     k = synthetic.normal_bf16(synthetic.rng(3), (1, kc, hkv, d))
     q = synthetic.normal_bf16(synthetic.rng(4), (1, 1, 1, d))
     qp = np.array([[kc - 1]], np.int32)
@@ -51,7 +51,7 @@ def test_padded_contraction_length_is_6016_for_6005_keys():
 @pytest.mark.parametrize("pos,slot", [(1023, 1023), (1024, 0), (2500, 452), (4096, 0), (8191, 1023)])
 def test_ring_slot_of_position_for_window_1024(pos, slot):
     W = FACTS["sliding_window"]["window"]
-    hkv, d = 1, 8
+    hkv, d = 1, 32
     rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
     kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
     off = np.zeros(1, np.int64)

@@ -70,7 +70,7 @@ def check_decode_batch(B=5, W=64, Hkv=2, G=4, D=32, positions=(0, 10, 63, 64, 20
 
 def check_rotation_invariance():
     """The same window stored at a different rotation gives the same output."""
-    W, Hkv, G, D = 32, 1, 2, 16
+    W, Hkv, G, D = 32, 1, 2, 32
     w = synthetic.Workload("t", B=1, Hkv=Hkv, G=G, D=D, W=W)
     x = synthetic.sliding_decode(w, seed=12, positions=[100])
     outs = []
@@ -86,7 +86,7 @@ def check_rotation_invariance():
 
 
 def check_zero_keys_give_mean_of_values():
-    W, Hkv, G, D = 32, 2, 2, 16
+    W, Hkv, G, D = 32, 2, 2, 32
     w = synthetic.Workload("t", B=2, Hkv=Hkv, G=G, D=D, W=W)
     x = synthetic.sliding_decode(w, seed=13, positions=[20, 77])
     k0 = np.zeros_like(x["k"])
@@ -100,7 +100,7 @@ def check_zero_keys_give_mean_of_values():
 
 
 def check_identical_queries_identical_outputs():
-    W, Hkv, G, D = 32, 2, 4, 16
+    W, Hkv, G, D = 32, 2, 4, 32
     w = synthetic.Workload("t", B=1, Hkv=Hkv, G=G, D=D, W=W)
     x = synthetic.sliding_decode(w, seed=14, positions=[50])
     q = x["q"].copy()
@@ -151,7 +151,7 @@ def check_verify_matches_sdpa():
 def check_verify_masks():
     """Row i ignores proposals after i and the i+1 oldest ring keys, and does
     depend on the oldest key it should see."""
-    W, Hkv, G, D, S = 32, 1, 2, 16, 4
+    W, Hkv, G, D, S = 32, 1, 2, 32, 4
     w = synthetic.Workload("t", B=1, Hkv=Hkv, G=G, D=D, W=W, S=S)
     x = synthetic.sliding_verify(w, seed=22, positions=[90])  # full ring, p0 >= W
     base = run_verify(x, W, Hkv, 0.25)
@@ -179,7 +179,7 @@ def check_verify_masks():
 
 
 def check_verify_single_proposal_is_decode():
-    W, Hkv, G, D = 32, 2, 2, 16
+    W, Hkv, G, D = 32, 2, 2, 32
     w = synthetic.Workload("t", B=3, Hkv=Hkv, G=G, D=D, W=W, S=1)
     x = synthetic.sliding_verify(w, seed=24, positions=[5, 32, 77])
     ver = run_verify(x, W, Hkv, 0.25)
@@ -233,7 +233,7 @@ def check_padded_tail_leaves_output_unchanged():
 
 
 def check_global_equals_sliding_when_window_covers_context():
-    kc, Hkv, G, D = 40, 2, 2, 16
+    kc, Hkv, G, D = 40, 2, 2, 32
     w = synthetic.Workload("t", B=1, Hkv=Hkv, G=G, D=D, S=1, key_count=kc)
     x = synthetic.global_verify(w, seed=33)
     kp, vp, ko, vo = global_pools(x["k"], x["v"], x["key_count"], 64)
@@ -245,7 +245,7 @@ def check_global_equals_sliding_when_window_covers_context():
 
 
 def check_fp8_power_of_two_scales_equal_dequantised_bf16():
-    W, Hkv, G, D = 32, 2, 2, 32
+    W, Hkv, G, D = 32, 2, 2, 64
     w = synthetic.Workload("t", B=2, Hkv=Hkv, G=G, D=D, W=W)
     x = synthetic.sliding_decode(w, seed=41, positions=[20, 90])
     ks, vs = 2.0 ** -3, 2.0 ** -4

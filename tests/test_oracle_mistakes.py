@@ -29,6 +29,8 @@ MISTAKES = [
      "const int64_t h = k / 16, r = k % 16;"),
     ("K granule ignores the element size", "const int64_t R = 16 / elem_size(dtype); /* dims per 16-byte granule */",
      "const int64_t R = 8;"),
+    ("K granules not grouped by row", "(q / 4) * 64 * R + r * 4 * R + (q % 4) * R + d % R",
+     "q * 16 * R + r * R + d % R"),
     ("K head stride ignores the tile padding", "return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D",
      "return (size_t)(((int64_t)g * cap + 32 * t) * D + h * 16 * D"),
     ("append slot off by one", "int64_t s = wrap ? p % cb : p;", "int64_t s = wrap ? (p + 1) % cb : p;"),

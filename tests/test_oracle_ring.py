@@ -24,14 +24,15 @@ def stored(cap):
 
 def k_view(pool, off, cap, hkv, d, esize=2):
     """[slot][Hkv][D] view of a K region: tiles of 32 slots, each two halves
-    of 16 rows stored granule-major ([Hkv][S/32][2][D/R][16][R])."""
+    of 16 rows; a half holds blocks of four 16-byte granules, row-major within
+    the block ([Hkv][S/32][2][D/(4R)][16][4][R])."""
     S, R = stored(cap), 16 // esize
     a = pool[off:off + S * hkv * d * esize].view(np.uint16 if esize == 2 else np.uint8)
-    a = a.reshape(hkv, S // 32, 2, d // R, 16, R)
+    a = a.reshape(hkv, S // 32, 2, d // (4 * R), 16, 4, R)
     slot = np.arange(cap)
     t, k = slot // 32, slot % 32
     half, row = (k // 4) % 2, 4 * (k // 8) + k % 4
-    return a[:, t, half, :, row, :].reshape(cap, hkv, d)
+    return a[:, t, half, :, row, :, :].reshape(cap, hkv, d)
 
 
 def v_view(pool, off, cap, hkv, d, esize=2):
@@ -50,7 +51,7 @@ def position_tokens(n, hkv, d, base=0):
 
 
 def test_slot_is_position_mod_window_one_by_one():
-    W, hkv, d = 16, 2, 8
+    W, hkv, d = 16, 2, 32
     rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
     kp = np.zeros(rb, np.uint8)
     vp = np.zeros(rb, np.uint8)
@@ -70,7 +71,7 @@ def test_slot_is_position_mod_window_one_by_one():
 
 
 def test_batched_append_equals_sequential_appends():
-    W, hkv, d, T = 16, 1, 8, 37
+    W, hkv, d, T = 16, 1, 32, 37
     g = synthetic.rng(5)
     k = synthetic.normal_bf16(g, (3, T, hkv, d))
     v = synthetic.normal_bf16(g, (3, T, hkv, d))
@@ -89,7 +90,7 @@ def test_batched_append_equals_sequential_appends():
 
 
 def test_global_mode_slot_is_position_and_bounds():
-    cap, hkv, d = 64, 2, 8
+    cap, hkv, d = 64, 2, 32
     rb = oracle.region_bytes(cap, hkv, d, oracle.BF16)
     kp, vp = np.zeros(rb, np.uint8), np.zeros(rb, np.uint8)
     off = np.zeros(1, np.int64)
@@ -105,7 +106,7 @@ def test_global_mode_slot_is_position_and_bounds():
 
 
 def test_fp8_append_stores_encoded_codes():
-    W, hkv, d = 16, 2, 32
+    W, hkv, d = 16, 2, 64
     g = synthetic.rng(9)
     k = synthetic.normal_bf16(g, (1, 5, hkv, d))
     v = synthetic.normal_bf16(g, (1, 5, hkv, d))
