@@ -6,6 +6,8 @@
 //             ("Announcing Carat", ring buffer section; "Improving Decode
 //             Throughput on Intel Gaudi 3", Our approach: the ring is read in
 //             place, in storage order, with no gather and no un-rotation);
+//             with the append, the same launch first writes the new token
+//             into its slot (the token replaces the oldest one);
 //   verify  : G heads x S proposals per KV head over the ring plus the
 //             proposals ("Announcing Carat", Doing it all in one kernel can be
 //             slower: the grouped rows share one K/V stream);

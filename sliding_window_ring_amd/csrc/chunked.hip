@@ -20,7 +20,8 @@
 // not bandwidth, is what bounds a job this small.  So a block of keys (two
 // of the page's 64-key pads) becomes the unit of work:
 //   pass 1 (chunk_kernel): one workgroup per (request, KV head, 128 keys)
-//     issues every K, V and Q load on entry, then runs the three products of
+//     issues its K and Q loads on entry and its V loads as soon as the
+//     scores are computed, and runs the three products of
 //     the page on its chunk -- scores (bf16 MFMA, fp32), the masked softmax
 //     over the chunk, and P x V (bf16 MFMA, fp32) -- with Q, the scores and
 //     P kept in LDS, and writes the chunk's unnormalised rows with their
@@ -71,10 +72,6 @@ __device__ __forceinline__ int region_keys(const AttnParams& p, int b) {
 // ------------------------------------------------------------------ pass 1
 
 constexpr int kChunkKeys = 128;                 // keys per workgroup of pass 1
-// V loads go out once the chunk's scores are computed rather than on entry:
-// a smaller first burst of requests across all workgroups streams faster,
-// and the value loads still overlap the softmax.
-constexpr bool kLateV = true;
 constexpr int kChunkWaves = kChunkKeys / 8;     // 16 waves: two per 16-key subtile
 
 // Chunks of one (request, KV head) that pass 1 filled, a prefix of the
@@ -224,7 +221,6 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         kop[c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
       }
     }
-    if (!kLateV) load_v();
   } else {
     if (p.append) {  // the proposals into their slots, 8 head dims per thread
       const int per = D / 8;
@@ -308,7 +304,10 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     // C rows 4*lq + r are keys 8*lq + 4*(kq%2) + r of tile kq/2
     *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][32 * (kq >> 1) + 8 * lq + 4 * (kq & 1)]) = acc;
   }
-  if (kLateV && !prop) load_v();
+  // V loads go out once the chunk's scores are computed rather than on
+  // entry: a smaller first burst of requests across all workgroups streams
+  // faster, and the value loads still overlap the softmax.
+  if (!prop) load_v();
   __syncthreads();
 
   // ---------------------------------------------------------- softmax

@@ -44,7 +44,7 @@ swr_status to_status(hipError_t e) { return e == hipSuccess ? SWR_OK : SWR_ERR_L
 
 // Launch of the append kernel for an already validated call.
 swr_status append_tokens(const swr_kv* kv, const void* k_new, const void* v_new, const int32_t* pos0,
-                         int B, int T, int Hkv, int D, int wrap, hipStream_t stream) {
+                         const int32_t* n_new, int B, int T, int Hkv, int D, int wrap, hipStream_t stream) {
   swr::AppendParams p{};
   p.k_base = static_cast<uint8_t*>(kv->k_base);
   p.v_base = static_cast<uint8_t*>(kv->v_base);
@@ -58,7 +58,7 @@ swr_status append_tokens(const swr_kv* kv, const void* k_new, const void* v_new,
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.pos0 = pos0;
-  p.n_new = nullptr;
+  p.n_new = n_new;
   p.B = B;
   p.T = T;
   p.Hkv = Hkv;
@@ -129,7 +129,7 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
     } else {
       // long call: the append kernel first, then the streamed pass with the
       // positions and key counts derived from pos0
-      const swr_status st2 = append_tokens(kv, k_prop, v_prop, pos, B, S, Hkv, D, 0, stream);
+      const swr_status st2 = append_tokens(kv, k_prop, v_prop, pos, nullptr, B, S, Hkv, D, 0, stream);
       if (st2 != SWR_OK) return st2;
       p.qpos_from_pos0 = 1;
     }
@@ -168,25 +168,7 @@ swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
   if (!k_new || !v_new || !pos0 || !aligned16(k_new) || !aligned16(v_new)) return SWR_ERR_INVALID;
   if (wrap && kv->cap_b) return SWR_ERR_INVALID;  // rings share one window
   if (B == 0) return SWR_OK;
-  swr::AppendParams p{};
-  p.k_base = static_cast<uint8_t*>(kv->k_base);
-  p.v_base = static_cast<uint8_t*>(kv->v_base);
-  p.k_off = kv->k_off;
-  p.v_off = kv->v_off;
-  p.cap_b = kv->cap_b;
-  p.cap = kv->cap;
-  p.wrap = wrap ? 1 : 0;
-  p.k_scale = kv->k_scale;
-  p.v_scale = kv->v_scale;
-  p.k_new = static_cast<const uint16_t*>(k_new);
-  p.v_new = static_cast<const uint16_t*>(v_new);
-  p.pos0 = pos0;
-  p.n_new = n_new;
-  p.B = B;
-  p.T = T;
-  p.Hkv = Hkv;
-  p.D = D;
-  return to_status(swr::launch_append(p, kv->dtype == SWR_KV_FP8_E4M3, stream));
+  return append_tokens(kv, k_new, v_new, pos0, n_new, B, T, Hkv, D, wrap, stream);
 }
 
 swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const int32_t* pos, int B,

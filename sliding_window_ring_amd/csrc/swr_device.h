@@ -27,10 +27,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
 // Streaming read: the non-temporal cache policy (bit 1 of the aux operand on
 // gfx94x/gfx950) marks lines read once, so K/V streams do not evict reused data.
 __device__ __forceinline__ u32x4 load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
