@@ -126,6 +126,13 @@ struct ChunkSmem {
   __attribute__((aligned(16))) __bf16 qbuf[16 * NCT][D + 8];
 };
 
+// The call's own tokens, staged by the global chunk that holds their slots
+// when a bf16 global call appends them itself: dynamic LDS of [2][S][D]
+// bf16 (K, then V), sized at launch -- none for the other calls.
+extern __shared__ __attribute__((aligned(16))) __bf16 chunk_tokens[];
+template <int MODE, bool FP8>
+constexpr bool stages_tokens() { return MODE == MODE_GLOBAL && !FP8; }
+
 // One chunk of one (request, KV head); every wave of the workgroup calls it
 // with the same arguments.  Returns early (all waves alike) for a chunk past
 // the request's keys; waves without value work return after the softmax.
@@ -267,6 +274,33 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
     }
   }
+  // bf16 global call that appends its own S tokens (keys pos0 .. pos0+S-1):
+  // the chunk holding any of their slots stages them in LDS (one 16-byte
+  // piece of K and of V per thread: S*D/8 <= 512 pieces), loaded here behind
+  // the region's loads and written to LDS after the Q loads have gone out
+  // (the load counter drains in order, so writing them first would hold the
+  // Q loads back until the region's data arrived); the Q barrier covers the
+  // writes.  The operands take them in place of the slots' old contents, and
+  // the regions receive them from the merge pass, after every chunk has read.
+  constexpr bool SUBP = stages_tokens<MODE, FP8>();
+  __bf16* const tok_k = chunk_tokens;
+  __bf16* const tok_v = chunk_tokens + S * D;
+  int pos0 = 0;
+  bool tok_chunk = false, tok_piece = false;
+  u32x4 tok_kbits = {0u, 0u, 0u, 0u}, tok_vbits = {0u, 0u, 0u, 0u};
+  if constexpr (SUBP) {
+    if (p.append) {
+      pos0 = p.pos[b];
+      tok_chunk = pos0 < k0 + CK && pos0 + S > k0;  // uniform over the workgroup
+      tok_piece = tok_chunk && (int)threadIdx.x < S * (D / 8);
+      if (tok_piece) {
+        const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
+        const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
+        tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+        tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+      }
+    }
+  }
   // Q of the group's rows, once per workgroup, into LDS (rows past p.rows
   // load row 0 and store zeros)
   constexpr int QPIECES = ROWS * D / 8;
@@ -282,6 +316,12 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = ok ? v : bf16x8{};
     }
   }
+  if constexpr (SUBP) {
+    if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
+      *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
+      *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
+    }
+  }
   // softmax role: slot wave*4 + lane/16 takes row `srow` (slots past the
   // rows idle), keys KPL*(lane%16) .. of the chunk; a global row's query
   // position is fetched with the loads
@@ -295,6 +335,15 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // ---------------------------------------------------------- scores
   __syncthreads();  // Q in LDS
+  if constexpr (SUBP) {
+    if (tok_chunk) {  // this lane's K row is token j of the call
+      const int j = k0 + 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3) - pos0;
+      if (j >= 0 && j < S) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(&tok_k[j * D + dh * DH + kdim(c)]);
+      }
+    }
+  }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -367,6 +416,25 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   if (wave >= PVW) return;
 
   // ---------------------------------------------------------- values
+  if constexpr (SUBP) {
+    if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          u32x4 w = __builtin_bit_cast(u32x4, vop[ks][dt]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = k0 + 32 * ks + 8 * lq + e - pos0;
+            if (j >= 0 && j < S) {
+              const uint32_t nv = __builtin_bit_cast(uint16_t, tok_v[j * D + vdim(dt)]);
+              w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (nv << 16)) : ((w[e >> 1] & 0xFFFF0000u) | nv);
+            }
+          }
+          vop[ks][dt] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+  }
   if (!prop && k0 + CK > n_keys) {  // last chunk: zero values of keys past the count
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -463,6 +531,37 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 16;
 constexpr int kMaxChunks = 513;  // 65536 region keys (+ a proposal chunk)
 
+// A bf16 global call that appended its own tokens: token j's head dims
+// 8*d8 .. +7 go into slot pos0 + j of its region (dropped past the region,
+// as by the append call).  Done by the merge pass, once every chunk has
+// read: the token's bits are loaded before the merge's own loads and stored
+// after them, so the stores add no round trip of their own.
+struct CallToken {
+  u32x4 k, v;
+  int j = -1, d8 = 0;
+};
+
+__device__ __forceinline__ CallToken load_call_token(const AttnParams& p, int D, int b, int g, int j, int d8) {
+  CallToken t;
+  const size_t src = ((size_t)(b * p.S + j) * p.Hkv + g) * D + (size_t)d8 * 8;
+  t.k = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+  t.v = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+  t.j = j;
+  t.d8 = d8;
+  return t;
+}
+
+__device__ __forceinline__ void store_call_token(const AttnParams& p, int D, int b, int g, const CallToken& t) {
+  const int cap_r = region_slots(p, b);
+  const int slot = p.pos[b] + t.j;
+  if (t.j < 0 || slot < 0 || slot >= cap_r) return;
+  const int S_r = stored_slots(cap_r);
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+  store_token_piece<false>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, 1.f, 1.f);
+}
+
 struct RunningRow {
   float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
@@ -535,11 +634,15 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   const int d = quarter * PART + (tid - grp * TPG) * 4;
   const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
 
+  CallToken tok;  // the call's tokens, this quarter's dims
+  if (MODE == MODE_GLOBAL && p.append && row == 0 && tid < p.S * (PART / 8))
+    tok = load_call_token(p, D, b, g, tid / (PART / 8), quarter * (PART / 8) + tid % (PART / 8));
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
     merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r);
   }
+  if (MODE == MODE_GLOBAL && p.append) store_call_token(p, D, b, g, tok);
   if (tid - grp * TPG == 0) {
     gml[grp][0] = r.M;
     gml[grp][1] = r.L;
@@ -577,10 +680,15 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
   const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
 
+  // the call's tokens: thread d/8 of row 0 (of each unit) takes head dims
+  // d .. d+7 of every token, one token per loop
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
     merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r);
+  }
+  if (MODE == MODE_GLOBAL && p.append && row == 0 && d % 8 == 0) {
+    for (int j = 0; j < p.S; ++j) store_call_token(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
   }
   store_row4(p, D, b, g, row, d, r.L, r.O);
 }
@@ -595,10 +703,12 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 template <int D, int NCT, int MODE>
 hipError_t launch_chunks(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   const dim3 grid(pl.units * pl.nchunk), block(64 * kChunkWaves);
-  if (pl.fp8)
+  if (pl.fp8) {
     hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((chunk_kernel<D, NCT, false, MODE>), grid, block, 0, s, p);
+  } else {
+    const size_t tok_bytes = (MODE == MODE_GLOBAL && p.append) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
+    hipLaunchKernelGGL((chunk_kernel<D, NCT, false, MODE>), grid, block, tok_bytes, s, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.nchunk > kMergeBatch)

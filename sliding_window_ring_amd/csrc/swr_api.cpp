@@ -125,7 +125,8 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
   p.v_scale_store = kv->v_scale;
   if (mode == swr::MODE_GLOBAL && append) {
     if (pl.chunked) {
-      p.append = 1;  // the proposals' chunk stores them
+      p.append = 1;  // stored by the merge (bf16, global form) or the proposals' chunk (fp8, verify form)
+      if (pl.mode == swr::MODE_GLOBAL) p.qpos_from_pos0 = 1;
     } else {
       // long call: the append kernel first, then the streamed pass with the
       // positions and key counts derived from pos0
@@ -220,10 +221,11 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
     case SWR_OP_GQA_VERIFY: mode = swr::MODE_VERIFY; break;
     case SWR_OP_GLOBAL_ATTEND: mode = swr::MODE_GLOBAL; break;
     case SWR_OP_SWA_APPEND_DECODE: mode = swr::MODE_DECODE_APPEND; S = 1; break;
-    case SWR_OP_GLOBAL_APPEND_ATTEND: {
-      AttnPlan pl;
-      if (!swr::plan_global_append(B, S, Hq, Hkv, D, 0, cap_or_max_keys, &pl)) return 0;
-      return pl.ws_bytes;
+    case SWR_OP_GLOBAL_APPEND_ATTEND: {  // the larger of the bf16 and fp8 plans
+      AttnPlan p16, p8;
+      if (!swr::plan_global_append(B, S, Hq, Hkv, D, 0, cap_or_max_keys, &p16)) return 0;
+      if (!swr::plan_global_append(B, S, Hq, Hkv, D, 1, cap_or_max_keys, &p8)) return 0;
+      return std::max(p16.ws_bytes, p8.ws_bytes);
     }
     default: return 0;
   }
