@@ -138,7 +138,10 @@ def test_fused_global_append_validation():
     need = swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 1, 4, 16, 2, 512, 6005)
     assert need > 0
     assert call() == WORKSPACE
-    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE
+    # the size covers both element types; the fp8 form needs all of it
+    r8 = kv(cap=6016, dtype=1, k_scale=0.01, v_scale=0.01)
+    assert g(ctypes.byref(r8), FAKE, FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, FAKE, need - 1,
+             None) == WORKSPACE
 
 
 def test_append_validation():
