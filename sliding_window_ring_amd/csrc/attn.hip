@@ -734,9 +734,14 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
 // least this many 32-key tiles: the split-K partials are then a small
 // fraction of the bytes read, and there are enough splits to fill the chip.
 constexpr long kStreamTiles = 2048;
-// Tiles per split of a streamed global call: short enough that the splits of
-// unequal requests balance across the compute units.
-constexpr int kStreamSplitTiles = 16;
+// Most tiles per split of a streamed global call: short enough that the
+// splits of unequal requests balance across the compute units, long enough
+// that the splits of a batch of long contexts fit the chip's workgroup slots
+// in about one round.  Measured on the 16-request mixed step (contexts
+// log-uniform in 512 .. 65536, 2 KV heads x 512): 8 / 16 / 24 / 32 / 40 / 48
+// tiles gave 241 / 227 / 231 / 213 / 227 / 248 us (bf16) and 142 / 130 /
+// 151 / 114 / 128 / 144 us (fp8).
+constexpr int kStreamSplitTiles = 32;
 
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
                     AttnPlan* pl) {
