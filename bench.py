@@ -182,6 +182,30 @@ def _timed(torch, fn, reps, sets):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def read_ceiling(swr, torch):
+    """Achievable HBM read rate on this chip: the library's plain streaming
+    read (swr_read_ceiling) over 2 GiB, alternating two buffers so that no
+    launch finds its range in the 256 MB last-level cache; the best of a
+    grid sweep, each grid timed over 10 launches."""
+    nb = 2 << 30
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    best = (0.0, 0, 0)
+    sweep = {}
+    for pattern in (0, 1):
+        for grid in (128, 192, 256, 320, 384, 448, 512, 768, 1024, 2048, 4096, 8192, 16384):
+            us = _timed(torch, lambda i: swr.read_ceiling(bufs[i], sink, grid, pattern), 10, 2)
+            gbs = nb / (us * 1e-6) / 1e9
+            sweep[f"{('sweep', 'span')[pattern]}_{grid}"] = round(gbs, 1)
+            best = max(best, (gbs, grid, pattern))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"GB/s": round(best[0], 1), "bytes_per_launch": nb, "grid": best[1],
+            "pattern": ("grid-wide sweep", "contiguous span per workgroup")[best[2]],
+            "kernel": "read_ceiling_kernel (swr_read_ceiling), 256 threads, 16-byte non-temporal loads",
+            "GB/s_by_pattern_and_grid": sweep}
+
+
 def other_workloads(swr, torch, sweep=True):
     """The remaining workloads, each timed on its own (us per call, GB/s of
     algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the mixed
@@ -519,6 +543,7 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = (b_dec + b_app_s) / (sliding_b2b_us * 1e-6) / 1e9
     traffic = measured_traffic(b_dec + b_app_s)
+    ceiling = read_ceiling(swr, torch)
 
     result = {
         "metric": "attention KV GB/s & % HBM peak; us/layer, sliding decode B=56 + global verify",
@@ -541,6 +566,8 @@ def main():
             "algorithmic_bytes_per_step": step_bytes,
         },
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "hbm_read_ceiling": ceiling,
+        "read_ceiling_frac": round(value / ceiling["GB/s"], 4),
         "us_per_layer": {
             "sliding_decode_b56_append_and_attention": round(sliding_b2b_us, 2),
             "sliding_decode_b56_append_and_attention_events_in_step": round(sliding_us, 2),
@@ -566,6 +593,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": b_dec + b_app_s,
+            "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4),
         },
         "host_wall_s": round(wall, 3),
     }

@@ -275,6 +275,21 @@ swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_fr
  * memset node, so it may be captured into a graph). */
 swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
 
+/* Measurement aid, outside the attention path: one streaming read of `bytes`
+ * (a multiple of 16, at most 2^40) of device memory at `src` (16-byte
+ * aligned) by `grid` workgroups (1 .. 65536) of 256 threads on `stream`.
+ * pattern 0: the grid sweeps the range together (16-byte word i to thread
+ * i mod (grid * 256)); pattern 1: each workgroup streams one contiguous span
+ * of about bytes / grid.  Timing it over a range well beyond the chip's
+ * caches gives the HBM read rate the attention kernels are compared with.
+ * `sink`: caller-owned device memory of at least 1024 bytes that the kernel
+ * may write (its contents mean nothing).  SWR_ERR_INVALID for a null
+ * pointer, a misaligned `src`, a size that is not a multiple of 16 or too
+ * large, a grid out of range or another pattern; SWR_OK with no launch for
+ * bytes == 0. */
+swr_status swr_read_ceiling(const void* src, size_t bytes, void* sink, int grid, int pattern,
+                            hipStream_t stream);
+
 /* Text for a status code (static storage). */
 const char* swr_status_string(swr_status status);
 

@@ -33,7 +33,7 @@ EXPORTS = [
     "swr_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
     "swr_global_append_attend", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
-    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_status_string",
+    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_read_ceiling", "swr_status_string",
 ]
 
 
@@ -77,6 +77,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                ctypes.POINTER(ctypes.c_int32)], I),
         "swr_pool_stats": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I),
         "swr_zero_fill": ([P, SZ, P], I),
+        "swr_read_ceiling": ([P, SZ, P, I, I, P], I),
         "swr_status_string": ([I], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -269,6 +270,19 @@ def zero_fill(t: torch.Tensor, offset: int = 0, nbytes: Optional[int] = None, st
     if offset < 0 or offset + nbytes > total:
         raise ValueError("range outside the tensor")
     _check("swr_zero_fill", lib.swr_zero_fill(ctypes.c_void_p(t.data_ptr() + offset), nbytes, _stream(stream)))
+
+
+def read_ceiling(src: torch.Tensor, sink: torch.Tensor, grid: int, pattern: int = 0, stream=None) -> None:
+    """swr_read_ceiling: one streaming read of the whole device tensor `src`
+    (a measurement aid); sink: a device tensor of at least 1024 bytes."""
+    _dev(src, "src")
+    _dev(sink, "sink")
+    if sink.numel() * sink.element_size() < 1024:
+        raise ValueError("sink needs at least 1024 bytes")
+    _check("swr_read_ceiling", lib.swr_read_ceiling(ctypes.c_void_p(src.data_ptr()),
+                                                    src.numel() * src.element_size(),
+                                                    ctypes.c_void_p(sink.data_ptr()), grid, pattern,
+                                                    _stream(stream)))
 
 
 class Pool:

@@ -157,6 +157,11 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
 
 }  // namespace
 
+namespace swr {
+hipError_t launch_read_ceiling(const void* src, size_t n16, uint32_t* sink, int grid, int pattern,
+                               hipStream_t stream);
+}  // namespace swr
+
 extern "C" {
 
 swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
@@ -244,6 +249,17 @@ swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return SWR_OK;
   if (!ptr) return SWR_ERR_INVALID;
   return to_status(swr::launch_zero_fill(ptr, bytes, stream));
+}
+
+swr_status swr_read_ceiling(const void* src, size_t bytes, void* sink, int grid, int pattern,
+                            hipStream_t stream) {
+  // read_ceiling.hip; a measurement aid, kept out of the attention kernels' shared header
+  if (bytes == 0) return SWR_OK;
+  if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15) || bytes > (size_t(1) << 40) ||
+      grid < 1 || grid > 65536 || (pattern != 0 && pattern != 1))
+    return SWR_ERR_INVALID;
+  return to_status(
+      swr::launch_read_ceiling(src, bytes / 16, static_cast<uint32_t*>(sink), grid, pattern, stream));
 }
 
 const char* swr_status_string(swr_status s) {

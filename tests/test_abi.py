@@ -156,6 +156,18 @@ def test_append_validation():
     assert f(ctypes.byref(r), FAKE, FAKE, FAKE, None, 0, 1, 8, 256, 1, None) == OK
 
 
+def test_read_ceiling_validation():
+    f = swr.lib.swr_read_ceiling
+    assert f(FAKE, 1 << 20, FAKE, 0, 0, None) == INVALID       # grid out of range
+    assert f(FAKE, 1 << 20, FAKE, 65537, 1, None) == INVALID
+    assert f(FAKE, 1 << 20, FAKE, 256, 2, None) == INVALID     # no such pattern
+    assert f(FAKE, (1 << 20) + 8, FAKE, 256, 0, None) == INVALID  # not whole 16-byte words
+    assert f(FAKE + 8, 1 << 20, FAKE, 256, 0, None) == INVALID  # misaligned
+    assert f(None, 1 << 20, FAKE, 256, 0, None) == INVALID
+    assert f(FAKE, 1 << 20, None, 256, 0, None) == INVALID
+    assert f(FAKE, 0, FAKE, 256, 0, None) == OK                 # nothing to read, no launch
+
+
 def test_zero_batch_attention_is_a_no_op():
     assert decode(B=0) == OK
 

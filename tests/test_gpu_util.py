@@ -1,0 +1,34 @@
+"""The library's utility kernels on the GPU: zero fill over ragged ranges (the
+pool zero-fills every region it hands out) and the streaming-read
+measurement kernel.  Neither may touch a byte outside its range."""
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_ring_amd as swr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("offset,nbytes", [(0, 0), (0, 16), (3, 1), (5, 29), (16, 4096), (7, (1 << 20) + 9),
+                                           (0, 1 << 22)])
+def test_zero_fill_exact_range(offset, nbytes):
+    t = torch.full(((1 << 22) + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    swr.zero_fill(t, offset, nbytes)
+    torch.cuda.synchronize()
+    h = t.cpu().numpy()
+    assert np.all(h[offset:offset + nbytes] == 0)
+    assert np.all(h[:offset] == 0xA5) and np.all(h[offset + nbytes:] == 0xA5)
+
+
+@pytest.mark.parametrize("pattern", [0, 1])
+@pytest.mark.parametrize("grid", [1, 7, 256, 65536])
+def test_read_ceiling_reads_and_leaves_memory_alone(grid, pattern):
+    src = torch.arange((1 << 20) + 48, dtype=torch.int32, device="cuda").view(torch.uint8)
+    before = src.clone()
+    guard = torch.full((3 * 1024,), 0x3C, dtype=torch.uint8, device="cuda")
+    swr.read_ceiling(src, guard[1024:2048], grid, pattern)
+    torch.cuda.synchronize()
+    assert torch.equal(src, before)
+    g = guard.cpu().numpy()
+    assert np.all(g[:1024] == 0x3C) and np.all(g[2048:] == 0x3C)
