@@ -58,10 +58,10 @@
  *   is the key order of the gfx950 bf16 matrix instruction's operand in the
  *   kernels; a lane group's operand load (16 rows x 4 granules) is one
  *   contiguous 1 KB block, and a row's four granules are 64 contiguous
- *   bytes, so a token written on its own touches few cache lines.  V is kept in blocks of 8 slots so that
- *   the values of one dim for 8 consecutive slots are contiguous: the
- *   operand shape along the key axis.  A region is S*Hkv*D*e bytes
- *   (swr_kv_region_bytes).
+ *   bytes, so a token written on its own touches few cache lines.  V is
+ *   kept in blocks of 8 slots so that the values of one dim for 8
+ *   consecutive slots are contiguous: the operand shape along the key axis.
+ *   A region is S*Hkv*D*e bytes (swr_kv_region_bytes).
  *   Ring regions: cap = W for every request, slot = position mod W.
  *   Global regions: slot = position; each region holds >= pad64(key_count)
  *   slots, those beyond key_count holding finite values (the pool's zero
@@ -221,9 +221,11 @@ swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const i
  * pos0[b] + S.  Equivalent to swr_kv_append(kv, k_new, v_new, pos0, NULL, B,
  * S, Hkv, D, 0) followed by swr_global_attend: same region bytes, same
  * attention.  When the K/V of all (request, KV head) pairs spans fewer than
- * 2048 tiles of 32 keys the call is one chunked pass plus its merge (the
- * proposals' workgroup stores them while it attends); longer calls run the
- * append and then the streamed pass.
+ * 2048 tiles of 32 keys the call is one chunked pass plus its merge (bf16:
+ * the chunk holding the tokens' slots takes them from k_new/v_new and the
+ * merge stores them once every chunk has read; fp8: the proposals'
+ * workgroup encodes and stores them and attends over the stored codes);
+ * longer calls run the append and then the streamed pass.
  *   k_new, v_new  : device bf16 [B][S][Hkv][D]
  *   q, out        : device bf16 [B][S][Hq][D]
  *   pos0          : device int32 [B], pos0[b] >= 0, pos0[b] + S <= max_key_count and
