@@ -222,6 +222,52 @@ def test_global_sweep_subset():
     assert w.key_count == 6005
 
 
+def sweep_counts():
+    """The checked counts of the 4000..8192 key-count sweep: every count in
+    6000..6080, each multiple of 64 in range with its neighbours, the
+    endpoints, and 64 seeded random counts."""
+    mult = [m + d for m in range(4032, 8193, 64) for d in (-1, 0, 1)]
+    rnd = synthetic.rng(35).integers(4000, 8193, 64)
+    return sorted({c for c in list(range(6000, 6081)) + mult + [4000, 8192] + [int(r) for r in rnd]
+                   if 4000 <= c <= 8192})
+
+
+SWEEP_GROUPS = 6
+
+
+@pytest.mark.parametrize("group", range(SWEEP_GROUPS))
+def test_global_sweep_each_count_as_launched(group):
+    """Each checked count of the sweep as its own B=1 call, launched as the
+    benchmark times it (max_key_count = the count), over one region of 8192
+    keys whose keys past the count are other (finite, masked) tokens."""
+    counts = sweep_counts()[group::SWEEP_GROUPS]
+    hist = synthetic.global_verify(synthetic.Workload("t", B=1, Hkv=2, G=8, D=512, S=4, key_count=8192), seed=36)
+    kp, vp, ko, vo = global_pools(hist["k"], hist["v"], np.array([8192], np.int32), 8192)
+    L = layer(kp, vp, ko, vo, 8192)
+    q = synthetic.normal_bf16(synthetic.rng(37 + group), (1, 4, 16, 512))
+    qd = dev_bf16(q)
+    scale = 512 ** -0.5
+    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, 4, 16, 2, 512, 8192), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for kc in counts:
+        qp = np.arange(kc - 4, kc, dtype=np.int32)[None, :]
+        outs.append(swr.global_attend(L, qd, dev_i32(qp), dev_i32([kc]), kc, 2, scale, ws=ws).clone())
+    torch.cuda.synchronize()
+    for kc, out in zip(counts, outs):
+        qp = np.arange(kc - 4, kc, dtype=np.int32)[None, :]
+        ref = oracle.global_attend(kp, vp, ko, vo, 8192, oracle.BF16, 1.0, 1.0, q, qp, np.array([kc], np.int32), 2,
+                                   scale)
+        assert_parity(host_f64(out), ref, f"key_count {kc}")
+
+
+def test_sweep_counts_cover_the_stated_set():
+    c = sweep_counts()
+    assert set(range(6000, 6081)) <= set(c)
+    assert {4000, 8192, 4095, 4096, 4097, 8191} <= set(c)
+    assert len(c) >= 81 + 3 * 65
+
+
 @pytest.mark.parametrize("S,G,D", [(1, 8, 512), (2, 8, 512), (4, 2, 64), (3, 4, 256), (1, 16, 128)])
 def test_global_shapes(S, G, D):
     kc = np.array([1, 63, 64, 65, 700, 2000], np.int32)
