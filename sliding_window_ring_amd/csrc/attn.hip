@@ -43,6 +43,13 @@
 
 namespace swr {
 
+// An empty instruction that reads v: what computes v is placed before it
+// (and v's own load, if any, waited for), and with the memory clobber no load
+// or store moves across it.
+__device__ __forceinline__ void pin(u32x4 v) { asm volatile("" ::"v"(v) : "memory"); }
+// The same as a read-write of v: what uses v afterwards stays after it.
+__device__ __forceinline__ void hold(u32x4& v) { asm volatile("" : "+v"(v)::"memory"); }
+
 // Slots of request b's region (global regions may carry a capacity each).
 __device__ __forceinline__ int region_cap(const AttnParams& p, int b) {
   return p.cap_b ? max(min(p.cap_b[b], p.cap), 0) : p.cap;
@@ -142,11 +149,24 @@ attn_kernel(const AttnParams p) {
   // K and V operand registers.  The loads for tile t+KW are issued as soon as
   // tile t has consumed the registers (K after the score product, V after the
   // value product), so every wave keeps a tile's worth of loads in flight
-  // while it computes.
+  // while it computes.  fp8 outside verify (RAW): the loads land as codes
+  // (kraw, vraw) and are converted to bf16 operands only where the tile is
+  // used, since a conversion next to its load makes the wave wait for the
+  // tile there and then; the next tile's loads then go out as soon as this
+  // tile's codes are converted.  (fp8 verify converts at the load: the raw
+  // registers would cost its larger row tiles occupancy.)
+  constexpr bool RAW = FP8 && MODE != MODE_VERIFY;
   bf16x8 kop[2][NCH];
   bf16x8 vop[NDT];
+  u32x4 kraw[2][RAW ? NCH / 2 : 1];
+  u32x4 vraw[RAW ? NDT / 2 : 1];
 
-  auto load_k = [&](int t) {
+  // RAW: a wave with no next tile still issues its next-tile loads, through
+  // a resource of zero bytes (they return zeros and read nothing), so that
+  // the loop has no branch around its loads and every wait can count exactly
+  // the loads ahead of the ones it needs.
+  const __amdgpu_buffer_rsrc_t rnull = make_rsrc(p.k_base, 0);
+  auto load_k = [&](int t, bool live = true) {
     const int kb = t * 32;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
 #pragma unroll
@@ -159,7 +179,11 @@ attn_kernel(const AttnParams p) {
       if (!prop_tile) {
         constexpr int R = FP8 ? 16 : 8;  // dims per 16-byte granule
         const uint32_t hb = k_half_base(g, S_r, kb, sub, D, ESZ);
-        if (FP8) {
+        if (RAW) {
+#pragma unroll
+          for (int c = 0; c < NCH; c += 2)
+            kraw[sub][c / 2] = load16_stream(live ? rk : rnull, hb + k_granule_offset((d_base + kdim(c)) / R, lr));
+        } else if (FP8) {
 #pragma unroll
           for (int c = 0; c < NCH; c += 2) {
             const u32x4 w = load16_stream(rk, hb + k_granule_offset((d_base + kdim(c)) / R, lr));
@@ -206,12 +230,16 @@ attn_kernel(const AttnParams p) {
     return v;
   };
 
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t, bool live = true) {
     const int kb = t * 32;
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     if (!prop_tile) {
       const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + (kb >> 3) + lq) * D;
-      if (FP8) {
+      if (RAW) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt += 2)
+          vraw[dt / 2] = load16_stream(live ? rv : rnull, (vblock + (uint32_t)vdim(dt)) * 8);
+      } else if (FP8) {
 #pragma unroll
         for (int dt = 0; dt < NDT; dt += 2) {
           const u32x4 w = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
@@ -225,6 +253,32 @@ attn_kernel(const AttnParams p) {
     } else {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) vop[dt] = prop_v(dt, false);
+    }
+  };
+
+  // RAW: the codes of a tile as bf16 operands
+  auto cvt_k = [&]() {
+    if constexpr (RAW) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int c = 0; c < NCH; c += 2) {
+          kop[sub][c] = fp8x8_to_bf16x8(u32x2{kraw[sub][c / 2][0], kraw[sub][c / 2][1]});
+          kop[sub][c + 1] = fp8x8_to_bf16x8(u32x2{kraw[sub][c / 2][2], kraw[sub][c / 2][3]});
+        }
+    }
+  };
+  auto cvt_v = [&]() {
+    if constexpr (RAW) {
+      // held behind the next tile's K loads: converted ahead of them, the
+      // codes would have to arrive before those loads could go out
+#pragma unroll
+      for (int j = 0; j < NDT / 2; ++j) hold(vraw[j]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt += 2) {
+        vop[dt] = fp8x8_to_bf16x8(u32x2{vraw[dt / 2][0], vraw[dt / 2][1]});
+        vop[dt + 1] = fp8x8_to_bf16x8(u32x2{vraw[dt / 2][2], vraw[dt / 2][3]});
+      }
     }
   };
 
@@ -294,6 +348,16 @@ attn_kernel(const AttnParams p) {
     }
   }
 
+  if (RAW) {
+    // Q's loads, issued before the first tile's, are waited for here, behind
+    // them: left pending into the loop they would make the loop's first
+    // product wait for every load in flight
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) pin(__builtin_bit_cast(u32x4, qop[ct][c]));
+  }
+
   for (int it = 0; it < n_it; ++it) {
     const int lam = kw + it * KW;
     if (lam >= nt) {  // wave-uniform; keeps the barrier count equal across waves
@@ -306,6 +370,14 @@ attn_kernel(const AttnParams p) {
     const bool prop_tile = (MODE == MODE_VERIFY) && (t == nt_region);
     const int kb = t * 32;
     const bool subst = SUBST && writer && t == t_new;  // wave-uniform
+    // RAW: the next tile's loads go out as soon as this tile's codes are
+    // converted; the other forms load straight into the operand registers,
+    // after this tile's product has read them
+    const int t_load = has_next ? t_next : t;
+    auto next_k = [&]() {
+      if (FIRST && writer && has_next && t_next == t_new) wait_vm_all();
+      load_k(t_load, has_next);
+    };
 
     if (subst) {
       // K: row r_new of half h_new is the new token; the lanes of the two
@@ -342,6 +414,14 @@ attn_kernel(const AttnParams p) {
     }
 
     // ------------------------------------------------ scores = K . Q^T
+    if (RAW) cvt_k();
+    if (RAW) {  // the conversions first, so that the loads reuse their registers
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) pin(__builtin_bit_cast(u32x4, kop[sub][c]));
+      next_k();
+    }
     f32x4 sc[2][NCT];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -352,10 +432,7 @@ attn_kernel(const AttnParams p) {
         for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
         sc[sub][ct] = acc;
       }
-    if (has_next) {
-      if (FIRST && writer && t_next == t_new) wait_vm_all();
-      load_k(t_next);
-    }
+    if (!RAW && has_next) next_k();
 
     if (DSPLIT > 1) {  // add the head-dim slices of the scores, in slice order
       float* buf = smem + (size_t)((it & 1) * KW + kw) * DSPLIT * RED * 64;
@@ -431,6 +508,12 @@ attn_kernel(const AttnParams p) {
     }
 
     // ------------------------------------------------ O^T += V^T . P^T
+    if (RAW) cvt_v();
+    if (RAW) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) pin(__builtin_bit_cast(u32x4, vop[dt]));
+      load_v(t_load, has_next);
+    }
     if (!prop_tile && kb + 32 > n_keys) {  // last region tile: zero values of keys past the valid range
       u32x4 keep;
 #pragma unroll
@@ -454,7 +537,7 @@ attn_kernel(const AttnParams p) {
         for (int ct = 0; ct < NCT; ++ct) o[ct][dt] = mfma16x16x32(vlo, pop[ct], o[ct][dt]);
       }
     }
-    if (has_next) load_v(t_next);
+    if (!RAW && has_next) load_v(t_next);
   }
 
 #pragma unroll
