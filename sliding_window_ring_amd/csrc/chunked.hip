@@ -185,9 +185,15 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   };
 
   // ---------------------------------------------------------- loads
+  // fp8 region codes land in kraw / vraw and become bf16 operands only where
+  // the product needs them: a conversion next to its load would make the
+  // wave wait for each load in turn (the compiler places it right there),
+  // where the bf16 operands let all of them fly at once.
   const int kq = wave % KQ, dh = wave / KQ;
   bf16x8 kop[NCH];
   bf16x8 vop[KS][NDT];
+  u32x4 kraw[FP8 ? NCH : 1];     // paired: entries 0 .. NCH/2-1; else the low halves
+  u32x4 vraw[KS][FP8 ? NDT : 1];
   auto load_v = [&]() {
     if (wave >= PVW) return;
 #pragma unroll
@@ -195,17 +201,50 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + ((k0 + 32 * ks) >> 3) + lq) * D;
       if (VPAIR) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt += 2) {
-          const u32x4 w = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
-          vop[ks][dt] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-          vop[ks][dt + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
-        }
+        for (int dt = 0; dt < NDT; dt += 2) vraw[ks][dt / 2] = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
       } else {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const uint32_t off = (vblock + (uint32_t)vdim(dt)) * 8 * ESZ;
-          vop[ks][dt] = FP8 ? fp8x8_to_bf16x8(load8(rv, off)) : as_bf16x8(load16_stream(rv, off));
+          if (FP8) {
+            const u32x2 w = load8(rv, off);
+            vraw[ks][dt] = u32x4{w[0], w[1], 0u, 0u};
+          } else {
+            vop[ks][dt] = as_bf16x8(load16_stream(rv, off));
+          }
         }
+      }
+    }
+  };
+  auto cvt_v = [&]() {
+    if constexpr (FP8) {
+      if (wave >= PVW) return;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (VPAIR) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; dt += 2) {
+            vop[ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt / 2][0], vraw[ks][dt / 2][1]});
+            vop[ks][dt + 1] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt / 2][2], vraw[ks][dt / 2][3]});
+          }
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vop[ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt][0], vraw[ks][dt][1]});
+        }
+      }
+    }
+  };
+  auto cvt_k = [&]() {
+    if constexpr (FP8) {
+      if (KPAIR) {
+#pragma unroll
+        for (int c = 0; c < NCH; c += 2) {
+          kop[c] = fp8x8_to_bf16x8(u32x2{kraw[c / 2][0], kraw[c / 2][1]});
+          kop[c + 1] = fp8x8_to_bf16x8(u32x2{kraw[c / 2][2], kraw[c / 2][3]});
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) kop[c] = fp8x8_to_bf16x8(u32x2{kraw[c][0], kraw[c][1]});
       }
     }
   };
@@ -215,17 +254,19 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     const uint32_t hb = k_half_base(g, S_r, k0 + 32 * (kq >> 1), kq & 1, D, ESZ);
     if (KPAIR) {
 #pragma unroll
-      for (int c = 0; c < NCH; c += 2) {
-        const u32x4 w = load16_stream(rk, hb + k_granule_offset((dh * DH + kdim(c)) / R, lr));
-        kop[c] = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-        kop[c + 1] = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
-      }
+      for (int c = 0; c < NCH; c += 2)
+        kraw[c / 2] = load16_stream(rk, hb + k_granule_offset((dh * DH + kdim(c)) / R, lr));
     } else {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int dim = dh * DH + kdim(c);
         const uint32_t off = hb + k_granule_offset(dim / R, lr) + (uint32_t)((dim % R) * ESZ);
-        kop[c] = FP8 ? fp8x8_to_bf16x8(load8(rk, off)) : as_bf16x8(load16_stream(rk, off));
+        if (FP8) {
+          const u32x2 w = load8(rk, off);
+          kraw[c] = u32x4{w[0], w[1], 0u, 0u};
+        } else {
+          kop[c] = as_bf16x8(load16_stream(rk, off));
+        }
       }
     }
   } else {
@@ -335,6 +376,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // ---------------------------------------------------------- scores
   __syncthreads();  // Q in LDS
+  if (!prop) cvt_k();
   if constexpr (SUBP) {
     if (tok_chunk) {  // this lane's K row is token j of the call
       const int j = k0 + 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3) - pos0;
@@ -416,6 +458,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   if (wave >= PVW) return;
 
   // ---------------------------------------------------------- values
+  if (!prop) cvt_v();
   if constexpr (SUBP) {
     if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
 #pragma unroll
