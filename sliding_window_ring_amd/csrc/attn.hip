@@ -897,14 +897,10 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
 bool plan_global_append(int B, int S, int Hq, int Hkv, int D, int fp8, int max_keys, AttnPlan* pl) {
   if (B < 0 || S < 1 || Hkv < 1 || max_keys < S) return false;
   if ((long)B * Hkv * ceil_div(max_keys, 32) < kStreamTiles) {
-    // bf16: the global chunked form, tokens taken from their buffers and
-    // stored by the merge; fp8 (operands must be the stored codes): the
-    // chunked verify form, whose proposal chunk encodes and stores them
-    if (fp8) {
-      if (!plan_chunked(MODE_VERIFY, B, S, Hq, Hkv, D, std::max(max_keys - S, 1), pl)) return false;
-    } else {
-      if (S > 8 || !plan_chunked(MODE_GLOBAL, B, S, Hq, Hkv, D, max_keys, pl)) return false;
-    }
+    // the global chunked form: the chunk holding the tokens' slots takes them
+    // from their buffers (over fp8, as the values of the codes to be stored)
+    // and the merge stores them
+    if (!plan_chunked(MODE_GLOBAL, B, S, Hq, Hkv, D, max_keys, pl)) return false;
     pl->fp8 = fp8 ? 1 : 0;
     return true;
   }

@@ -113,12 +113,9 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 // are bf16 values: their scores take scale * log2(e) without k_scale, and
 // their accumulated values are divided by v_scale (in fp32) before the
 // store, since pass 2 multiplies every chunk by v_scale.
-// Fused append (global regions, which never wrap, so every committed key
-// stays visible to every row): the proposal chunk also stores the proposals
-// into slots pos0 .. pos0+S-1, and over an fp8 region it takes their stored
-// codes as operands, exactly as a later call would read them.  The region
-// chunks read only slots below pos0; a store can only meet a read of a slot
-// the chunk masks (its K scores are replaced and its V lanes zeroed).
+// Fused append (a global call storing its own S tokens at pos0 .. pos0+S-1):
+// the chunk holding their slots takes them in place of the slots' old
+// contents, and the merge pass stores them (below).
 template <int D, int NCT>
 struct ChunkSmem {
   float sbuf[2][16 * NCT][kChunkKeys + 4];
@@ -127,11 +124,12 @@ struct ChunkSmem {
 };
 
 // The call's own tokens, staged by the global chunk that holds their slots
-// when a bf16 global call appends them itself: dynamic LDS of [2][S][D]
-// bf16 (K, then V), sized at launch -- none for the other calls.
+// when a global call appends them itself: dynamic LDS of [2][S][D] bf16 (K,
+// then V; over an fp8 region the values its stored codes decode to, in units
+// of the scale), sized at launch -- none for the other calls.
 extern __shared__ __attribute__((aligned(16))) __bf16 chunk_tokens[];
-template <int MODE, bool FP8>
-constexpr bool stages_tokens() { return MODE == MODE_GLOBAL && !FP8; }
+template <int MODE>
+constexpr bool stages_tokens() { return MODE == MODE_GLOBAL; }
 
 // One chunk of one (request, KV head); every wave of the workgroup calls it
 // with the same arguments.  Returns early (all waves alike) for a chunk past
@@ -270,17 +268,6 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
     }
   } else {
-    if (p.append) {  // the proposals into their slots, 8 head dims per thread
-      const int per = D / 8;
-      for (int idx = threadIdx.x; idx < S * per; idx += 64 * NW) {
-        const int j = idx / per, d8 = idx - (idx / per) * per;
-        const int slot = p.pos[b] + j;
-        if (slot < 0 || slot >= cap_r) continue;  // outside the region: dropped, as by the append call
-        const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
-        store_token_piece<FP8>(rk, rv, slot, g, S_r, D, d8, *reinterpret_cast<const u32x4*>(p.k_prop + src),
-                               *reinterpret_cast<const u32x4*>(p.v_prop + src), p.k_scale_store, p.v_scale_store);
-      }
-    }
     // proposals j = 0..S-1 are keys 0..S-1 of the chunk: row r of the
     // wave's subtile is key 32*(kq/2) + 8*(r/4) + 4*(kq%2) + r%4 (so j < 8
     // lands in subtiles 0 and 1), and value k step 0, lane group 0; every
@@ -291,10 +278,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (pj < S) {
       const uint16_t* src = p.k_prop + ((size_t)(b * S + pj) * Hkv + g) * D + dh * DH;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
-        if (FP8 && p.append) kop[c] = fp8_stored_values(kop[c], p.k_scale_store);
-      }
+      for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -309,13 +293,12 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           uint16_t bits = 0;
           if (j < S) bits = p.v_prop[((size_t)(b * S + j) * Hkv + g) * D + vdim(dt)];
           v[j] = __builtin_bit_cast(__bf16, bits);
-          if (FP8 && p.append) v[j] = fp8_stored_value(v[j], p.v_scale_store);
         }
         vop[0][dt] = v;
       }
     }
   }
-  // bf16 global call that appends its own S tokens (keys pos0 .. pos0+S-1):
+  // global call that appends its own S tokens (keys pos0 .. pos0+S-1):
   // the chunk holding any of their slots stages them in LDS (one 16-byte
   // piece of K and of V per thread: S*D/8 <= 512 pieces), loaded here behind
   // the region's loads and written to LDS after the Q loads have gone out
@@ -323,7 +306,9 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // Q loads back until the region's data arrived); the Q barrier covers the
   // writes.  The operands take them in place of the slots' old contents, and
   // the regions receive them from the merge pass, after every chunk has read.
-  constexpr bool SUBP = stages_tokens<MODE, FP8>();
+  // Over an fp8 region the staged values are those of the codes the merge
+  // will store, exactly as a later call reads them.
+  constexpr bool SUBP = stages_tokens<MODE>();
   __bf16* const tok_k = chunk_tokens;
   __bf16* const tok_v = chunk_tokens + S * D;
   int pos0 = 0;
@@ -359,6 +344,10 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   }
   if constexpr (SUBP) {
     if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
+      if (FP8) {
+        tok_kbits = __builtin_bit_cast(u32x4, fp8_stored_values(__builtin_bit_cast(bf16x8, tok_kbits), p.k_scale_store));
+        tok_vbits = __builtin_bit_cast(u32x4, fp8_stored_values(__builtin_bit_cast(bf16x8, tok_vbits), p.v_scale_store));
+      }
       *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
       *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
     }
@@ -403,7 +392,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // ---------------------------------------------------------- softmax
   const size_t slot = ((size_t)unit * p.nchunk + chunk) * p.rows;
-  const bool bf16_prop = FP8 && prop && !p.append;  // proposals as bf16 values, not codes
+  const bool bf16_prop = FP8 && prop;  // proposals as bf16 values, not codes
   const float qs = bf16_prop ? p.qk_scale_prop : p.qk_scale;
   if (srow < ROWS) {
     const int kk = KPL * lr;
@@ -574,11 +563,12 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 16;
 constexpr int kMaxChunks = 513;  // 65536 region keys (+ a proposal chunk)
 
-// A bf16 global call that appended its own tokens: token j's head dims
-// 8*d8 .. +7 go into slot pos0 + j of its region (dropped past the region,
-// as by the append call).  Done by the merge pass, once every chunk has
-// read: the token's bits are loaded before the merge's own loads and stored
-// after them, so the stores add no round trip of their own.
+// A global call that appended its own tokens: token j's head dims 8*d8 ..
+// +7 go into slot pos0 + j of its region (dropped past the region, as by the
+// append call; over an fp8 region as their E4M3 codes).  Done by the merge
+// pass, once every chunk has read: the token's bits are loaded before the
+// merge's own loads and stored after them, so the stores add no round trip
+// of their own.
 struct CallToken {
   u32x4 k, v;
   int j = -1, d8 = 0;
@@ -594,15 +584,16 @@ __device__ __forceinline__ CallToken load_call_token(const AttnParams& p, int D,
   return t;
 }
 
+template <bool FP8>
 __device__ __forceinline__ void store_call_token(const AttnParams& p, int D, int b, int g, const CallToken& t) {
   const int cap_r = region_slots(p, b);
   const int slot = p.pos[b] + t.j;
   if (t.j < 0 || slot < 0 || slot >= cap_r) return;
   const int S_r = stored_slots(cap_r);
-  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * 2);
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * (FP8 ? 1 : 2));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
-  store_token_piece<false>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, 1.f, 1.f);
+  store_token_piece<FP8>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, p.k_scale_store, p.v_scale_store);
 }
 
 struct RunningRow {
@@ -659,7 +650,8 @@ __device__ __forceinline__ void store_row4(const AttnParams& p, int D, int b, in
 // Many chunks per row: one workgroup per (request, KV head, row, quarter of
 // the head dims); thread group k of NG takes chunks k, k+NG, ... for its
 // four dims, and the groups are merged in group order through LDS.
-template <int D, int MODE>
+// FP8: the call's tokens (if it appended them) go into fp8 regions.
+template <int D, int MODE, bool FP8 = false>
 __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams p) {
   constexpr int PART = D / 4;                  // dims per workgroup
   constexpr int TPG = PART / 4;                // threads per group (4 dims each)
@@ -685,7 +677,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
     merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r);
   }
-  if (MODE == MODE_GLOBAL && p.append) store_call_token(p, D, b, g, tok);
+  if (MODE == MODE_GLOBAL && p.append) store_call_token<FP8>(p, D, b, g, tok);
   if (tid - grp * TPG == 0) {
     gml[grp][0] = r.M;
     gml[grp][1] = r.L;
@@ -710,7 +702,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
 
 // Few chunks per row: one thread per (request, KV head, row, four dims)
 // takes every chunk in order.
-template <int MODE>
+template <int MODE, bool FP8 = false>
 __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, int D) {
   const int per_row = D / 4;
   const int per_unit = p.rows * per_row;
@@ -731,7 +723,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
     merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r);
   }
   if (MODE == MODE_GLOBAL && p.append && row == 0 && d % 8 == 0) {
-    for (int j = 0; j < p.S; ++j) store_call_token(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
+    for (int j = 0; j < p.S; ++j) store_call_token<FP8>(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
   }
   store_row4(p, D, b, g, row, d, r.L, r.O);
 }
@@ -746,19 +738,26 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 template <int D, int NCT, int MODE>
 hipError_t launch_chunks(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   const dim3 grid(pl.units * pl.nchunk), block(64 * kChunkWaves);
-  if (pl.fp8) {
-    hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, 0, s, p);
-  } else {
-    const size_t tok_bytes = (MODE == MODE_GLOBAL && p.append) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
+  const size_t tok_bytes = (MODE == MODE_GLOBAL && p.append) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
+  if (pl.fp8)
+    hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, tok_bytes, s, p);
+  else
     hipLaunchKernelGGL((chunk_kernel<D, NCT, false, MODE>), grid, block, tok_bytes, s, p);
-  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (pl.nchunk > kMergeBatch)
-    hipLaunchKernelGGL((merge_grouped<D, MODE>), dim3(pl.units * pl.rows * 4), dim3(kMergeThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((merge_flat<MODE>), dim3(cdiv((long)pl.units * pl.rows * (D / 4), kMergeThreads)),
-                       dim3(kMergeThreads), 0, s, p, D);
+  const bool fp8_tokens = MODE == MODE_GLOBAL && p.append && pl.fp8;  // the merge stores codes
+  const dim3 mgrid(pl.units * pl.rows * 4), fgrid(cdiv((long)pl.units * pl.rows * (D / 4), kMergeThreads));
+  if (pl.nchunk > kMergeBatch) {
+    if (fp8_tokens)
+      hipLaunchKernelGGL((merge_grouped<D, MODE, true>), mgrid, dim3(kMergeThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((merge_grouped<D, MODE>), mgrid, dim3(kMergeThreads), 0, s, p);
+  } else {
+    if (fp8_tokens)
+      hipLaunchKernelGGL((merge_flat<MODE, true>), fgrid, dim3(kMergeThreads), 0, s, p, D);
+    else
+      hipLaunchKernelGGL((merge_flat<MODE>), fgrid, dim3(kMergeThreads), 0, s, p, D);
+  }
   return hipGetLastError();
 }
 

@@ -125,8 +125,8 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
   p.v_scale_store = kv->v_scale;
   if (mode == swr::MODE_GLOBAL && append) {
     if (pl.chunked) {
-      p.append = 1;  // stored by the merge (bf16, global form) or the proposals' chunk (fp8, verify form)
-      if (pl.mode == swr::MODE_GLOBAL) p.qpos_from_pos0 = 1;
+      p.append = 1;  // taken by the chunk holding the slots, stored by the merge
+      p.qpos_from_pos0 = 1;
     } else {
       // long call: the append kernel first, then the streamed pass with the
       // positions and key counts derived from pos0

@@ -38,7 +38,7 @@ struct AttnParams {
   const int32_t* key_count;  // global: [B]
   const uint16_t* k_prop;  // verify: proposals; fused append: the tokens to store.  bf16 [B][S][Hkv][D]
   const uint16_t* v_prop;
-  int append;              // chunked global call storing its own S tokens at pos0 + j (bf16: the merge; fp8: verify form)
+  int append;              // chunked global call storing its own S tokens at pos0 + j (by the merge)
   int qpos_from_pos0;      // streamed global: pos is pos0[B]; q_pos[b][i] = pos0[b] + i, key_count = pos0[b] + S
   float k_scale_store;     // fp8 regions: the scales a stored token's K and V are divided by
   float v_scale_store;
@@ -98,10 +98,9 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
 hipError_t launch_attention(const AttnPlan& plan, const AttnParams& p, hipStream_t stream);
 
 // Plan of a global call that appends its S tokens itself (max_keys bounds
-// pos0 + S): in chunked form (bf16: the global form, tokens read from their
-// buffers, stored by the merge; fp8: the verify form, whose proposal chunk
-// stores them), or for long calls the streamed global pass (run after the
-// append kernel), positions derived from pos0.
+// pos0 + S): in chunked form (tokens read from their buffers by the chunk
+// holding their slots, stored by the merge), or for long calls the streamed
+// global pass (run after the append kernel), positions derived from pos0.
 bool plan_global_append(int B, int S, int Hq, int Hkv, int D, int fp8, int max_keys, AttnPlan* plan);
 
 struct AppendParams {
