@@ -221,11 +221,11 @@ swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const i
  * pos0[b] + S.  Equivalent to swr_kv_append(kv, k_new, v_new, pos0, NULL, B,
  * S, Hkv, D, 0) followed by swr_global_attend: same region bytes, same
  * attention.  When the K/V of all (request, KV head) pairs spans fewer than
- * 2048 tiles of 32 keys the call is one chunked pass plus its merge (bf16:
- * the chunk holding the tokens' slots takes them from k_new/v_new and the
- * merge stores them once every chunk has read; fp8: the proposals'
- * workgroup encodes and stores them and attends over the stored codes);
- * longer calls run the append and then the streamed pass.
+ * 2048 tiles of 32 keys the call is one chunked pass plus its merge: the
+ * chunk holding the tokens' slots takes them from k_new/v_new (over fp8, as
+ * the values of the codes that will be stored) and the merge stores them
+ * once every chunk has read; longer calls run the append and then the
+ * streamed pass.
  *   k_new, v_new  : device bf16 [B][S][Hkv][D]
  *   q, out        : device bf16 [B][S][Hq][D]
  *   pos0          : device int32 [B], pos0[b] >= 0, pos0[b] + S <= max_key_count and
