@@ -206,6 +206,87 @@ def read_ceiling(swr, torch):
             "GB/s_by_pattern_and_grid": sweep}
 
 
+def decode_stack(swr, torch, randn, dev):
+    """One decode step's attention through a Gemma-4-31B-shaped stack: 50
+    sliding layers and 10 global layers ("Improving Decode Throughput on
+    Intel Gaudi 3", Patching sliding window KV allocation), five sliding to
+    one global, at B=56 with contexts U[1024, 4096].  Every layer appends its
+    token and attends (swr_swa_append_decode, swr_global_append_attend with
+    S=1) over rings and regions of its own, 30 GB in all, so nothing is read
+    from the caches; the 60 calls are one HIP graph, timed over 5 replays."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1006)
+    pos = torch.randint(1024, 4097, (B,), device=dev, dtype=torch.int32, generator=gen)
+    ctx = [int(c) for c in pos.tolist()]
+    caps = [(c + 1 + 63) // 64 * 64 for c in ctx]
+    # one random source for every layer's history (the layers differ in where they live)
+    hk, hv = randn(B, W, HKV, D), randn(B, W, HKV, D)
+    gkh, gvh = randn(B, max(ctx) + 1, GHKV, GD), randn(B, max(ctx) + 1, GHKV, GD)
+    rb = swr.region_bytes(W, HKV, D)
+    roff = torch.arange(B, device=dev, dtype=torch.int64) * rb
+    grb = [swr.region_bytes(c, GHKV, GD) for c in caps]
+    starts, at = [], 0
+    for n in grb:
+        starts.append(at)
+        at += n
+    goff = torch.tensor(starts, device=dev, dtype=torch.int64)
+    capb = torch.tensor(caps, device=dev, dtype=torch.int32)
+    sliding, glob = [], []
+    for _ in range(50):
+        k = torch.empty(B * rb, dtype=torch.uint8, device=dev)
+        v = torch.empty_like(k)
+        L = swr.KVLayer(k, v, roff, roff, W)
+        swr.kv_append(L, hk, hv, (pos - W).to(torch.int32))
+        sliding.append(L)
+    for _ in range(10):
+        k = torch.zeros(sum(grb), dtype=torch.uint8, device=dev)
+        v = torch.zeros_like(k)
+        L = swr.KVLayer(k, v, goff, goff, max(caps), cap_b=capb)
+        swr.kv_append(L, gkh, gvh, torch.zeros(B, device=dev, dtype=torch.int32), n_new=pos, wrap=False)
+        glob.append(L)
+    q_s, q_g = randn(B, HKV * G, D), randn(B, 1, GHKV * GG, GD)
+    kn_s, vn_s = randn(B, HKV, D), randn(B, HKV, D)
+    kn_g, vn_g = randn(B, 1, GHKV, GD), randn(B, 1, GHKV, GD)
+    out_s, out_g = torch.empty_like(q_s), torch.empty_like(q_g)
+    dws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W)),
+                      dtype=torch.uint8, device=dev)
+    gws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, GHKV * GG, GHKV, GD,
+                                                  max(ctx) + 1)), dtype=torch.uint8, device=dev)
+
+    def step():
+        for i in range(10):
+            for j in range(5):
+                swr.swa_append_decode(sliding[5 * i + j], kn_s, vn_s, q_s, pos, D ** -0.5, out=out_s, ws=dws)
+            swr.global_append_attend(glob[i], kn_g, vn_g, q_g, pos, max(ctx) + 1, GD ** -0.5, out=out_g, ws=gws)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    n_win = sum(min(c + 1, W) for c in ctx)
+    sliding_bytes = n_win * HKV * D * 2 * 2 + 2 * B * HKV * G * D * 2 + B * HKV * D * 2 * 2 * 2
+    global_bytes = sum(c + 1 for c in ctx) * GHKV * GD * 2 * 2 + 2 * B * GHKV * GG * GD * 2 + \
+        B * GHKV * GD * 2 * 2 * 2
+    nbytes = 50 * sliding_bytes + 10 * global_bytes
+    del sliding, glob, hk, hv, gkh, gvh
+    torch.cuda.empty_cache()
+    return {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
+            "layers": "50 sliding (W=1024, 8 KV heads x 256) + 10 global (2 KV heads x 512), five sliding to one global",
+            "batch": B, "contexts": "U[1024, 4096], seed 1006",
+            "note": "one HIP graph of the 60 fused append + attention calls; every layer on K/V of its own"}
+
+
 def other_workloads(swr, torch, sweep=True):
     """The remaining workloads, each timed on its own (us per call, GB/s of
     algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the mixed
@@ -368,6 +449,8 @@ def other_workloads(swr, torch, sweep=True):
                                                "algorithmic_bytes": nbytes}
         del pool, sl, gl, dws, gws, fws
         torch.cuda.synchronize()
+
+    res["decode_step_b56_gemma4_31b_attention_stack"] = decode_stack(swr, torch, randn, dev)
 
     if not sweep:
         return res

@@ -873,7 +873,12 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   // Split-K across workgroups only when the units alone do not fill the chip.
   int tps = pl->max_tiles;
   if (mode == MODE_GSTREAM) {
-    tps = std::min(std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU)),
+    // about four splits per CU if every unit had max_tiles; real requests are
+    // shorter (their splits past the key count exit at once), so aiming at
+    // two left the non-empty splits too few to spread evenly: B=56 decode
+    // contexts U[1024, 4096] took 123 us per global layer against 108 us,
+    // the 16-request mixed step 222 us either way; eight made both slower
+    tps = std::min(std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 4 * kNumCU)),
                    kStreamSplitTiles);
     tps = std::min(tps, pl->max_tiles);
   } else if (pl->units > 0 && pl->units < kNumCU) {
