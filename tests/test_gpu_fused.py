@@ -193,17 +193,21 @@ def test_fused_global_verify_6005_keys(dtype):
     print("fused global verify max-abs %.3e rel-L2 %.3e" % e)
 
 
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("S,G,D", [(4, 8, 512), (1, 8, 512), (2, 4, 64), (3, 4, 256), (1, 16, 128), (8, 4, 128)])
-def test_fused_global_shapes(S, G, D):
+def test_fused_global_shapes(S, G, D, dtype):
     # key counts: no context (proposals only), proposals across a 128-key
-    # chunk boundary and a 32-key tile boundary, chunk-aligned context
+    # chunk boundary and a 32-key tile boundary, chunk-aligned context.
+    # Over fp8 the value codes load in pairs of dims only at D=512, so the
+    # smaller head dims take the unpaired substitution of the call's tokens.
     kc = np.array([S, 126 + S, 128 + S, 131, 700, 2000], np.int32)
     kc = np.maximum(kc, S)
     B = kc.size
     g = synthetic.rng(73)
     x = dict(key_count=kc, k=synthetic.normal_bf16(g, (B, 2048, 2, D)),
              v=quarter_scale(synthetic.normal_bf16(g, (B, 2048, 2, D))), q=synthetic.normal_bf16(g, (B, S, 2 * G, D)))
-    out, ref = fused_global_case(x, S, 2048)
+    ks, vs = (4.2 / 448, 1.3 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    out, ref = fused_global_case(x, S, 2048, dtype, ks, vs)
     assert_parity(host_f64(out), ref, f"fused global S={S} G={G} D={D}")
 
 
