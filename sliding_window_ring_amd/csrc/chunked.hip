@@ -71,8 +71,9 @@ __device__ __forceinline__ int region_keys(const AttnParams& p, int b) {
 
 // ------------------------------------------------------------------ pass 1
 
-constexpr int kChunkKeys = 128;                 // keys per workgroup of pass 1
+constexpr int kChunkKeys = 128;                 // keys per workgroup of pass 1 (global)
 constexpr int kChunkWaves = kChunkKeys / 8;     // 16 waves: two per 16-key subtile
+constexpr int kVerifyChunkKeys = 2 * kChunkKeys;  // verify ring chunks: two halves in turn
 
 // Chunks of one (request, KV head) that pass 1 filled, a prefix of the
 // launch's chunks: the region chunks up to the key count (verify: after the
@@ -84,7 +85,8 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
     const int tiles = (region_keys<MODE_GLOBAL>(p, b) + 31) / 32;
     return min((tiles + p.tiles_per_split - 1) / p.tiles_per_split, p.nchunk);
   }
-  const int n = (region_keys<MODE>(p, b) + kChunkKeys - 1) / kChunkKeys;
+  const int ck = MODE == MODE_VERIFY ? kVerifyChunkKeys : kChunkKeys;
+  const int n = (region_keys<MODE>(p, b) + ck - 1) / ck;
   return min(n + (MODE == MODE_VERIFY ? 1 : 0), p.nchunk);
 }
 
@@ -106,6 +108,12 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 //   values   waves w < PVW: O^T(dims w*DPW .. +DPW, rows) = V^T . P^T over
 //            the chunk, bf16 MFMA into fp32; the unnormalised rows go to the
 //            workspace for pass 2 with streaming stores.
+// A verify ring chunk is 256 keys taken as two 128-key halves in turn (K of
+// both on entry, V of both after the first half's scores), the softmax
+// lanes carrying each row's running (max, sum) from one half to the next
+// and the value waves rescaling their rows by the factor the softmax lanes
+// leave in LDS: one partial per 256 keys, so pass 1 writes and pass 2 reads
+// half as many.
 // Masks: global -- key < key_count and key <= q_pos of the row's position;
 // verify ring chunk -- a committed slot no older than W-2-i positions before
 // pos0-1 for proposal i (position pos0+i sees positions >= pos0+i-W+1);
@@ -121,6 +129,7 @@ struct ChunkSmem {
   float sbuf[2][16 * NCT][kChunkKeys + 4];
   __attribute__((aligned(16))) __bf16 pbuf[16 * NCT][kChunkKeys + 8];
   __attribute__((aligned(16))) __bf16 qbuf[16 * NCT][D + 8];
+  float alpha[16 * NCT];  // verify: each row's rescale from one half to the next
 };
 
 // The call's own tokens, staged by the global chunk that holds their slots
@@ -146,6 +155,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   constexpr int DPW = D / PVW;                       // value dims per value wave
   constexpr int NDT = DPW / 16;                      // 16-dim value tiles per value wave
   constexpr int KS = CK / 32;                        // 32-key k steps of the value product
+  constexpr int NH = MODE == MODE_VERIFY ? 2 : 1;    // 128-key halves per ring chunk (verify: 256 keys)
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr bool KPAIR = FP8 && NCH % 2 == 0;        // 16-byte fp8 K loads (two k chunks)
   constexpr bool VPAIR = FP8 && NDT % 2 == 0;        // 16-byte fp8 V loads (two adjacent dims)
@@ -163,7 +173,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
   const bool prop = MODE == MODE_VERIFY && chunk == 0;           // the proposals' chunk
-  const int k0 = (MODE == MODE_VERIFY ? chunk - 1 : chunk) * CK;  // region slot of key 0
+  const int k0 = (MODE == MODE_VERIFY ? chunk - 1 : chunk) * CK * NH;  // region slot of key 0
   const int64_t k_off = p.k_off[b], v_off = p.v_off[b];
   const int cap_r = region_slots(p, b);
   const int S_r = stored_slots(cap_r);  // slots stored per KV head (region layout: swr_device.h)
@@ -188,33 +198,35 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // wave wait for each load in turn (the compiler places it right there),
   // where the bf16 operands let all of them fly at once.
   const int kq = wave % KQ, dh = wave / KQ;
-  bf16x8 kop[NCH];
-  bf16x8 vop[KS][NDT];
-  u32x4 kraw[FP8 ? NCH : 1];     // paired: entries 0 .. NCH/2-1; else the low halves
-  u32x4 vraw[KS][FP8 ? NDT : 1];
-  auto load_v = [&]() {
+  // Operands of half h (keys k0 + 128h ..) of the chunk.
+  bf16x8 kop[NH][NCH];
+  bf16x8 vop[NH][KS][NDT];
+  u32x4 kraw[NH][FP8 ? NCH : 1];  // paired: entries 0 .. NCH/2-1; else the low halves
+  u32x4 vraw[NH][KS][FP8 ? NDT : 1];
+  auto load_v = [&](int h) {
     if (wave >= PVW) return;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + ((k0 + 32 * ks) >> 3) + lq) * D;
+      const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + ((k0 + CK * h + 32 * ks) >> 3) + lq) * D;
       if (VPAIR) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt += 2) vraw[ks][dt / 2] = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
+        for (int dt = 0; dt < NDT; dt += 2)
+          vraw[h][ks][dt / 2] = load16_stream(rv, (vblock + (uint32_t)vdim(dt)) * 8);
       } else {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const uint32_t off = (vblock + (uint32_t)vdim(dt)) * 8 * ESZ;
           if (FP8) {
             const u32x2 w = load8(rv, off);
-            vraw[ks][dt] = u32x4{w[0], w[1], 0u, 0u};
+            vraw[h][ks][dt] = u32x4{w[0], w[1], 0u, 0u};
           } else {
-            vop[ks][dt] = as_bf16x8(load16_stream(rv, off));
+            vop[h][ks][dt] = as_bf16x8(load16_stream(rv, off));
           }
         }
       }
     }
   };
-  auto cvt_v = [&]() {
+  auto cvt_v = [&](int h) {
     if constexpr (FP8) {
       if (wave >= PVW) return;
 #pragma unroll
@@ -222,48 +234,52 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         if (VPAIR) {
 #pragma unroll
           for (int dt = 0; dt < NDT; dt += 2) {
-            vop[ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt / 2][0], vraw[ks][dt / 2][1]});
-            vop[ks][dt + 1] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt / 2][2], vraw[ks][dt / 2][3]});
+            vop[h][ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[h][ks][dt / 2][0], vraw[h][ks][dt / 2][1]});
+            vop[h][ks][dt + 1] = fp8x8_to_bf16x8(u32x2{vraw[h][ks][dt / 2][2], vraw[h][ks][dt / 2][3]});
           }
         } else {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vop[ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[ks][dt][0], vraw[ks][dt][1]});
+          for (int dt = 0; dt < NDT; ++dt)
+            vop[h][ks][dt] = fp8x8_to_bf16x8(u32x2{vraw[h][ks][dt][0], vraw[h][ks][dt][1]});
         }
       }
     }
   };
-  auto cvt_k = [&]() {
+  auto cvt_k = [&](int h) {
     if constexpr (FP8) {
       if (KPAIR) {
 #pragma unroll
         for (int c = 0; c < NCH; c += 2) {
-          kop[c] = fp8x8_to_bf16x8(u32x2{kraw[c / 2][0], kraw[c / 2][1]});
-          kop[c + 1] = fp8x8_to_bf16x8(u32x2{kraw[c / 2][2], kraw[c / 2][3]});
+          kop[h][c] = fp8x8_to_bf16x8(u32x2{kraw[h][c / 2][0], kraw[h][c / 2][1]});
+          kop[h][c + 1] = fp8x8_to_bf16x8(u32x2{kraw[h][c / 2][2], kraw[h][c / 2][3]});
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) kop[c] = fp8x8_to_bf16x8(u32x2{kraw[c][0], kraw[c][1]});
+        for (int c = 0; c < NCH; ++c) kop[h][c] = fp8x8_to_bf16x8(u32x2{kraw[h][c][0], kraw[h][c][1]});
       }
     }
   };
   if (!prop) {
-    // row lr of half kq%2 of tile kq/2; granule (dh*DH + kdim(c)) / R of it
-    constexpr int R = FP8 ? 16 : 8;
-    const uint32_t hb = k_half_base(g, S_r, k0 + 32 * (kq >> 1), kq & 1, D, ESZ);
-    if (KPAIR) {
 #pragma unroll
-      for (int c = 0; c < NCH; c += 2)
-        kraw[c / 2] = load16_stream(rk, hb + k_granule_offset((dh * DH + kdim(c)) / R, lr));
-    } else {
+    for (int h = 0; h < NH; ++h) {
+      // row lr of half kq%2 of tile kq/2; granule (dh*DH + kdim(c)) / R of it
+      constexpr int R = FP8 ? 16 : 8;
+      const uint32_t hb = k_half_base(g, S_r, k0 + CK * h + 32 * (kq >> 1), kq & 1, D, ESZ);
+      if (KPAIR) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int dim = dh * DH + kdim(c);
-        const uint32_t off = hb + k_granule_offset(dim / R, lr) + (uint32_t)((dim % R) * ESZ);
-        if (FP8) {
-          const u32x2 w = load8(rk, off);
-          kraw[c] = u32x4{w[0], w[1], 0u, 0u};
-        } else {
-          kop[c] = as_bf16x8(load16_stream(rk, off));
+        for (int c = 0; c < NCH; c += 2)
+          kraw[h][c / 2] = load16_stream(rk, hb + k_granule_offset((dh * DH + kdim(c)) / R, lr));
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int dim = dh * DH + kdim(c);
+          const uint32_t off = hb + k_granule_offset(dim / R, lr) + (uint32_t)((dim % R) * ESZ);
+          if (FP8) {
+            const u32x2 w = load8(rk, off);
+            kraw[h][c] = u32x4{w[0], w[1], 0u, 0u};
+          } else {
+            kop[h][c] = as_bf16x8(load16_stream(rk, off));
+          }
         }
       }
     }
@@ -274,16 +290,16 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     // other operand element is zero
     const int pj = 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kop[c] = bf16x8{};
+    for (int c = 0; c < NCH; ++c) kop[0][c] = bf16x8{};
     if (pj < S) {
       const uint16_t* src = p.k_prop + ((size_t)(b * S + pj) * Hkv + g) * D + dh * DH;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
+      for (int c = 0; c < NCH; ++c) kop[0][c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vop[ks][dt] = bf16x8{};
+      for (int dt = 0; dt < NDT; ++dt) vop[0][ks][dt] = bf16x8{};
     if (wave < PVW && lq == 0) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -294,7 +310,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           if (j < S) bits = p.v_prop[((size_t)(b * S + j) * Hkv + g) * D + vdim(dt)];
           v[j] = __builtin_bit_cast(__bf16, bits);
         }
-        vop[0][dt] = v;
+        vop[0][0][dt] = v;
       }
     }
   }
@@ -365,134 +381,164 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // ---------------------------------------------------------- scores
   __syncthreads();  // Q in LDS
-  if (!prop) cvt_k();
-  if constexpr (SUBP) {
-    if (tok_chunk) {  // this lane's K row is token j of the call
-      const int j = k0 + 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3) - pos0;
-      if (j >= 0 && j < S) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) kop[c] = *reinterpret_cast<const bf16x8*>(&tok_k[j * D + dh * DH + kdim(c)]);
-      }
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      acc = mfma16x16x32(kop[c], *reinterpret_cast<const bf16x8*>(&qbuf[ct * 16 + lr][dh * DH + kdim(c)]), acc);
-    // C rows 4*lq + r are keys 8*lq + 4*(kq%2) + r of tile kq/2
-    *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][32 * (kq >> 1) + 8 * lq + 4 * (kq & 1)]) = acc;
-  }
-  // V loads go out once the chunk's scores are computed rather than on
-  // entry: a smaller first burst of requests across all workgroups streams
-  // faster, and the value loads still overlap the softmax.
-  if (!prop) load_v();
-  __syncthreads();
-
-  // ---------------------------------------------------------- softmax
   const size_t slot = ((size_t)unit * p.nchunk + chunk) * p.rows;
   const bool bf16_prop = FP8 && prop;  // proposals as bf16 values, not codes
   const float qs = bf16_prop ? p.qk_scale_prop : p.qk_scale;
-  if (srow < ROWS) {
-    const int kk = KPL * lr;
-    // verify: slot age of the newest committed position, and the oldest age
-    // row i still sees
-    const int ring_head = (MODE == MODE_VERIFY && p.pos[b] > 0) ? (p.pos[b] - 1) % p.cap : 0;
-    const int age_lim = p.cap - 2 - si;
-    float sv[KPL];
-    float mx = -INFINITY;
+  // verify: slot age of the newest committed position, and the oldest age
+  // row i still sees
+  const int ring_head = (MODE == MODE_VERIFY && p.pos[b] > 0) ? (p.pos[b] - 1) % p.cap : 0;
+  const int age_lim = p.cap - 2 - si;
+  // halves this chunk computes: a second half wholly past the key count
+  // adds nothing (uniform over the workgroup)
+  const int nh = (prop || k0 + CK >= n_keys) ? 1 : NH;
+  float m_run = -INFINITY, l_run = 0.f;  // softmax lanes: the row's running (max, sum)
+  f32x4 o[NCT][NDT];                     // value lanes: rows ct*16 + lr, unnormalised
 #pragma unroll
-    for (int e4 = 0; e4 < KPL; e4 += 4) {
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sbuf[0][srow][kk + e4]);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sbuf[1][srow][kk + e4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = kk + e4 + e;  // key of the chunk
-        bool vis;
-        if (MODE == MODE_GLOBAL) {
-          vis = k0 + j < n_keys && k0 + j <= qp;
-        } else if (prop) {
-          vis = j < S && j <= si;
-        } else {
-          int age = ring_head - (k0 + j);
-          if (age < 0) age += p.cap;
-          vis = k0 + j < n_keys && age <= age_lim;
-        }
-        vis = vis && srow_ok;
-        sv[e4 + e] = vis ? (s0[e] + s1[e]) * qs : -INFINITY;
-        mx = fmaxf(mx, sv[e4 + e]);
-      }
-    }
-    const float m = max16lanes(mx);
-    const float m_use = (m == -INFINITY) ? 0.f : m;
-    float ps = 0.f;
-#pragma unroll
-    for (int e4 = 0; e4 < KPL; e4 += 4) {
-      bf16x4 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = (__bf16)fast_exp2(sv[e4 + e] - m_use);
-        ps += (float)pb[e];
-      }
-      *reinterpret_cast<bf16x4*>(&pbuf[srow][kk + e4]) = pb;
-    }
-    const float l = sum16lanes(ps);
-    if (lr == 0 && srow_ok) {
-      p.ws_pml[(slot + srow) * 2 + 0] = m;
-      p.ws_pml[(slot + srow) * 2 + 1] = l;
-    }
-  }
-  __syncthreads();
-  if (wave >= PVW) return;
-
-  // ---------------------------------------------------------- values
-  if (!prop) cvt_v();
-  if constexpr (SUBP) {
-    if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          u32x4 w = __builtin_bit_cast(u32x4, vop[ks][dt]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = k0 + 32 * ks + 8 * lq + e - pos0;
-            if (j >= 0 && j < S) {
-              const uint32_t nv = __builtin_bit_cast(uint16_t, tok_v[j * D + vdim(dt)]);
-              w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (nv << 16)) : ((w[e >> 1] & 0xFFFF0000u) | nv);
-            }
-          }
-          vop[ks][dt] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-  }
-  if (!prop && k0 + CK > n_keys) {  // last chunk: zero values of keys past the count
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 keep;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = k0 + 32 * ks + 8 * lq + 2 * j;
-        keep[j] = (kk < n_keys ? 0x0000FFFFu : 0u) | (kk + 1 < n_keys ? 0xFFFF0000u : 0u);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        vop[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[ks][dt]) & keep);
-    }
-  }
-  f32x4 o[NCT][NDT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 pt = *reinterpret_cast<const bf16x8*>(&pbuf[ct * 16 + lr][32 * ks + 8 * lq]);
+  for (int h = 0; h < NH; ++h) {
+    if (h >= nh) break;
+    const int kh = k0 + CK * h;  // region slot of the half's key 0
+    if (!prop) cvt_k(h);
+    if constexpr (SUBP) {
+      if (tok_chunk) {  // this lane's K row is token j of the call
+        const int j = kh + 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3) - pos0;
+        if (j >= 0 && j < S) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[ks][dt], pt, o[ct][dt]);
+          for (int c = 0; c < NCH; ++c)
+            kop[h][c] = *reinterpret_cast<const bf16x8*>(&tok_k[j * D + dh * DH + kdim(c)]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        acc = mfma16x16x32(kop[h][c], *reinterpret_cast<const bf16x8*>(&qbuf[ct * 16 + lr][dh * DH + kdim(c)]), acc);
+      // C rows 4*lq + r are keys 8*lq + 4*(kq%2) + r of tile kq/2
+      *reinterpret_cast<f32x4*>(&sbuf[dh][ct * 16 + lr][32 * (kq >> 1) + 8 * lq + 4 * (kq & 1)]) = acc;
+    }
+    // V loads (every half's) go out once the first half's scores are
+    // computed rather than on entry: a smaller first burst of requests
+    // across all workgroups streams faster, and the value loads still
+    // overlap the softmax.
+    if (h == 0 && !prop) {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+        if (hh < nh) load_v(hh);
+    }
+    __syncthreads();
+
+    // -------------------------------------------------------- softmax
+    if (srow < ROWS) {
+      const int kk = KPL * lr;
+      float sv[KPL];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e4 = 0; e4 < KPL; e4 += 4) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&sbuf[0][srow][kk + e4]);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&sbuf[1][srow][kk + e4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = kk + e4 + e;  // key of the half
+          bool vis;
+          if (MODE == MODE_GLOBAL) {
+            vis = kh + j < n_keys && kh + j <= qp;
+          } else if (prop) {
+            vis = j < S && j <= si;
+          } else {
+            int age = ring_head - (kh + j);
+            if (age < 0) age += p.cap;
+            vis = kh + j < n_keys && age <= age_lim;
+          }
+          vis = vis && srow_ok;
+          sv[e4 + e] = vis ? (s0[e] + s1[e]) * qs : -INFINITY;
+          mx = fmaxf(mx, sv[e4 + e]);
+        }
+      }
+      const float m_new = fmaxf(m_run, max16lanes(mx));
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);  // 0 on the first half
+      float ps = 0.f;
+#pragma unroll
+      for (int e4 = 0; e4 < KPL; e4 += 4) {
+        bf16x4 pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[e] = (__bf16)fast_exp2(sv[e4 + e] - m_use);
+          ps += (float)pb[e];
+        }
+        *reinterpret_cast<bf16x4*>(&pbuf[srow][kk + e4]) = pb;
+      }
+      l_run = l_run * alpha + sum16lanes(ps);
+      m_run = m_new;
+      if (NH > 1 && lr == 0) sm.alpha[srow] = alpha;
+    }
+    __syncthreads();
+
+    // --------------------------------------------------------- values
+    if (wave < PVW) {
+      if (!prop) cvt_v(h);
+      if constexpr (SUBP) {
+        if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              u32x4 w = __builtin_bit_cast(u32x4, vop[h][ks][dt]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int j = kh + 32 * ks + 8 * lq + e - pos0;
+                if (j >= 0 && j < S) {
+                  const uint32_t nv = __builtin_bit_cast(uint16_t, tok_v[j * D + vdim(dt)]);
+                  w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (nv << 16)) : ((w[e >> 1] & 0xFFFF0000u) | nv);
+                }
+              }
+              vop[h][ks][dt] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+      }
+      if (!prop && kh + CK > n_keys) {  // last half: zero values of keys past the count
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 keep;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kk = kh + 32 * ks + 8 * lq + 2 * j;
+            keep[j] = (kk < n_keys ? 0x0000FFFFu : 0u) | (kk + 1 < n_keys ? 0xFFFF0000u : 0u);
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            vop[h][ks][dt] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, vop[h][ks][dt]) & keep);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (NH > 1 && h > 0) {  // rescale to the running maximum of the row
+          const float a = sm.alpha[ct * 16 + lr];
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[ct][dt] *= a;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 pt = *reinterpret_cast<const bf16x8*>(&pbuf[ct * 16 + lr][32 * ks + 8 * lq]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[h][ks][dt], pt, o[ct][dt]);
+        }
+      }
     }
   }
+
+  // ----------------------------------------------------------- partials
+  if (srow < ROWS && lr == 0 && srow_ok) {
+    p.ws_pml[(slot + srow) * 2 + 0] = m_run;
+    p.ws_pml[(slot + srow) * 2 + 1] = l_run;
+  }
+  if (wave >= PVW) return;
   // Lane (lr, lq) holds rows ct*16 + lr; group q of four consecutive dims
   // starts at qdim(q).  Proposal values are bf16, not codes: divided by
   // v_scale here so that the merge's v_scale restores them.
@@ -522,11 +568,12 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 // last.  When the units are a multiple of the 8 XCDs (workgroup j runs on
 // XCD j % 8), all ring chunks of a unit go to one XCD, whose L2 then serves
 // the unit's Q to all of them after one read.
-// Up to 256 head dims two workgroups stay resident per CU (eight waves per
-// SIMD, 64 registers a lane); 512 dims need more registers and keep one.
+// Up to 256 head dims two global workgroups stay resident per CU (eight
+// waves per SIMD, 64 registers a lane); 512 dims, and verify with its two
+// halves' operands, need more registers and keep one.
 template <int D, int NCT, bool FP8, int MODE>
-__global__ void __launch_bounds__(64 * kChunkWaves) __attribute__((amdgpu_waves_per_eu(D <= 256 ? 8 : 4)))
-chunk_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(64 * kChunkWaves)
+__attribute__((amdgpu_waves_per_eu(D <= 256 && MODE != MODE_VERIFY ? 8 : 4))) chunk_kernel(const AttnParams p) {
   __shared__ ChunkSmem<D, NCT> sm;
   if (MODE == MODE_VERIFY) {
     const int nring = p.nchunk - 1;
@@ -797,7 +844,7 @@ bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, Attn
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
   const int rows = (Hq / Hkv) * S;
   if (rows > 32) return false;
-  const int nchunk = cdiv(keys, kChunkKeys) + (mode == MODE_VERIFY ? 1 : 0);
+  const int nchunk = mode == MODE_VERIFY ? cdiv(keys, kVerifyChunkKeys) + 1 : cdiv(keys, kChunkKeys);
   if (nchunk > kMaxChunks) return false;
   pl->mode = mode;
   pl->chunked = 1;
