@@ -145,6 +145,21 @@ def test_verify_proposal_counts(S, G):
     assert_parity(host_f64(out), ref, f"verify S={S} G={G}")
 
 
+@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+def test_verify_ring_chunk_halves(dtype, D):
+    # A ring chunk of the chunked form covers 256 slots as two 128-key
+    # halves: committed counts that end inside the first half, exactly at
+    # and just past the half boundary, inside the second half, at a chunk
+    # boundary and past the window (wrapped rings)
+    positions = (0, 1, 127, 128, 129, 200, 255, 256, 257, 300, 511, 512, 700, 1023, 1024, 1500)
+    w = synthetic.Workload("t", B=len(positions), Hkv=2, G=8, D=D, W=1024, S=4)
+    x = synthetic.sliding_verify(w, seed=42, positions=positions)
+    ks, vs = (4.2 / 448, 4.4 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    out, ref = verify_case(w, x, dtype, ks, vs)
+    assert_parity(host_f64(out), ref, "verify ring chunk halves")
+
+
 @pytest.mark.parametrize("D", [64, 128, 512])
 def test_verify_head_dims(D):
     w = synthetic.Workload("t", B=3, Hkv=2, G=8, D=D, W=64, S=4)
