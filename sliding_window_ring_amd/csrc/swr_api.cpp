@@ -25,6 +25,10 @@ bool supported_d(int D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
 int elem_size(int dtype) { return dtype == SWR_KV_FP8_E4M3 ? 1 : 2; }
 
+// Slots a region stores (whole 32-slot tiles), without the int overflow of
+// the device-side helper for capacities near INT32_MAX.
+int64_t stored_slots64(int cap) { return ((int64_t)cap + 31) / 32 * 32; }
+
 // Checks the fields of a KV view that every call shares.
 swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
   if (!kv || !kv->k_base || !kv->v_base || !kv->k_off || !kv->v_off) return SWR_ERR_INVALID;
@@ -35,7 +39,7 @@ swr_status check_kv(const swr_kv* kv, int Hkv, int D) {
     if (!(kv->k_scale > 0.f) || !std::isfinite(kv->k_scale)) return SWR_ERR_INVALID;
     if (!(kv->v_scale > 0.f) || !std::isfinite(kv->v_scale)) return SWR_ERR_INVALID;
   }
-  const double bytes = (double)swr::stored_slots(kv->cap) * Hkv * D * elem_size(kv->dtype);
+  const double bytes = (double)stored_slots64(kv->cap) * Hkv * D * elem_size(kv->dtype);
   if (bytes > 4294967295.0) return SWR_ERR_UNSUPPORTED;  // regions are addressed with 32-bit offsets
   return SWR_OK;
 }
@@ -89,7 +93,7 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
     if ((!append && !key_count) || cap_or_max_keys < 1) return SWR_ERR_INVALID;
     if (append && cap_or_max_keys < S) return SWR_ERR_INVALID;
     // the padded contraction reads pad64(key_count) slots of every region
-    if ((long)(cap_or_max_keys + 63) / 64 * 64 > kv->cap) return SWR_ERR_INVALID;
+    if (((int64_t)cap_or_max_keys + 63) / 64 * 64 > kv->cap) return SWR_ERR_INVALID;
   }
   const int fp8 = kv->dtype == SWR_KV_FP8_E4M3;
   AttnPlan pl;
@@ -242,7 +246,7 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
 int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype) {
   if (cap <= 0 || cap % 8 != 0 || Hkv <= 0 || D <= 0) return -1;
   if (dtype != SWR_KV_BF16 && dtype != SWR_KV_FP8_E4M3) return -1;
-  return (int64_t)swr::stored_slots(cap) * Hkv * D * elem_size(dtype);
+  return stored_slots64(cap) * Hkv * D * elem_size(dtype);
 }
 
 swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {

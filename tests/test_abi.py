@@ -99,6 +99,19 @@ def test_verify_and_global_validation():
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6017, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 0, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
     assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == WORKSPACE
+    # a key bound near INT32_MAX is past the region, not an overflow
+    assert g(ctypes.byref(rg), FAKE, FAKE, FAKE, FAKE, 2**31 - 1, 1, 4, 16, 2, 512, 0.04, None, 0, None) == INVALID
+
+
+def test_regions_past_32_bit_offsets_are_unsupported():
+    # capacities whose regions pass 4 GiB (the kernels address a region with
+    # 32-bit offsets), up to INT32_MAX with no overflow on the way
+    g = swr.lib.swr_global_attend
+    for cap in (2_097_152, 2**31 - 8):
+        r = kv(cap=cap)
+        assert g(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == UNSUPPORTED
+    r = kv(cap=2_097_120)  # just under 4 GiB at 2 KV heads x 512 bf16
+    assert g(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, 6005, 1, 4, 16, 2, 512, 0.04, None, 0, None) == WORKSPACE
 
 
 def test_fused_append_decode_validation():
@@ -179,6 +192,7 @@ def test_workspace_bytes_unsupported_is_zero():
 
 def test_region_bytes():
     assert swr.region_bytes(1024, 8, 256) == 1024 * 8 * 256 * 2
+    assert swr.region_bytes(2**31 - 8, 1, 64) == 2**31 * 64 * 2  # 64-bit count, slots rounded to 32
     assert swr.region_bytes(1024, 8, 256, swr.SWR_KV_FP8_E4M3) == 1024 * 8 * 256
     with pytest.raises(ValueError):
         swr.region_bytes(1001, 8, 256)
