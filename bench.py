@@ -7,16 +7,18 @@ one global layer of the 6005-key speculative verify (append the 4 proposals,
 then the grouped 32-row attention over the 64-padded region).  Each layer is
 one library call that does both (swr_swa_append_decode,
 swr_global_append_attend); the separate append and attention calls are timed
-beside it.  Every step
-uses the K/V of a different layer (3 sliding layers x 470 MB, 24 global
-layers x 24.6 MB, all carved from one pool), so the K/V stream comes from
-HBM and not from the 256 MB Infinity Cache.
+beside it.  Every step uses the K/V of a different layer (3 sliding layers x
+470 MB, 24 global layers x 24.6 MB, all carved from one pool), so the K/V
+stream comes from HBM and not from the 256 MB Infinity Cache.
 
 Prints one JSON line: aggregate algorithmic K/V GB/s of the step, us/layer of
 each layer type, the roofline of the dominant kernel (the sliding decode),
-and the oracle's rate on the host cores as a CPU baseline.
+the chip's measured streaming-read ceiling, the other workloads (sliding
+verify, fp8 decode, the mixed step, a 60-layer decode stack, the global
+key-count sweep) and the oracle's rate on the host cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-extra] [--no-sweep]
 """
 from __future__ import annotations
 
