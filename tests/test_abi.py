@@ -185,6 +185,14 @@ def test_zero_batch_attention_is_a_no_op():
     assert decode(B=0) == OK
 
 
+def test_verify_workspace_is_one_partial_per_256_ring_keys():
+    # B=8 x 8 KV heads, W=1024: 4 ring chunks of 256 keys + 1 proposal chunk
+    # per unit, 32 rows of 256 fp32 dims each, plus a (max, sum) per row
+    units, chunks, rows, d = 8 * 8, 1024 // 256 + 1, 8 * 4, 256
+    want = units * chunks * rows * d * 4 + units * chunks * rows * 2 * 4
+    assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 4, 64, 8, 256, 1024) == want
+
+
 def test_workspace_bytes_unsupported_is_zero():
     assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 9, 64, 8, 256, 1024) == 0
     assert swr.workspace_bytes(99, 8, 4, 64, 8, 256, 1024) == 0
