@@ -137,6 +137,26 @@ struct ChunkSmem {
 // then V; over an fp8 region the values its stored codes decode to, in units
 // of the scale), sized at launch -- none for the other calls.
 extern __shared__ __attribute__((aligned(16))) __bf16 chunk_tokens[];
+
+// Piece t of a global call's tokens over an fp8 region: values 4t .. 4t+3
+// of K's S*D values then V's ((token j, head dim d) at j*D + d), as bf16
+// bits.
+__device__ __forceinline__ u32x4 load_token_piece4(const AttnParams& p, int b, int g, int D, int t) {
+  const int n = p.S * D, v = 4 * t;
+  const bool is_v = v >= n;
+  const int r = v - (is_v ? n : 0), j = r / D, d = r - j * D;
+  const size_t src = ((size_t)(b * p.S + j) * p.Hkv + g) * D + (size_t)d;
+  const u32x2 w = *reinterpret_cast<const u32x2*>((is_v ? p.v_prop : p.k_prop) + src);
+  return u32x4{w[0], w[1], 0u, 0u};
+}
+
+// Writes piece t's values, as the region will hold them, to the staged
+// tokens (K's S*D values, then V's).
+__device__ __forceinline__ void stage_token_piece4(const AttnParams& p, __bf16* tok, int S, int D, int t, u32x4 bits) {
+  const bool is_v = 4 * t >= S * D;
+  *reinterpret_cast<u32x2*>(&tok[4 * t]) =
+      fp8_stored_values4(u32x2{bits[0], bits[1]}, is_v ? p.v_scale_store : p.k_scale_store);
+}
 template <int MODE>
 constexpr bool stages_tokens() { return MODE == MODE_GLOBAL; }
 
@@ -315,9 +335,12 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     }
   }
   // global call that appends its own S tokens (keys pos0 .. pos0+S-1):
-  // the chunk holding any of their slots stages them in LDS (one 16-byte
-  // piece of K and of V per thread: S*D/8 <= 512 pieces), loaded here behind
-  // the region's loads and written to LDS after the Q loads have gone out
+  // the chunk holding any of their slots stages them in LDS (bf16: one
+  // 16-byte piece of K and of V per thread, S*D/8 <= 512 pieces; fp8: one
+  // 4-value piece of K or V per thread, each value encoded and decoded, so
+  // that the encodes spread over every wave of the workgroup), loaded here
+  // behind the region's loads and written to LDS after the Q loads have gone
+  // out
   // (the load counter drains in order, so writing them first would hold the
   // Q loads back until the region's data arrived); the Q barrier covers the
   // writes.  The operands take them in place of the slots' old contents, and
@@ -334,12 +357,17 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (p.append) {
       pos0 = p.pos[b];
       tok_chunk = pos0 < k0 + CK && pos0 + S > k0;  // uniform over the workgroup
-      tok_piece = tok_chunk && (int)threadIdx.x < S * (D / 8);
-      if (tok_piece) {
-        const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
-        const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
-        tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
-        tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+      if (FP8) {
+        tok_piece = tok_chunk && (int)threadIdx.x < 2 * S * (D / 4);
+        if (tok_piece) tok_kbits = load_token_piece4(p, b, g, D, threadIdx.x);
+      } else {
+        tok_piece = tok_chunk && (int)threadIdx.x < S * (D / 8);
+        if (tok_piece) {
+          const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
+          const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
+          tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+          tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+        }
       }
     }
   }
@@ -359,11 +387,13 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     }
   }
   if constexpr (SUBP) {
-    if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
-      if (FP8) {
-        tok_kbits = __builtin_bit_cast(u32x4, fp8_stored_values(__builtin_bit_cast(bf16x8, tok_kbits), p.k_scale_store));
-        tok_vbits = __builtin_bit_cast(u32x4, fp8_stored_values(__builtin_bit_cast(bf16x8, tok_vbits), p.v_scale_store));
-      }
+    if (FP8) {
+      // piece t: values 4t .. 4t+3 of K's S*D then V's (token j = 4t/D of
+      // K or V); LDS holds K then V, so piece t lands at tok_k[4t]
+      if (tok_piece) stage_token_piece4(p, chunk_tokens, S, D, threadIdx.x, tok_kbits);
+      for (int t = threadIdx.x + 64 * NW; tok_chunk && t < 2 * S * (D / 4); t += 64 * NW)
+        stage_token_piece4(p, chunk_tokens, S, D, t, load_token_piece4(p, b, g, D, t));
+    } else if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
       *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
       *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
     }
@@ -610,12 +640,12 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 16;
 constexpr int kMaxChunks = 513;  // 65536 region keys (+ a proposal chunk)
 
-// A global call that appended its own tokens: token j's head dims 8*d8 ..
-// +7 go into slot pos0 + j of its region (dropped past the region, as by the
-// append call; over an fp8 region as their E4M3 codes).  Done by the merge
-// pass, once every chunk has read: the token's bits are loaded before the
-// merge's own loads and stored after them, so the stores add no round trip
-// of their own.
+// A global call that appended its own tokens: token j goes into slot
+// pos0 + j of its region (dropped past the region, as by the append call).
+// Done by the merge pass, once every chunk has read: the token's bits are
+// loaded before the merge's own loads and stored after them, so the stores
+// add no round trip of their own.  bf16 regions take 8-dim pieces
+// (CallToken); fp8 regions one E4M3 code per thread (CallTokenCode).
 struct CallToken {
   u32x4 k, v;
   int j = -1, d8 = 0;
@@ -631,16 +661,51 @@ __device__ __forceinline__ CallToken load_call_token(const AttnParams& p, int D,
   return t;
 }
 
-template <bool FP8>
 __device__ __forceinline__ void store_call_token(const AttnParams& p, int D, int b, int g, const CallToken& t) {
   const int cap_r = region_slots(p, b);
   const int slot = p.pos[b] + t.j;
   if (t.j < 0 || slot < 0 || slot >= cap_r) return;
   const int S_r = stored_slots(cap_r);
-  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * (FP8 ? 1 : 2));
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * 2);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
-  store_token_piece<FP8>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, p.k_scale_store, p.v_scale_store);
+  store_token_piece<false>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, p.k_scale_store, p.v_scale_store);
+}
+
+// fp8 regions: the call's token values are encoded one per thread, spread
+// over the unit's row workgroups of each quarter (2*S*PART values of the
+// quarter's dims, `per` to a row); an encode is too long a chain to leave
+// all of them to the row-0 threads.
+struct CallTokenCode {
+  uint16_t bits = 0;
+  int j = -1, d = 0;
+  bool is_v = false;
+};
+
+__device__ __forceinline__ CallTokenCode load_call_token_code(const AttnParams& p, int D, int part, int quarter, int b,
+                                                              int g, int v) {
+  CallTokenCode t;
+  const int n = p.S * part;  // values of one of K, V in the quarter
+  t.is_v = v >= n;
+  const int r = v - (t.is_v ? n : 0);
+  t.j = r / part;
+  t.d = quarter * part + (r - t.j * part);
+  const size_t src = ((size_t)(b * p.S + t.j) * p.Hkv + g) * D + (size_t)t.d;
+  t.bits = (t.is_v ? p.v_prop : p.k_prop)[src];
+  return t;
+}
+
+__device__ __forceinline__ void store_call_token_code(const AttnParams& p, int D, int b, int g, const CallTokenCode& t) {
+  const int cap_r = region_slots(p, b);
+  const int slot = p.pos[b] + t.j;
+  if (t.j < 0 || slot < 0 || slot >= cap_r) return;
+  const int S_r = stored_slots(cap_r);
+  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+  const uint8_t code = e4m3_encode(__builtin_bit_cast(float, (uint32_t)t.bits << 16),
+                                   t.is_v ? p.v_scale_store : p.k_scale_store);
+  store_token_code(rk, rv, slot, g, S_r, D, t.d, t.is_v, code);
 }
 
 struct RunningRow {
@@ -716,15 +781,35 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   const int d = quarter * PART + (tid - grp * TPG) * 4;
   const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
 
-  CallToken tok;  // the call's tokens, this quarter's dims
-  if (MODE == MODE_GLOBAL && p.append && row == 0 && tid < p.S * (PART / 8))
-    tok = load_call_token(p, D, b, g, tid / (PART / 8), quarter * (PART / 8) + tid % (PART / 8));
+  // the call's tokens, this quarter's dims: bf16 as 8-dim pieces in the
+  // row-0 workgroup; fp8 one value per thread, `per` values to a row
+  CallToken tok;
+  CallTokenCode tcode;
+  const int tok_values = 2 * p.S * PART;
+  const int per = (tok_values + p.rows - 1) / p.rows;
+  if (MODE == MODE_GLOBAL && p.append) {
+    if constexpr (FP8) {
+      if (tid < per && row * per + tid < tok_values) tcode = load_call_token_code(p, D, PART, quarter, b, g, row * per + tid);
+    } else if (row == 0 && tid < p.S * (PART / 8)) {
+      tok = load_call_token(p, D, b, g, tid / (PART / 8), quarter * (PART / 8) + tid % (PART / 8));
+    }
+  }
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
     merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r);
   }
-  if (MODE == MODE_GLOBAL && p.append) store_call_token<FP8>(p, D, b, g, tok);
+  if (MODE == MODE_GLOBAL && p.append) {
+    if constexpr (FP8) {
+      store_call_token_code(p, D, b, g, tcode);
+      // rows * kMergeThreads < tok_values: the rest in turn
+      for (int k = tid + kMergeThreads; k < per; k += kMergeThreads)
+        if (row * per + k < tok_values)
+          store_call_token_code(p, D, b, g, load_call_token_code(p, D, PART, quarter, b, g, row * per + k));
+    } else {
+      store_call_token(p, D, b, g, tok);
+    }
+  }
   if (tid - grp * TPG == 0) {
     gml[grp][0] = r.M;
     gml[grp][1] = r.L;
@@ -762,15 +847,21 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
   const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
 
-  // the call's tokens: thread d/8 of row 0 (of each unit) takes head dims
-  // d .. d+7 of every token, one token per loop
+  // the call's tokens: bf16, thread d/8 of row 0 (of each unit) takes head
+  // dims d .. d+7 of every token, one token per loop; fp8, the unit's
+  // threads take the 2*S*D values in turn, one per thread at a time
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
     merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r);
   }
-  if (MODE == MODE_GLOBAL && p.append && row == 0 && d % 8 == 0) {
-    for (int j = 0; j < p.S; ++j) store_call_token<FP8>(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
+  if (MODE == MODE_GLOBAL && p.append) {
+    if constexpr (FP8) {
+      for (int v = rem; v < 2 * p.S * D; v += per_unit)
+        store_call_token_code(p, D, b, g, load_call_token_code(p, D, D, 0, b, g, v));
+    } else if (row == 0 && d % 8 == 0) {
+      for (int j = 0; j < p.S; ++j) store_call_token(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
+    }
   }
   store_row4(p, D, b, g, row, d, r.L, r.O);
 }

@@ -153,17 +153,31 @@ __device__ __forceinline__ void store_token_piece(__amdgpu_buffer_rsrc_t rk, __a
   }
 }
 
-// The bf16 values an fp8 region holds for bf16 x after a store: the E4M3
-// codes of x/scale, decoded (in units of scale).
-__device__ __forceinline__ __bf16 fp8_stored_value(__bf16 x, float scale) {
-  return fp8x8_to_bf16x8(u32x2{(uint32_t)e4m3_encode((float)x, scale), 0u})[0];
+// Writes the E4M3 code of one head dim d of one token (K if !is_v, else V)
+// into slot `slot` of KV head g of an fp8 region storing S slots per head:
+// one byte, at the place store_token_piece puts it.
+__device__ __forceinline__ void store_token_code(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int slot,
+                                                 int g, int S, int D, int d, bool is_v, uint8_t code) {
+  if (!is_v) {
+    const int k32 = slot & 31;
+    store1(rk, k_half_base(g, S, slot & ~31, (k32 >> 2) & 1, D, 1) + k_granule_offset(d >> 4, 4 * (k32 >> 3) + (k32 & 3)) +
+                   (uint32_t)(d & 15), code);
+  } else {
+    store1(rv, (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * D + (size_t)d) * 8 + (size_t)(slot & 7)), code);
+  }
 }
 
-__device__ __forceinline__ bf16x8 fp8_stored_values(bf16x8 x, float scale) {
-  u32x2 c = {0u, 0u};
+// The bf16 values an fp8 region holds for four bf16 values (bits, two per
+// word) after a store: the E4M3 codes of x/scale, decoded (in units of
+// scale).
+__device__ __forceinline__ u32x2 fp8_stored_values4(u32x2 x, float scale) {
+  uint32_t c = 0u;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e >> 2] |= (uint32_t)e4m3_encode((float)x[e], scale) << (8 * (e & 3));
-  return fp8x8_to_bf16x8(c);
+  for (int e = 0; e < 4; ++e)
+    c |= (uint32_t)e4m3_encode(__builtin_bit_cast(float, ((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16), scale)
+         << (8 * e);
+  const u32x4 v = __builtin_bit_cast(u32x4, fp8x8_to_bf16x8(u32x2{c, 0u}));
+  return u32x2{v[0], v[1]};
 }
 
 // Waits until every vector memory access the wave has issued is complete,

@@ -83,15 +83,17 @@ def test_fp8_decode_batch_shape():
 
 
 def test_fp8_every_bf16_value():
-    # all 65536 bf16 patterns except NaNs through the device encoder, scale 1 and an
-    # arbitrary one: 256 tokens x 256 dims of one request
+    # all 65536 bf16 patterns except NaNs through the device encoder, at scale
+    # 1, arbitrary scales, the smallest positive fp32 (a subnormal scale) and
+    # scales near both ends of the fp32 range: 256 tokens x 256 dims of one
+    # request
     allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     allb = allb[~np.isnan(synthetic.bf16_to_f32(allb))]
     n = allb.size
     pad = (-n) % 256
     vals = np.concatenate([allb, np.zeros(pad, np.uint16)]).reshape(1, -1, 1, 256)
     T = vals.shape[1]
-    for s in (1.0, 0.37):
+    for s in (1.0, 0.37, 0.0123, 2.0 ** -149, 1e-30, 3e37, 3.4028235e38):
         rb = oracle.region_bytes(256, 1, 256, oracle.FP8)
         kp = np.zeros(rb, np.uint8)
         vp = np.zeros(rb, np.uint8)

@@ -212,6 +212,22 @@ def test_fused_global_shapes(S, G, D, dtype):
 
 
 @pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("S,G,D", [(1, 16, 128), (8, 4, 128), (3, 4, 256), (2, 4, 64)])
+def test_fused_global_many_chunks(S, G, D, dtype):
+    # more than 16 chunks of 128 keys: the merge pass that groups chunks per
+    # row, which also stores the call's tokens (over fp8, one value per
+    # thread across the row workgroups)
+    kc = np.array([S, 2100, 2300 + S], np.int32)
+    B = kc.size
+    g = synthetic.rng(76)
+    x = dict(key_count=kc, k=synthetic.normal_bf16(g, (B, 2560, 2, D)),
+             v=quarter_scale(synthetic.normal_bf16(g, (B, 2560, 2, D))), q=synthetic.normal_bf16(g, (B, S, 2 * G, D)))
+    ks, vs = (3.1 / 448, 0.9 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    out, ref = fused_global_case(x, S, 2560, dtype, ks, vs)
+    assert_parity(host_f64(out), ref, f"fused global, many chunks, S={S} G={G} D={D}")
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
 def test_fused_global_per_request_capacities(dtype):
     S, G, D = 4, 8, 512
     kc = np.array([4, 67, 640, 1500], np.int32)
