@@ -66,6 +66,7 @@ attn_kernel(const AttnParams p) {
   constexpr int RS = D + 4;         // padded LDS row stride (floats)
   constexpr bool DEC = MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND;
   constexpr bool APP = MODE == MODE_DECODE_APPEND;
+  static_assert(!(APP && FP8) || DS <= 256, "an fp8 append writes a slice's K and V from one wave's lanes");
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
@@ -316,13 +317,15 @@ attn_kernel(const AttnParams p) {
     if (x >= nt) x -= nt;
     return t_begin + x;
   };
+  // fp8: lane l < DS/8 encodes K dims 8*(d_base/8 + l) .. +7 and lane
+  // DS/8 + l the same dims of V, which halves the chain of encodes a lane runs
   auto write_new = [&]() {
-    if (FIRST && lane < DS / 8) {
-      const int d8 = d_base / 8 + lane;
+    if (FIRST && lane < DS / 4) {
+      const bool is_v = lane >= DS / 8;
+      const int d8 = d_base / 8 + lane - (is_v ? DS / 8 : 0);
       const size_t src = ((size_t)b * Hkv + g) * D + (size_t)d8 * 8;
-      const u32x4 kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
-      const u32x4 vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
-      store_token_piece<FP8>(rk, rv, slot_new, g, S_r, D, d8, kbits, vbits, p.k_scale_store, p.v_scale_store);
+      const u32x4 bits = *reinterpret_cast<const u32x4*>((is_v ? p.v_prop : p.k_prop) + src);
+      store_token_half_fp8(rk, rv, slot_new, g, S_r, D, d8, is_v, bits, is_v ? p.v_scale_store : p.k_scale_store);
     }
   };
 

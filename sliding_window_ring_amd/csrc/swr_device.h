@@ -153,6 +153,32 @@ __device__ __forceinline__ void store_token_piece(__amdgpu_buffer_rsrc_t rk, __a
   }
 }
 
+// Writes the E4M3 codes of head dims 8*d8 .. 8*d8+7 of one token's K (if
+// !is_v) or V (bf16 bits, two per word) into slot `slot` of KV head g of an
+// fp8 region storing S slots per head, where store_token_piece puts them:
+// half of that call's encodes, so that two lanes can share a piece.
+__device__ __forceinline__ void store_token_half_fp8(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int slot,
+                                                     int g, int S, int D, int d8, bool is_v, u32x4 bits,
+                                                     float scale) {
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    c[e >> 2] |= (uint32_t)e4m3_encode(__builtin_bit_cast(float, ((bits[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) << 16),
+                                       scale)
+                 << (8 * (e & 3));
+  if (!is_v) {
+    const int k32 = slot & 31;
+    store8(rk, k_half_base(g, S, slot & ~31, (k32 >> 2) & 1, D, 1) + k_granule_offset(d8 >> 1, 4 * (k32 >> 3) + (k32 & 3)) +
+                   (uint32_t)((d8 & 1) * 8),
+           u32x2{c[0], c[1]});
+  } else {
+    const uint32_t vrow = (uint32_t)((((size_t)g * (S >> 3) + (size_t)(slot >> 3)) * D + (size_t)d8 * 8) * 8 +
+                                     (size_t)(slot & 7));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store1(rv, vrow + 8 * e, (uint8_t)(c[e >> 2] >> (8 * (e & 3))));
+  }
+}
+
 // Writes the E4M3 code of one head dim d of one token (K if !is_v, else V)
 // into slot `slot` of KV head g of an fp8 region storing S slots per head:
 // one byte, at the place store_token_piece puts it.
