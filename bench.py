@@ -14,8 +14,9 @@ stream comes from HBM and not from the 256 MB Infinity Cache.
 Prints one JSON line: aggregate algorithmic K/V GB/s of the step, us/layer of
 each layer type, the roofline of the dominant kernel (the sliding decode),
 the chip's measured streaming-read ceiling, the other workloads (sliding
-verify, fp8 decode, the mixed step, a 60-layer decode stack, the global
-key-count sweep) and the oracle's rate on the host cores as a CPU baseline.
+verify, fp8 decode, the paged-cache baseline of the decode, the mixed step,
+a 60-layer decode stack, the global key-count sweep) and the oracle's rate
+on the host cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-extra] [--no-sweep]
@@ -184,6 +185,73 @@ def _timed(torch, fn, reps, sets):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def paged_baseline(swr, torch, randn, gen, dev, page_tokens=16):
+    """The B=56 decode over a paged cache: per step, swr_paged_gather_window
+    copies each request's window out of its pages (ids shuffled over the
+    pool) into a ring-layout workspace, and swr_swa_decode reads it.  Only the
+    pages that hold window positions are allocated."""
+    import numpy as np
+    import synthetic
+    w = synthetic.SWA_DECODE
+    sets = []
+    for _ in range(2):
+        pos = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+        ph = pos.cpu().numpy().astype(np.int64)
+        first, last = np.maximum(ph - w.W + 1, 0) // page_tokens, ph // page_tokens
+        n_pages = int((last - first + 1).sum())
+        ids = torch.randperm(n_pages, generator=torch.Generator().manual_seed(int(ph.sum()))).numpy()
+        bt = np.full((w.B, int(last.max()) + 1), -1, np.int32)
+        k = 0
+        for b in range(w.B):
+            n = int(last[b] - first[b] + 1)
+            bt[b, first[b]:last[b] + 1] = ids[k:k + n]
+            k += n
+        kp = randn(n_pages, page_tokens, w.Hkv, w.D)
+        vp = randn(n_pages, page_tokens, w.Hkv, w.D)
+        rb = swr.region_bytes(w.W, w.Hkv, w.D)
+        kb = torch.zeros(w.B * rb, dtype=torch.uint8, device=dev)
+        vb = torch.zeros_like(kb)
+        off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+        L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
+        q = randn(w.B, w.Hq, w.D)
+        sets.append((kp, vp, torch.from_numpy(bt).to(dev), pos, L, q, torch.empty_like(q)))
+    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W)),
+                     dtype=torch.uint8, device=dev)
+
+    def gather(i):
+        s = sets[i]
+        swr.paged_gather_window(s[0], s[1], s[2], s[3], s[4])
+
+    def decode(i):
+        s = sets[i]
+        swr.swa_decode(s[4], s[5], s[3], w.Hkv, w.D ** -0.5, out=s[6], ws=ws)
+
+    def both(i):
+        gather(i)
+        decode(i)
+
+    # reference for the gather's rate: torch's device copy of as many bytes
+    src = torch.empty(w.B * w.Hkv * w.W * w.D * 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+
+    def copy(i):
+        dst.copy_(src)
+
+    us_g = _timed(torch, gather, 60, len(sets))
+    us_d = _timed(torch, decode, 60, len(sets))
+    us = _timed(torch, both, 60, len(sets))
+    us_c = _timed(torch, copy, 30, 1)
+    kv = w.B * w.Hkv * w.W * w.D * 2 * 2
+    nbytes = kv + 2 * w.B * w.Hq * w.D * 2
+    return {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
+            "hbm_peak_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "gather_us": round(us_g, 2), "gather_GB/s_moved": round(2 * kv / us_g / 1e3, 1),
+            "torch_copy_same_bytes_GB/s_moved": round(2 * kv / (2 * us_c) / 1e3, 1),
+            "decode_on_gathered_ring_us": round(us_d, 2), "page_tokens": page_tokens,
+            "note": "the same decode kernel after a gather of each window's pages (read and written once more); "
+                    "GB/s and hbm_peak_frac count the decode's algorithmic bytes over gather + decode"}
+
+
 def read_ceiling(swr, torch):
     """Achievable HBM read rate on this chip: the library's plain streaming
     read (swr_read_ceiling) over 2 GiB, alternating two buffers so that no
@@ -291,9 +359,10 @@ def decode_stack(swr, torch, randn, dev):
 
 def other_workloads(swr, torch, sweep=True):
     """The remaining workloads, each timed on its own (us per call, GB/s of
-    algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the mixed
-    16-request step (bf16 and fp8, rings and global regions in one pool), and
-    the global verify over every key count 4000..8192."""
+    algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the B=56
+    decode over a paged cache (gather, then the decode), the mixed 16-request
+    step (bf16 and fp8, rings and global regions in one pool), and the global
+    verify over every key count 4000..8192."""
     import synthetic
 
     dev = torch.device("cuda", 0)
@@ -375,6 +444,11 @@ def other_workloads(swr, torch, sweep=True):
     res["sliding_decode_b56_fp8_append_and_attention"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                                                           "algorithmic_bytes": nbytes}
     del sets
+
+    # --- the paged-cache baseline of the same B=56 decode: each request's
+    # window in 16-token pages scattered over a page pool, gathered into a
+    # ring-layout workspace every step, then the same decode kernel
+    res["sliding_decode_b56_paged_gather_baseline"] = paged_baseline(swr, torch, randn, gen, dev)
 
     # --- mixed step: 16 requests, contexts log-uniform [512, 65536], one pool
     ctx = [int(c) for c in synthetic.mixed_contexts()]

@@ -277,6 +277,32 @@ swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_fr
  * memset node, so it may be captured into a graph). */
 swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
 
+/* ------------------------------------------------------ paged baseline */
+
+/* The paged-cache path the ring replaces ([Gaudi] "Expensive KV gathers":
+ * a sliding-window layer over a paged cache first gathers the window's
+ * pages into a contiguous buffer each step).  Copies request b's window --
+ * the positions max(0, pos[b]-W+1) .. pos[b] -- from its pages into ring
+ * slot position mod W of `ring`, the layout swr_swa_decode reads, so that
+ * a gather followed by swr_swa_decode computes what the ring computes after
+ * swr_kv_append.  Slots that hold no window position (pos[b] < W-1) and
+ * slots whose page is missing keep what they held.
+ *   k_pages, v_pages : device bf16 [n_pages][page_tokens][Hkv][D] (16-B
+ *                      aligned): the token at position p of request b is row
+ *                      p mod page_tokens of page block_table[b][p / page_tokens]
+ *   block_table      : device int32 [B][max_pages]; an entry outside
+ *                      0 .. n_pages-1, or a page index >= max_pages, is a
+ *                      missing page (its slots are skipped, nothing is read)
+ *   pos              : device int32 [B] (a negative entry skips the request)
+ *   ring             : bf16 ring regions (ring->cap = W, cap_b NULL)
+ * Errors: SWR_ERR_INVALID for null or misaligned pointers, B < 0, Hkv < 1,
+ * n_pages, page_tokens or max_pages < 1, or cap_b set; SWR_ERR_UNSUPPORTED
+ * for an fp8 ring or D outside {64, 128, 256, 512}.  B == 0 is a no-op. */
+swr_status swr_paged_gather_window(const void* k_pages, const void* v_pages, int64_t n_pages,
+                                   int page_tokens, const int32_t* block_table, int max_pages,
+                                   const int32_t* pos, const swr_kv* ring, int B, int Hkv, int D,
+                                   hipStream_t stream);
+
 /* Measurement aid, outside the attention path: one streaming read of `bytes`
  * (a multiple of 16, at most 2^40) of device memory at `src` (16-byte
  * aligned) by `grid` workgroups (1 .. 65536) of 256 threads on `stream`.

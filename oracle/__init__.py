@@ -189,6 +189,39 @@ def kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, k_scale, v_scale, k_new,
     _check_rc(rc, "kv_append")
 
 
+def paged_gather_window(k_pool, v_pool, k_off, v_off, W, k_pages, v_pages, block_table, pos):
+    """The paged-cache gather that a sliding-window layer needs when its KV
+    lives in scattered pages ("Improving Decode Throughput on Intel Gaudi 3",
+    "Expensive KV gathers"), into bf16 ring regions, in place.
+
+    Request b's window is the positions max(0, pos[b]-W+1) .. pos[b]; the
+    token at position p is row p mod page_tokens of page
+    block_table[b][p // page_tokens] of k_pages / v_pages (bf16 bits
+    [n_pages][page_tokens][Hkv][D]).  Each is written to ring slot p mod W by
+    kv_append; a position whose page index is past the table or whose entry
+    is not a page of the pool is skipped, as is a request with pos < 0.
+    """
+    k_pages = np.asarray(k_pages, np.uint16)
+    v_pages = np.asarray(v_pages, np.uint16)
+    n_pages, pt, hkv, d = k_pages.shape
+    bt = np.asarray(block_table, np.int64)
+    pos = np.asarray(pos, np.int64)
+    k_off = np.asarray(k_off, np.int64)
+    v_off = np.asarray(v_off, np.int64)
+    for b in range(pos.shape[0]):
+        P = int(pos[b])
+        if P < 0:
+            continue
+        for p in range(max(0, P - W + 1), P + 1):
+            i = p // pt
+            if i >= bt.shape[1] or not 0 <= bt[b, i] < n_pages:
+                continue
+            page, row = int(bt[b, i]), p % pt
+            kv_append(k_pool, v_pool, k_off[b:b + 1], v_off[b:b + 1], W, BF16, 1.0, 1.0,
+                      k_pages[page, row][None, None], v_pages[page, row][None, None],
+                      np.array([p], np.int32))
+
+
 def swa_decode(k_pool, v_pool, k_off, v_off, W, dtype, k_scale, v_scale, q, pos, hkv, scale):
     """Sliding-window decode over each request's ring, read in storage order.
 

@@ -33,7 +33,8 @@ EXPORTS = [
     "swr_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
     "swr_global_append_attend", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
-    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_read_ceiling", "swr_status_string",
+    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_paged_gather_window", "swr_read_ceiling",
+    "swr_status_string",
 ]
 
 
@@ -77,6 +78,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                ctypes.POINTER(ctypes.c_int32)], I),
         "swr_pool_stats": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I),
         "swr_zero_fill": ([P, SZ, P], I),
+        "swr_paged_gather_window": ([P, P, I64, I, P, I, P, KV, I, I, I, P], I),
         "swr_read_ceiling": ([P, SZ, P, I, I, P], I),
         "swr_status_string": ([I], ctypes.c_char_p),
     }
@@ -170,6 +172,26 @@ def kv_append(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch
     _check("swr_kv_append", lib.swr_kv_append(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(pos0),
                                               _ptr(n_new), B, T, hkv, d, 1 if wrap else 0,
                                               _stream(stream)))
+
+
+def paged_gather_window(k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                        pos: torch.Tensor, ring: KVLayer, stream=None) -> None:
+    """swr_paged_gather_window: k_pages, v_pages bf16 [n_pages][page_tokens][Hkv][D];
+    block_table int32 [B][max_pages]; pos int32 [B]."""
+    _dev(k_pages, "k_pages", torch.bfloat16)
+    _dev(v_pages, "v_pages", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(pos, "pos", torch.int32)
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must both be [n_pages][page_tokens][Hkv][D]")
+    if block_table.dim() != 2 or pos.shape != (block_table.shape[0],):
+        raise ValueError("block_table must be [B][max_pages] and pos [B]")
+    n_pages, page_tokens, hkv, d = k_pages.shape
+    B, max_pages = block_table.shape
+    _check("swr_paged_gather_window",
+           lib.swr_paged_gather_window(_ptr(k_pages), _ptr(v_pages), n_pages, page_tokens, _ptr(block_table),
+                                       max_pages, _ptr(pos), ctypes.byref(ring.c()), B, hkv, d,
+                                       _stream(stream)))
 
 
 def swa_decode(ring: KVLayer, q: torch.Tensor, pos: torch.Tensor, hkv: int, scale: float,

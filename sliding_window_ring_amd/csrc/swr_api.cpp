@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 
+#include "gather.h"
 #include "swr.h"
 #include "swr_internal.h"
 
@@ -253,6 +254,40 @@ swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return SWR_OK;
   if (!ptr) return SWR_ERR_INVALID;
   return to_status(swr::launch_zero_fill(ptr, bytes, stream));
+}
+
+swr_status swr_paged_gather_window(const void* k_pages, const void* v_pages, int64_t n_pages, int page_tokens,
+                                   const int32_t* block_table, int max_pages, const int32_t* pos,
+                                   const swr_kv* ring, int B, int Hkv, int D, hipStream_t stream) {
+  if (B < 0 || Hkv < 1 || D < 1 || n_pages < 1 || page_tokens < 1 || max_pages < 1) return SWR_ERR_INVALID;
+  if (!supported_d(D)) return SWR_ERR_UNSUPPORTED;
+  swr_status st = check_kv(ring, Hkv, D);
+  if (st != SWR_OK) return st;
+  if (ring->cap_b) return SWR_ERR_INVALID;                  // rings share one window
+  if (ring->dtype != SWR_KV_BF16) return SWR_ERR_UNSUPPORTED;
+  if (!k_pages || !v_pages || !block_table || !pos || !aligned16(k_pages) || !aligned16(v_pages))
+    return SWR_ERR_INVALID;
+  if ((int64_t)B * max_pages > INT32_MAX) return SWR_ERR_UNSUPPORTED;
+  const int64_t threads = (int64_t)B * Hkv * (ring->cap / 8) * (D / 8);
+  if ((threads + 255) / 256 > INT32_MAX) return SWR_ERR_UNSUPPORTED;
+  if (B == 0) return SWR_OK;
+  swr::GatherArgs a{};
+  a.k_pages = static_cast<const uint16_t*>(k_pages);
+  a.v_pages = static_cast<const uint16_t*>(v_pages);
+  a.block_table = block_table;
+  a.pos = pos;
+  a.k_base = static_cast<uint8_t*>(ring->k_base);
+  a.v_base = static_cast<uint8_t*>(ring->v_base);
+  a.k_off = ring->k_off;
+  a.v_off = ring->v_off;
+  a.n_pages = n_pages;
+  a.page_tokens = page_tokens;
+  a.max_pages = max_pages;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.W = ring->cap;
+  return to_status(swr::launch_paged_gather(a, stream));
 }
 
 swr_status swr_read_ceiling(const void* src, size_t bytes, void* sink, int grid, int pattern,

@@ -181,6 +181,28 @@ def test_read_ceiling_validation():
     assert f(FAKE, 0, FAKE, 256, 0, None) == OK                 # nothing to read, no launch
 
 
+def gather(ring=None, kp=FAKE, vp=FAKE, n_pages=4096, pt=16, bt=FAKE, max_pages=257, pos=FAKE, B=56, Hkv=8,
+           D=256):
+    r = kv() if ring is None else ring
+    return swr.lib.swr_paged_gather_window(kp, vp, n_pages, pt, bt, max_pages, pos, ctypes.byref(r), B, Hkv, D,
+                                           None)
+
+
+def test_paged_gather_validation():
+    for bad in (dict(kp=None), dict(vp=None), dict(bt=None), dict(pos=None), dict(kp=FAKE + 8),
+                dict(vp=FAKE + 2), dict(n_pages=0), dict(pt=0), dict(max_pages=0), dict(B=-1), dict(Hkv=0)):
+        assert gather(**bad) == INVALID, bad
+    assert gather(D=96) == UNSUPPORTED
+    assert gather(ring=kv(dtype=1)) == UNSUPPORTED         # bf16 rings only
+    assert gather(ring=kv(cap=1020)) == INVALID            # window not a multiple of 8
+    r = kv()
+    r.cap_b = FAKE
+    assert gather(ring=r) == INVALID                       # rings share one window
+    assert swr.lib.swr_paged_gather_window(FAKE, FAKE, 4096, 16, FAKE, 257, FAKE, None, 56, 8, 256,
+                                           None) == INVALID
+    assert gather(B=0) == OK                               # nothing to gather, no launch
+
+
 def test_zero_batch_attention_is_a_no_op():
     assert decode(B=0) == OK
 

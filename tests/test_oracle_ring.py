@@ -121,3 +121,91 @@ def test_fp8_append_stores_encoded_codes():
         s = (14 + t) % W
         assert np.array_equal(K[s], oracle.e4m3_encode(k[0, t], ks))
         assert np.array_equal(V[s], oracle.e4m3_encode(v[0, t], vs))
+
+
+def scatter_to_pages(tokens_k, tokens_v, pt, rng, spare=3):
+    """Lays out each request's token sequence ([B][n][Hkv][D] bits) in pages of
+    pt tokens whose ids are shuffled over the pool (with `spare` unused
+    pages): page block_table[b][i] holds positions pt*i .. pt*i+pt-1."""
+    B, n, hkv, d = tokens_k.shape
+    per = -(-n // pt)
+    ids = rng.permutation(B * per + spare)
+    bt = ids[:B * per].reshape(B, per).astype(np.int32)
+    kp = np.zeros((B * per + spare, pt, hkv, d), np.uint16)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for p in range(n):
+            kp[bt[b, p // pt], p % pt] = tokens_k[b, p]
+            vp[bt[b, p // pt], p % pt] = tokens_v[b, p]
+    return kp, vp, bt
+
+
+@pytest.mark.parametrize("W,pt,pos", [(16, 4, [3, 15, 16, 37]), (32, 16, [0, 31, 45, 100]), (64, 16, [63, 64, 65, 130])])
+def test_paged_gather_puts_each_window_position_in_its_slot(W, pt, pos):
+    # "Improving Decode Throughput on Intel Gaudi 3" (Expensive KV gathers):
+    # the window of the query at pos, read from pages, lands where the ring
+    # keeps it; the slots read back through the layout views above
+    hkv, d, B = 2, 32, len(pos)
+    n = max(pos) + 1
+    # position p of request b carries (p + 1) * 2^b: exact in bf16, distinct per request
+    vals = np.arange(1, n + 1, dtype=np.float32)[None, :, None, None] * 2.0 ** np.arange(B)[:, None, None, None]
+    tk = synthetic.bf16_bits(np.broadcast_to(vals, (B, n, hkv, d)))
+    tv = synthetic.bf16_bits(-np.broadcast_to(vals, (B, n, hkv, d)))
+    kp, vp, bt = scatter_to_pages(tk, tv, pt, np.random.default_rng(5))
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    kpool = np.zeros(B * rb, np.uint8)
+    vpool = np.zeros(B * rb, np.uint8)
+    off = np.arange(B, dtype=np.int64) * rb
+    oracle.paged_gather_window(kpool, vpool, off, off, W, kp, vp, bt, np.array(pos, np.int32))
+    for b, P in enumerate(pos):
+        kv = f64(k_view(kpool, int(off[b]), W, hkv, d))
+        vv = f64(v_view(vpool, int(off[b]), W, hkv, d))
+        for s in range(W):
+            p = P - ((P - s) % W)
+            want = (p + 1) * 2.0 ** b if p >= 0 else 0.0
+            assert np.all(kv[s] == want), (b, s)
+            assert np.all(vv[s] == -want if p >= 0 else vv[s] == 0.0), (b, s)
+
+
+def test_paged_gather_equals_appending_the_window():
+    # the same rings as appending each request's last W tokens in order
+    W, pt, hkv, d = 32, 16, 2, 64
+    g = synthetic.rng(41)
+    pos = np.array([5, 40, 95], np.int32)
+    B, n = pos.size, int(pos.max()) + 1
+    tk = synthetic.normal_bf16(g, (B, n, hkv, d))
+    tv = synthetic.normal_bf16(g, (B, n, hkv, d))
+    kp, vp, bt = scatter_to_pages(tk, tv, pt, np.random.default_rng(6))
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    off = np.arange(B, dtype=np.int64) * rb
+    got_k, got_v = np.zeros(B * rb, np.uint8), np.zeros(B * rb, np.uint8)
+    oracle.paged_gather_window(got_k, got_v, off, off, W, kp, vp, bt, pos)
+    want_k, want_v = np.zeros(B * rb, np.uint8), np.zeros(B * rb, np.uint8)
+    for b in range(B):
+        lo = max(0, int(pos[b]) - W + 1)
+        oracle.kv_append(want_k, want_v, off[b:b + 1], off[b:b + 1], W, oracle.BF16, 1.0, 1.0,
+                         tk[b:b + 1, lo:pos[b] + 1], tv[b:b + 1, lo:pos[b] + 1], np.array([lo], np.int32))
+    assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
+
+
+def test_paged_gather_skips_missing_pages():
+    W, pt, hkv, d = 16, 4, 1, 32
+    n = 20
+    vals = np.arange(1, n + 1, dtype=np.float32)[None, :, None, None]
+    tk = synthetic.bf16_bits(np.broadcast_to(vals, (1, n, hkv, d)))
+    kp, vp, bt = scatter_to_pages(tk, tk, pt, np.random.default_rng(7), spare=0)
+    bt = bt.copy()
+    bt[0, 2] = -1               # positions 8..11
+    bt[0, 3] = kp.shape[0] + 4  # positions 12..15: not a page of the pool
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    kpool = np.full(rb, 0x11, np.uint8)
+    vpool = np.full(rb, 0x11, np.uint8)
+    off = np.zeros(1, np.int64)
+    oracle.paged_gather_window(kpool, vpool, off, off, W, kp, vp, bt[:, :4], np.array([19], np.int32))
+    kv = k_view(kpool, 0, W, hkv, d)
+    for p in range(4, 20):
+        s = p % W
+        if 8 <= p < 20:  # pages 2, 3 missing; page 4 is past the table's 4 columns
+            assert np.all(kv[s] == 0x1111), p
+        else:
+            assert np.all(f64(kv[s]) == p + 1), p
