@@ -273,6 +273,37 @@ swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dty
 /* Bytes in use and the largest free range. */
 swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_free);
 
+/* Admission of one request ([Gaudi] "Patching sliding window KV
+ * allocation": a sliding layer only ever reads its last W tokens, so it
+ * keeps W slots however long the request grows, and only the global layers
+ * take KV in proportion to the context).  Carves, all or nothing, a K and a
+ * V region for each of n_sliding rings of W slots (cap W rounded up to 8,
+ * shape Hkv_s x D_s) and each of n_global global regions of `context`
+ * tokens (cap rounded up to 64, shape Hkv_g x D_g), all of element type
+ * dtype.
+ *   k_off, v_off : host int64 [n_sliding + n_global] (out), sliding layers
+ *                  first, in layer order
+ *   global_cap   : host int32 (out): the global regions' cap (may be NULL
+ *                  when n_global == 0)
+ * SWR_ERR_NOMEM when the request does not fit; the pool is then as before
+ * the call.  SWR_ERR_INVALID for a null pool or output, negative layer
+ * counts, no layer at all, context < 1 or an invalid shape.  The caller zero
+ * fills the regions before first use (swr_zero_fill). */
+swr_status swr_pool_admit(swr_pool* pool, int n_sliding, int W, int Hkv_s, int D_s, int n_global,
+                          int context, int Hkv_g, int D_g, int dtype, int64_t* k_off, int64_t* v_off,
+                          int32_t* global_cap);
+/* Releases the n K and n V ranges of a request (as filled by
+ * swr_pool_admit); SWR_ERR_INVALID if any offset was not allocated (the
+ * others are still released). */
+swr_status swr_pool_release(swr_pool* pool, int n, const int64_t* k_off, const int64_t* v_off);
+/* Region bytes (K and V of every layer, before the pool's 256-byte
+ * alignment) that swr_pool_admit carves for one request, or, with
+ * full_context != 0, what a cache that keeps the full context in every
+ * layer (sliding ones included) would carve: the two admission policies the
+ * page compares.  -1 for an invalid shape. */
+int64_t swr_request_kv_bytes(int n_sliding, int W, int Hkv_s, int D_s, int n_global, int context,
+                             int Hkv_g, int D_g, int dtype, int full_context);
+
 /* Zero `bytes` of device memory at `ptr` with a kernel on `stream` (no
  * memset node, so it may be captured into a graph). */
 swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream);

@@ -33,7 +33,8 @@ EXPORTS = [
     "swr_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
     "swr_global_append_attend", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
-    "swr_pool_alloc_kv", "swr_pool_stats", "swr_zero_fill", "swr_paged_gather_window", "swr_read_ceiling",
+    "swr_pool_alloc_kv", "swr_pool_stats", "swr_pool_admit", "swr_pool_release", "swr_request_kv_bytes",
+    "swr_zero_fill", "swr_paged_gather_window", "swr_read_ceiling",
     "swr_status_string",
 ]
 
@@ -77,6 +78,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "swr_pool_alloc_kv": ([P, I, I, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                ctypes.POINTER(ctypes.c_int32)], I),
         "swr_pool_stats": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I),
+        "swr_pool_admit": ([P, I, I, I, I, I, I, I, I, I, P, P, ctypes.POINTER(ctypes.c_int32)], I),
+        "swr_pool_release": ([P, I, P, P], I),
+        "swr_request_kv_bytes": ([I, I, I, I, I, I, I, I, I, I], I64),
         "swr_zero_fill": ([P, SZ, P], I),
         "swr_paged_gather_window": ([P, P, I64, I, P, I, P, KV, I, I, I, P], I),
         "swr_read_ceiling": ([P, SZ, P, I, I, P], I),
@@ -307,6 +311,14 @@ def read_ceiling(src: torch.Tensor, sink: torch.Tensor, grid: int, pattern: int 
                                                     _stream(stream)))
 
 
+def request_kv_bytes(n_sliding: int, W: int, hkv_s: int, d_s: int, n_global: int, context: int, hkv_g: int,
+                     d_g: int, dtype: int = SWR_KV_BF16, full_context: bool = False) -> int:
+    """swr_request_kv_bytes: one request's region bytes under ring admission,
+    or with every layer at full context."""
+    return int(lib.swr_request_kv_bytes(n_sliding, W, hkv_s, d_s, n_global, context, hkv_g, d_g, dtype,
+                                        1 if full_context else 0))
+
+
 class Pool:
     """Host bookkeeping (swr_pool_*) over one device byte buffer shared by
     ring and global regions ("Improving Decode Throughput on Intel Gaudi 3",
@@ -338,6 +350,30 @@ class Pool:
             zero_fill(self.buffer, ko.value, rb, stream)
             zero_fill(self.buffer, vo.value, rb, stream)
         return ko.value, vo.value, cap.value
+
+    def admit(self, n_sliding: int, W: int, hkv_s: int, d_s: int, n_global: int, context: int, hkv_g: int,
+              d_g: int, dtype: int = SWR_KV_BF16, zero: bool = True, stream=None):
+        """swr_pool_admit: one request's rings and global regions, all or
+        nothing; zero-fills them on the stream.  Returns (k_offsets,
+        v_offsets, global_cap), sliding layers first."""
+        n = n_sliding + n_global
+        ko, vo, gcap = (ctypes.c_int64 * max(n, 1))(), (ctypes.c_int64 * max(n, 1))(), ctypes.c_int32(0)
+        _check("swr_pool_admit", lib.swr_pool_admit(self._h, n_sliding, W, hkv_s, d_s, n_global, context, hkv_g,
+                                                    d_g, dtype, ko, vo, ctypes.byref(gcap)))
+        if zero:
+            for i in range(n):
+                glob = i >= n_sliding
+                rb = region_bytes(gcap.value if glob else -(-W // 8) * 8, hkv_g if glob else hkv_s,
+                                  d_g if glob else d_s, dtype)
+                zero_fill(self.buffer, ko[i], rb, stream)
+                zero_fill(self.buffer, vo[i], rb, stream)
+        return list(ko[:n]), list(vo[:n]), gcap.value
+
+    def release(self, k_offsets, v_offsets) -> None:
+        """swr_pool_release: the ranges of a request admitted by admit()."""
+        n = len(k_offsets)
+        _check("swr_pool_release", lib.swr_pool_release(self._h, n, (ctypes.c_int64 * max(n, 1))(*k_offsets),
+                                                        (ctypes.c_int64 * max(n, 1))(*v_offsets)))
 
     def stats(self):
         used, largest = ctypes.c_size_t(), ctypes.c_size_t()

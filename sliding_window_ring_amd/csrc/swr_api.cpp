@@ -398,6 +398,59 @@ swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dty
   return SWR_OK;
 }
 
+int64_t swr_request_kv_bytes(int n_sliding, int W, int Hkv_s, int D_s, int n_global, int context, int Hkv_g,
+                             int D_g, int dtype, int full_context) {
+  if (n_sliding < 0 || n_global < 0 || context < 1 || (n_sliding > 0 && W < 1)) return -1;
+  const int64_t ring_slots = full_context ? (int64_t)context : (int64_t)W;
+  const int64_t ring_cap = (ring_slots + 7) / 8 * 8, glob_cap = ((int64_t)context + 63) / 64 * 64;
+  if (ring_cap > INT32_MAX || glob_cap > INT32_MAX) return -1;
+  int64_t total = 0;
+  if (n_sliding > 0) {
+    const int64_t rb = swr_kv_region_bytes((int)ring_cap, Hkv_s, D_s, dtype);
+    if (rb <= 0) return -1;
+    total += 2 * rb * n_sliding;
+  }
+  if (n_global > 0) {
+    const int64_t gb = swr_kv_region_bytes((int)glob_cap, Hkv_g, D_g, dtype);
+    if (gb <= 0) return -1;
+    total += 2 * gb * n_global;
+  }
+  return total;
+}
+
+swr_status swr_pool_release(swr_pool* pool, int n, const int64_t* k_off, const int64_t* v_off) {
+  if (!pool || n < 0 || (n > 0 && (!k_off || !v_off))) return SWR_ERR_INVALID;
+  swr_status st = SWR_OK;
+  for (int i = 0; i < n; ++i) {
+    if (swr_pool_free(pool, k_off[i]) != SWR_OK) st = SWR_ERR_INVALID;
+    if (swr_pool_free(pool, v_off[i]) != SWR_OK) st = SWR_ERR_INVALID;
+  }
+  return st;
+}
+
+swr_status swr_pool_admit(swr_pool* pool, int n_sliding, int W, int Hkv_s, int D_s, int n_global, int context,
+                          int Hkv_g, int D_g, int dtype, int64_t* k_off, int64_t* v_off, int32_t* global_cap) {
+  if (!pool || n_sliding < 0 || n_global < 0 || n_sliding + n_global < 1 || context < 1) return SWR_ERR_INVALID;
+  if (!k_off || !v_off || (n_global > 0 && !global_cap)) return SWR_ERR_INVALID;
+  if (swr_request_kv_bytes(n_sliding, W, Hkv_s, D_s, n_global, context, Hkv_g, D_g, dtype, 0) < 0)
+    return SWR_ERR_INVALID;
+  int done = 0;
+  swr_status st = SWR_OK;
+  int32_t cap = 0;
+  for (; done < n_sliding + n_global; ++done) {
+    const bool glob = done >= n_sliding;
+    st = swr_pool_alloc_kv(pool, glob ? context : W, glob ? Hkv_g : Hkv_s, glob ? D_g : D_s, dtype, glob ? 1 : 0,
+                           &k_off[done], &v_off[done], &cap);
+    if (st != SWR_OK) break;
+    if (glob) *global_cap = cap;
+  }
+  if (st != SWR_OK) {  // all or nothing
+    swr_pool_release(pool, done, k_off, v_off);
+    return st;
+  }
+  return SWR_OK;
+}
+
 swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_free) {
   if (!pool) return SWR_ERR_INVALID;
   std::lock_guard<std::mutex> lk(pool->mu);

@@ -32,3 +32,22 @@ def test_read_ceiling_reads_and_leaves_memory_alone(grid, pattern):
     assert torch.equal(src, before)
     g = guard.cpu().numpy()
     assert np.all(g[:1024] == 0x3C) and np.all(g[2048:] == 0x3C)
+
+
+def test_pool_admit_zero_fills_each_region_and_nothing_else():
+    # one request of a small Gemma-like mix: 5 rings of 64 slots (2 x 64) and
+    # 2 global regions of a 300-token context (1 x 128) -> cap 320
+    pool = swr.Pool(8 << 20)
+    pool.buffer.fill_(0xA5)
+    ko, vo, cap = pool.admit(5, 64, 2, 64, 2, 300, 1, 128)
+    torch.cuda.synchronize()
+    assert cap == 320
+    h = pool.buffer.cpu().numpy()
+    mask = np.zeros(h.size, bool)
+    for i, (k, v) in enumerate(zip(ko, vo)):
+        rb = swr.region_bytes(64, 2, 64) if i < 5 else swr.region_bytes(320, 1, 128)
+        mask[k:k + rb] = True
+        mask[v:v + rb] = True
+    assert np.all(h[mask] == 0) and np.all(h[~mask] == 0xA5)
+    pool.release(ko, vo)
+    assert pool.stats()[0] == 0

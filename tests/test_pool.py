@@ -153,3 +153,100 @@ def test_mixed_rings_and_global_regions_share_one_pool():
     ranges.sort()
     for (s, z), (s2, _) in zip(ranges, ranges[1:]):
         assert s + z <= s2
+
+
+# --- admission ("Improving Decode Throughput on Intel Gaudi 3", Patching
+# sliding window KV allocation): sliding layers keep W slots, only global
+# layers grow with the context.  Gemma 4 31B's layer mix and shapes: 50
+# sliding layers (8 KV heads x 256, W = 1024), 10 global (2 KV heads x 512).
+GEMMA = dict(n_sliding=50, W=1024, hkv_s=8, d_s=256, n_global=10, hkv_g=2, d_g=512)
+
+
+def admit(pool, context, dtype=0, g=GEMMA):
+    n = g["n_sliding"] + g["n_global"]
+    ko, vo, cap = (ctypes.c_int64 * n)(), (ctypes.c_int64 * n)(), ctypes.c_int32(0)
+    st = swr.lib.swr_pool_admit(pool.h, g["n_sliding"], g["W"], g["hkv_s"], g["d_s"], g["n_global"], context,
+                                g["hkv_g"], g["d_g"], dtype, ko, vo, ctypes.byref(cap))
+    return st, list(ko), list(vo), cap.value
+
+
+def req_bytes(context, full, dtype=0, g=GEMMA):
+    return swr.request_kv_bytes(g["n_sliding"], g["W"], g["hkv_s"], g["d_s"], g["n_global"], context, g["hkv_g"],
+                                g["d_g"], dtype, full)
+
+
+def test_request_bytes_by_hand():
+    # bf16: a sliding token is 8 x 256 x 2 bytes of K and as much of V, a
+    # global token 2 x 512 x 2 of each
+    ring = 50 * 1024 * 8 * 256 * 2 * 2
+    glob = 10 * 4096 * 2 * 512 * 2 * 2
+    assert req_bytes(4096, False) == ring + glob == 587_202_560
+    assert req_bytes(4096, True) == 50 * 4096 * 8 * 256 * 4 + glob
+    # the global regions round the context up to 64 slots, the rings keep W
+    assert req_bytes(4000, False) == ring + 10 * 4032 * 2 * 512 * 4
+    # a context inside the window still takes the whole ring
+    assert req_bytes(100, False) == ring + 10 * 128 * 2 * 512 * 4
+    # fp8 halves every region
+    assert req_bytes(4096, False, dtype=1) * 2 == req_bytes(4096, False)
+
+
+def test_admission_ratio_at_4k_context():
+    # full-context KV per 4k request over ring admission: 3.14x with these
+    # shapes (the page reports 3.5x for its deployment without its arithmetic)
+    r = req_bytes(4096, True) / req_bytes(4096, False)
+    assert abs(r - 1_845_493_760 / 587_202_560) < 1e-12
+    assert 3.1 < r < 3.2
+
+
+def test_admit_until_full_then_release():
+    per = req_bytes(4096, False)
+    pool = Pool(per * 7 + per // 2)
+    admitted = []
+    while True:
+        used_before = pool.stats()
+        st, ko, vo, cap = admit(pool, 4096)
+        if st != 0:
+            assert st == 5  # pool exhausted
+            assert pool.stats() == used_before  # all or nothing
+            break
+        assert cap == 4096
+        admitted.append((ko, vo))
+    assert len(admitted) == 7
+    assert pool.stats()[0] == 7 * per
+    # every region is its own range: no two overlap
+    ranges = sorted((o, o) for ko, vo in admitted for o in ko + vo)
+    assert len({o for o, _ in ranges}) == 7 * 120
+    ko, vo = admitted.pop(3)
+    n = len(ko)
+    assert swr.lib.swr_pool_release(pool.h, n, (ctypes.c_int64 * n)(*ko), (ctypes.c_int64 * n)(*vo)) == 0
+    assert pool.stats()[0] == 6 * per
+    st, ko2, vo2, _ = admit(pool, 4096)  # fits again, into the freed ranges
+    assert st == 0 and sorted(ko2 + vo2) == sorted(ko + vo)
+
+
+def test_admission_fits_more_requests_than_full_context():
+    pool_bytes = 64 << 30
+    full = req_bytes(4096, True)
+    pool = Pool(pool_bytes)
+    count = 0
+    while admit(pool, 4096)[0] == 0:
+        count += 1
+    assert count == pool_bytes // req_bytes(4096, False) == 117
+    assert pool_bytes // full == 37
+
+
+def test_admit_validation():
+    pool = Pool(1 << 30)
+    n = 60
+    ko, vo, cap = (ctypes.c_int64 * n)(), (ctypes.c_int64 * n)(), ctypes.c_int32()
+    f = swr.lib.swr_pool_admit
+    assert f(None, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, -1, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, 0, 1024, 8, 256, 0, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1  # no layer
+    assert f(pool.h, 50, 1024, 8, 256, 10, 0, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1   # no context
+    assert f(pool.h, 50, 1024, 8, 0, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1   # head dim
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 7, ko, vo, ctypes.byref(cap)) == 1  # element type
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, None, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, None) == 1
+    assert pool.stats()[0] == 0
+    assert swr.lib.swr_pool_release(pool.h, 1, (ctypes.c_int64 * 1)(256), (ctypes.c_int64 * 1)(512)) == 1
