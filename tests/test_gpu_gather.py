@@ -66,7 +66,7 @@ def run_gather(W, d, hkv, pt, pos, seed, bt_edit=None):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256, 512])
-@pytest.mark.parametrize("W,pt", [(64, 16), (1024, 16), (96, 8), (256, 32)])
+@pytest.mark.parametrize("W,pt", [(64, 16), (1024, 16), (96, 8), (256, 32), (40, 16)])
 def test_gather_bytes_bit_exact(W, pt, D):
     # windows partly filled (pos < W - 1, partial 8-slot blocks), exactly
     # full, wrapped once and several times
