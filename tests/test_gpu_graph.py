@@ -127,3 +127,44 @@ def test_global_attend_in_graph():
             lambda: swr.global_attend(L, q, qp, kcs, w.key_count, w.Hkv, w.D ** -0.5, out=out_g, ws=ws),
             lambda: (out_g,), busy_work()):
         assert np.array_equal(host_bits(o), want), rep
+
+
+def test_paged_gather_then_decode_in_graph():
+    # the paged-cache baseline's two launches (gather, then the ring decode)
+    # captured together; the ring workspace starts from random bytes
+    W, hkv, d, G, pt = 256, 2, 128, 4, 16
+    pos = np.array([3, 255, 256, 700, 1000], np.int32)
+    B = pos.size
+    g = synthetic.rng(97)
+    n_pages = int((pos // pt + 1).sum()) + 3
+    kpages = dev_bf16(synthetic.normal_bf16(g, (n_pages, pt, hkv, d)))
+    vpages = dev_bf16(synthetic.normal_bf16(g, (n_pages, pt, hkv, d)))
+    per = int(pos.max()) // pt + 1
+    ids = np.random.default_rng(97).permutation(n_pages)
+    bt = np.full((B, per), -1, np.int32)
+    k = 0
+    for b in range(B):
+        n = int(pos[b]) // pt + 1
+        bt[b, :n] = ids[k:k + n]
+        k += n
+    bt, pos_d = dev_i32(bt), dev_i32(pos)
+    q = dev_bf16(synthetic.normal_bf16(g, (B, hkv * G, d)))
+    rb = oracle.region_bytes(W, hkv, d, oracle.BF16)
+    start = g.integers(0, 256, B * rb, dtype=np.uint8)
+    off = np.arange(B, dtype=np.int64) * rb
+    Le, Lg = copies(start, start, off, off, W)
+    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, hkv * G, hkv, d, W)),
+                     dtype=torch.uint8, device="cuda")  # 10 units: split-K with its combine
+    swr.paged_gather_window(kpages, vpages, bt, pos_d, Le)
+    out_e = swr.swa_decode(Le, q, pos_d, hkv, d ** -0.5, ws=ws)
+    torch.cuda.synchronize()
+    want = (host_bits(out_e), Le.k_base.cpu().numpy(), Le.v_base.cpu().numpy())
+    out_g = torch.empty_like(out_e)
+
+    def run():
+        swr.paged_gather_window(kpages, vpages, bt, pos_d, Lg)
+        swr.swa_decode(Lg, q, pos_d, hkv, d ** -0.5, out=out_g, ws=ws)
+
+    for rep, (o, kb, vb) in replay_and_check(run, lambda: (out_g, Lg.k_base, Lg.v_base), busy_work()):
+        assert np.array_equal(host_bits(o), want[0]), rep
+        assert np.array_equal(kb.cpu().numpy(), want[1]) and np.array_equal(vb.cpu().numpy(), want[2]), rep
