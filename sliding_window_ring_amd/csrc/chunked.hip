@@ -715,10 +715,11 @@ struct RunningRow {
 
 // Adds chunks c = c0 + j*step (j < kMergeBatch, c < nvalid) of the row at
 // `slot0` (+ c*rows), four dims at `d`.  On the first batch the request's
-// chunk count is read after the batch's loads are issued.
-template <int MODE>
+// chunk count is read, and `issued` runs, after the batch's loads are
+// issued: work that waits only for earlier loads then overlaps them.
+template <int MODE, typename F>
 __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, size_t slot0, int d, int c0,
-                                            int step, bool first, int& nvalid, RunningRow& r) {
+                                            int step, bool first, int& nvalid, RunningRow& r, F&& issued) {
   float m[kMergeBatch], l[kMergeBatch];
   f32x4 a[kMergeBatch];
 #pragma unroll
@@ -733,7 +734,10 @@ __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, s
       a[j] = *reinterpret_cast<const f32x4*>(p.ws_part + at * D + d);
     }
   }
-  if (first) nvalid = valid_chunks<MODE>(p, b);
+  if (first) {
+    nvalid = valid_chunks<MODE>(p, b);
+    issued();
+  }
   float mb = r.M;
 #pragma unroll
   for (int j = 0; j < kMergeBatch; ++j) mb = (c0 + j * step < nvalid) ? fmaxf(mb, m[j]) : mb;
@@ -794,21 +798,28 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
       tok = load_call_token(p, D, b, g, tid / (PART / 8), quarter * (PART / 8) + tid % (PART / 8));
     }
   }
+  bool tokens_stored = false;
+  auto store_tokens = [&] {
+    if (MODE == MODE_GLOBAL && p.append && !tokens_stored) {
+      if constexpr (FP8)
+        store_call_token_code(p, D, b, g, tcode);
+      else
+        store_call_token(p, D, b, g, tok);
+    }
+    tokens_stored = true;
+  };
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
-    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r);
+    // the tokens' stores go out once the first batch's loads are in flight
+    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r, [&] { store_tokens(); });
   }
-  if (MODE == MODE_GLOBAL && p.append) {
-    if constexpr (FP8) {
-      store_call_token_code(p, D, b, g, tcode);
-      // rows * kMergeThreads < tok_values: the rest in turn
+  store_tokens();  // a group with no chunk to merge
+  if constexpr (FP8) {  // rows * kMergeThreads < tok_values: the rest in turn
+    if (MODE == MODE_GLOBAL && p.append)
       for (int k = tid + kMergeThreads; k < per; k += kMergeThreads)
         if (row * per + k < tok_values)
           store_call_token_code(p, D, b, g, load_call_token_code(p, D, PART, quarter, b, g, row * per + k));
-    } else {
-      store_call_token(p, D, b, g, tok);
-    }
   }
   if (tid - grp * TPG == 0) {
     gml[grp][0] = r.M;
@@ -853,7 +864,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
-    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r);
+    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r, [] {});
   }
   if (MODE == MODE_GLOBAL && p.append) {
     if constexpr (FP8) {
