@@ -279,6 +279,42 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
     }
   };
+  // global call that appends its own S tokens (keys pos0 .. pos0+S-1):
+  // the chunk holding any of their slots stages them in LDS (bf16: one
+  // 16-byte piece of K and of V per thread, S*D/8 <= 512 pieces; fp8: one
+  // 4-value piece of K or V per thread, each value encoded and decoded, so
+  // that the encodes spread over every wave of the workgroup), loaded here
+  // ahead of the region's loads and written to LDS after the Q loads have
+  // gone out (the load counter drains in order: the staging then waits for
+  // the tokens alone, and an LDS write placed before the Q loads would hold
+  // them back until the tokens arrived); the Q barrier covers the writes.  The operands take them in place of the slots' old contents, and
+  // the regions receive them from the merge pass, after every chunk has read.
+  // Over an fp8 region the staged values are those of the codes the merge
+  // will store, exactly as a later call reads them.
+  constexpr bool SUBP = stages_tokens<MODE>();
+  __bf16* const tok_k = chunk_tokens;
+  __bf16* const tok_v = chunk_tokens + S * D;
+  int pos0 = 0;
+  bool tok_chunk = false, tok_piece = false;
+  u32x4 tok_kbits = {0u, 0u, 0u, 0u}, tok_vbits = {0u, 0u, 0u, 0u};
+  if constexpr (SUBP) {
+    if (p.append) {
+      pos0 = p.pos[b];
+      tok_chunk = pos0 < k0 + CK && pos0 + S > k0;  // uniform over the workgroup
+      if (FP8) {
+        tok_piece = tok_chunk && (int)threadIdx.x < 2 * S * (D / 4);
+        if (tok_piece) tok_kbits = load_token_piece4(p, b, g, D, threadIdx.x);
+      } else {
+        tok_piece = tok_chunk && (int)threadIdx.x < S * (D / 8);
+        if (tok_piece) {
+          const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
+          const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
+          tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+          tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+        }
+      }
+    }
+  }
   if (!prop) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -331,43 +367,6 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           v[j] = __builtin_bit_cast(__bf16, bits);
         }
         vop[0][0][dt] = v;
-      }
-    }
-  }
-  // global call that appends its own S tokens (keys pos0 .. pos0+S-1):
-  // the chunk holding any of their slots stages them in LDS (bf16: one
-  // 16-byte piece of K and of V per thread, S*D/8 <= 512 pieces; fp8: one
-  // 4-value piece of K or V per thread, each value encoded and decoded, so
-  // that the encodes spread over every wave of the workgroup), loaded here
-  // behind the region's loads and written to LDS after the Q loads have gone
-  // out
-  // (the load counter drains in order, so writing them first would hold the
-  // Q loads back until the region's data arrived); the Q barrier covers the
-  // writes.  The operands take them in place of the slots' old contents, and
-  // the regions receive them from the merge pass, after every chunk has read.
-  // Over an fp8 region the staged values are those of the codes the merge
-  // will store, exactly as a later call reads them.
-  constexpr bool SUBP = stages_tokens<MODE>();
-  __bf16* const tok_k = chunk_tokens;
-  __bf16* const tok_v = chunk_tokens + S * D;
-  int pos0 = 0;
-  bool tok_chunk = false, tok_piece = false;
-  u32x4 tok_kbits = {0u, 0u, 0u, 0u}, tok_vbits = {0u, 0u, 0u, 0u};
-  if constexpr (SUBP) {
-    if (p.append) {
-      pos0 = p.pos[b];
-      tok_chunk = pos0 < k0 + CK && pos0 + S > k0;  // uniform over the workgroup
-      if (FP8) {
-        tok_piece = tok_chunk && (int)threadIdx.x < 2 * S * (D / 4);
-        if (tok_piece) tok_kbits = load_token_piece4(p, b, g, D, threadIdx.x);
-      } else {
-        tok_piece = tok_chunk && (int)threadIdx.x < S * (D / 8);
-        if (tok_piece) {
-          const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
-          const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
-          tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
-          tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
-        }
       }
     }
   }
