@@ -75,7 +75,7 @@ def build_layers(swr, torch, pool):
     for _ in range(N_SLIDING_SETS):
         ko, vo = [], []
         for _b in range(B):
-            k_off, v_off, cap = pool.alloc_kv(W, HKV, D)
+            k_off, v_off, cap = pool.alloc_ring(W, HKV, D)
             ko.append(k_off)
             vo.append(v_off)
         L = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor(ko, device=dev), torch.tensor(vo, device=dev), W)
@@ -84,20 +84,20 @@ def build_layers(swr, torch, pool):
         for half in range(2):
             k = torch.randn(B, W // 2, HKV, D, device=dev, generator=gen).to(torch.bfloat16)
             v = torch.randn(B, W // 2, HKV, D, device=dev, generator=gen).to(torch.bfloat16)
-            swr.kv_append(L, k, v, (pos - W + half * (W // 2)).to(torch.int32))
+            swr.ring_kv_append(L, k, v, (pos - W + half * (W // 2)).to(torch.int32))
         k_new = torch.randn(B, 1, HKV, D, device=dev, generator=gen).to(torch.bfloat16)
         v_new = torch.randn(B, 1, HKV, D, device=dev, generator=gen).to(torch.bfloat16)
         q = torch.randn(B, HKV * G, D, device=dev, generator=gen).to(torch.bfloat16)
         sliding.append(dict(L=L, pos=pos, k_new=k_new, v_new=v_new, q=q, out=torch.empty_like(q)))
     glob = []
     for _ in range(N_GLOBAL_SETS):
-        k_off, v_off, cap = pool.alloc_kv(KC, GHKV, GD, global_layer=True)
+        k_off, v_off, cap = pool.alloc_global(KC, GHKV, GD)
         L = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor([k_off], device=dev),
                         torch.tensor([v_off], device=dev), cap)
         ctx = KC - GS
         k = torch.randn(1, ctx, GHKV, GD, device=dev, generator=gen).to(torch.bfloat16)
         v = torch.randn(1, ctx, GHKV, GD, device=dev, generator=gen).to(torch.bfloat16)
-        swr.kv_append(L, k, v, torch.zeros(1, device=dev, dtype=torch.int32), wrap=False)
+        swr.ring_kv_append(L, k, v, torch.zeros(1, device=dev, dtype=torch.int32), wrap=False)
         k_prop = torch.randn(1, GS, GHKV, GD, device=dev, generator=gen).to(torch.bfloat16)
         v_prop = torch.randn(1, GS, GHKV, GD, device=dev, generator=gen).to(torch.bfloat16)
         q = torch.randn(1, GS, GHKV * GG, GD, device=dev, generator=gen).to(torch.bfloat16)
@@ -306,13 +306,13 @@ def decode_stack(swr, torch, randn, dev):
         k = torch.empty(B * rb, dtype=torch.uint8, device=dev)
         v = torch.empty_like(k)
         L = swr.KVLayer(k, v, roff, roff, W)
-        swr.kv_append(L, hk, hv, (pos - W).to(torch.int32))
+        swr.ring_kv_append(L, hk, hv, (pos - W).to(torch.int32))
         sliding.append(L)
     for _ in range(10):
         k = torch.zeros(sum(grb), dtype=torch.uint8, device=dev)
         v = torch.zeros_like(k)
         L = swr.KVLayer(k, v, goff, goff, max(caps), cap_b=capb)
-        swr.kv_append(L, gkh, gvh, torch.zeros(B, device=dev, dtype=torch.int32), n_new=pos, wrap=False)
+        swr.ring_kv_append(L, gkh, gvh, torch.zeros(B, device=dev, dtype=torch.int32), n_new=pos, wrap=False)
         glob.append(L)
     q_s, q_g = randn(B, HKV * G, D), randn(B, 1, GHKV * GG, GD)
     kn_s, vn_s = randn(B, HKV, D), randn(B, HKV, D)
@@ -383,7 +383,7 @@ def other_workloads(swr, torch, sweep=True):
         off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
         L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
         p0 = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
-        swr.kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
+        swr.ring_kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
         q = randn(w.B, w.S, w.Hq, w.D)
         sets.append((L, randn(w.B, w.S, w.Hkv, w.D), randn(w.B, w.S, w.Hkv, w.D), q, p0, torch.empty_like(q)))
     ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, w.B, w.S, w.Hq, w.Hkv, w.D, w.W)),
@@ -405,7 +405,7 @@ def other_workloads(swr, torch, sweep=True):
         off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
         L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
         pos = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
-        swr.kv_append(L, randn(w.B, w.W, 1, w.D), randn(w.B, w.W, 1, w.D), (pos - w.W + 1).to(torch.int32))
+        swr.ring_kv_append(L, randn(w.B, w.W, 1, w.D), randn(w.B, w.W, 1, w.D), (pos - w.W + 1).to(torch.int32))
         q = randn(w.B, w.G, w.D)
         sets.append((L, q, pos, torch.empty_like(q)))
     hws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.G, 1, w.D, w.W)),
@@ -428,7 +428,7 @@ def other_workloads(swr, torch, sweep=True):
         L = swr.KVLayer(kb, vb, off, off.clone(), w.W, swr.SWR_KV_FP8_E4M3, 4.5 / 448, 4.5 / 448)
         pos = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
         for half in range(2):
-            swr.kv_append(L, randn(w.B, w.W // 2, w.Hkv, w.D), randn(w.B, w.W // 2, w.Hkv, w.D),
+            swr.ring_kv_append(L, randn(w.B, w.W // 2, w.Hkv, w.D), randn(w.B, w.W // 2, w.Hkv, w.D),
                           (pos - w.W + 1 + half * (w.W // 2)).to(torch.int32))
         q = randn(w.B, w.Hq, w.D)
         sets.append((L, q, pos, torch.empty_like(q), randn(w.B, w.Hkv, w.D), randn(w.B, w.Hkv, w.D)))
@@ -462,10 +462,10 @@ def other_workloads(swr, torch, sweep=True):
         pool = swr.Pool(total)
         rk, rv, gk, gv, gc = [], [], [], [], []
         for c in ctx:
-            k_off, v_off, _ = pool.alloc_kv(ws_s.W, ws_s.Hkv, ws_s.D, dtype)
+            k_off, v_off, _ = pool.alloc_ring(ws_s.W, ws_s.Hkv, ws_s.D, dtype)
             rk.append(k_off)
             rv.append(v_off)
-            k_off, v_off, cap = pool.alloc_kv(c + 1, ws_g.Hkv, ws_g.D, dtype, global_layer=True)
+            k_off, v_off, cap = pool.alloc_global(c + 1, ws_g.Hkv, ws_g.D, dtype)
             gk.append(k_off)
             gv.append(v_off)
             gc.append(cap)
@@ -480,12 +480,12 @@ def other_workloads(swr, torch, sweep=True):
             one = torch.tensor([b], device=dev)
             n = min(c + 1, ws_s.W)
             ring = swr.KVLayer(pool.buffer, pool.buffer, sl.k_off[one], sl.v_off[one], ws_s.W, dtype, sc, sc)
-            swr.kv_append(ring, randn(1, n, ws_s.Hkv, ws_s.D), randn(1, n, ws_s.Hkv, ws_s.D),
+            swr.ring_kv_append(ring, randn(1, n, ws_s.Hkv, ws_s.D), randn(1, n, ws_s.Hkv, ws_s.D),
                           torch.tensor([c - n + 1], device=dev, dtype=torch.int32))
             glob1 = swr.KVLayer(pool.buffer, pool.buffer, gl.k_off[one], gl.v_off[one], gc[b], dtype, sc, sc)
             for s0 in range(0, c + 1, 8192):
                 n2 = min(8192, c + 1 - s0)
-                swr.kv_append(glob1, randn(1, n2, ws_g.Hkv, ws_g.D), randn(1, n2, ws_g.Hkv, ws_g.D),
+                swr.ring_kv_append(glob1, randn(1, n2, ws_g.Hkv, ws_g.D), randn(1, n2, ws_g.Hkv, ws_g.D),
                               torch.tensor([s0], device=dev, dtype=torch.int32), wrap=False)
         qs = randn(B, ws_s.Hq, ws_s.D)
         qg = randn(B, 1, ws_g.Hq, ws_g.D)
@@ -538,7 +538,7 @@ def other_workloads(swr, torch, sweep=True):
     vb = torch.zeros_like(kb)
     off = torch.zeros(1, device=dev, dtype=torch.int64)
     L = swr.KVLayer(kb, vb, off, off.clone(), cap)
-    swr.kv_append(L, randn(1, hi, GHKV, GD), randn(1, hi, GHKV, GD), torch.zeros(1, device=dev, dtype=torch.int32),
+    swr.ring_kv_append(L, randn(1, hi, GHKV, GD), randn(1, hi, GHKV, GD), torch.zeros(1, device=dev, dtype=torch.int32),
                   wrap=False)
     counts = torch.arange(lo, hi + 1, device=dev, dtype=torch.int32)
     qpos = (counts.view(-1, 1) - GS + torch.arange(GS, device=dev, dtype=torch.int32).view(1, -1)).contiguous()
@@ -624,7 +624,7 @@ def main():
                                  ws=gws)
 
     def global_separate(g):
-        swr.kv_append(g["L"], g["k_prop"], g["v_prop"], g["ctx"], wrap=False)
+        swr.ring_kv_append(g["L"], g["k_prop"], g["v_prop"], g["ctx"], wrap=False)
         swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, scale_g, out=g["out"], ws=gws)
 
     def step(i, events=None):
@@ -670,7 +670,7 @@ def main():
     decode_only_us = _timed(torch, lambda i: swr.swa_decode(sliding[i]["L"], sliding[i]["q"], sliding[i]["pos"], HKV,
                                                             scale_s, out=sliding[i]["out"], ws=dws),
                             30, N_SLIDING_SETS)
-    append_only_us = _timed(torch, lambda i: swr.kv_append(sliding[i]["L"], sliding[i]["k_new"], sliding[i]["v_new"],
+    append_only_us = _timed(torch, lambda i: swr.ring_kv_append(sliding[i]["L"], sliding[i]["k_new"], sliding[i]["v_new"],
                                                            sliding[i]["pos"]), 30, N_SLIDING_SETS)
 
     # The global layer's launches are short: also time them the way a serving

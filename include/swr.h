@@ -27,7 +27,8 @@
  * Conventions for every call below
  *   - All pointers marked "device" point to GPU memory the caller owns; the
  *     library allocates no device memory and keeps no state between calls
- *     (the pool functions keep host-side bookkeeping only).
+ *     (the pool functions keep host-side bookkeeping of a caller-owned
+ *     device buffer).
  *   - Calls are asynchronous on `stream`; the caller keeps every buffer alive
  *     until the stream has passed the call.
  *   - Every call validates its host-side arguments first and, on failure,
@@ -35,10 +36,16 @@
  *     launch failures are reported as SWR_ERR_LAUNCH.  Nothing throws.
  *   - bf16 means the 16-bit bfloat16 format; fp32 sums; outputs are rounded to
  *     bf16 with round-to-nearest-even.
- *   - Values that live in device memory (positions, key counts) cannot be
- *     checked on the host; the preconditions stated for them are the
- *     caller's.  Region reads and writes are bounded in hardware to the
- *     region, so a broken precondition gives wrong numbers, not a fault.
+ *   - Values that live in device memory (positions, key counts, region
+ *     offsets) cannot be checked on the host; the preconditions stated for
+ *     them are the caller's.  Every region read and write goes through a
+ *     buffer resource whose base is k_base + k_off[b] (v_base + v_off[b])
+ *     and whose extent is the region's size, so a position or key count out
+ *     of range gives wrong numbers, not an access outside the region -- but
+ *     only while k_off[b] and v_off[b] point at regions of the stated
+ *     capacity inside allocated memory: a wrong offset moves the base itself
+ *     and can fault.  Queries, outputs, new tokens and workspaces are plain
+ *     arrays of the sizes stated for each call.
  *
  * KV region layout (one request, one layer; K and V regions separate; a
  * region has `cap` slots, cap a multiple of 8, and stores S = cap rounded up
@@ -120,8 +127,10 @@ typedef struct swr_kv {
 
 /* ------------------------------------------------------------------ append */
 
-/* Write new tokens' K and V into each request's region ([Carat] ring section;
- * [Gaudi] "Our approach": K and V of a token go to the same slot).
+/* Write new tokens' K and V into each request's region ([Carat] ring section:
+ * a token's slot is its position modulo the window; [Gaudi] "Our approach":
+ * K and V of a token go to the same slot).  The same call writes contiguous
+ * global regions (wrap == 0).
  *   k_new, v_new : device bf16 [B][T][Hkv][D] (row-major, 16-B aligned)
  *   pos0         : device int32 [B], position of token 0 of request b (>= 0)
  *   n_new        : device int32 [B] tokens to write for request b (0..T), or
@@ -135,9 +144,9 @@ typedef struct swr_kv {
  *   fp8 regions store the code nearest to value/scale (exact quotient,
  *   ties to even, saturating at +-448; NaN -> 0x7F with its sign).
  * Supported: D in {64, 128, 256, 512}; T >= 1; B >= 0 (B == 0 is a no-op). */
-swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
-                         const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv, int D,
-                         int wrap, hipStream_t stream);
+swr_status swr_ring_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
+                              const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv,
+                              int D, int wrap, hipStream_t stream);
 
 /* -------------------------------------------------------- sliding decode */
 
@@ -161,7 +170,7 @@ swr_status swr_swa_decode(const swr_kv* ring, const void* q, void* out, const in
 /* Append + sliding decode in one call ([Carat] ring section: a decode step
  * writes the new token into the slot of the oldest one and attends over the
  * window; [Gaudi] "Our approach": K and V go to the same slot).  Equivalent
- * to swr_kv_append(ring, k_new, v_new, pos, NULL, B, 1, Hkv, D, 1) followed
+ * to swr_ring_kv_append(ring, k_new, v_new, pos, NULL, B, 1, Hkv, D, 1) followed
  * by swr_swa_decode(ring, q, out, pos, ...): the ring holds the same bytes
  * afterwards and the output is the same attention, from one launch (plus
  * the split merge when B*Hkv is small) instead of two.
@@ -182,7 +191,7 @@ swr_status swr_swa_append_decode(const swr_kv* ring, const void* k_new, const vo
  * separately so that none of the keys the first rows still need is evicted.
  * Row (i, h) at position pos0+i sees ring keys with position >= pos0+i-W+1
  * and proposals 0..i.  After acceptance the caller appends the accepted
- * prefix with swr_kv_append.
+ * prefix with swr_ring_kv_append.
  *   k_prop, v_prop : device bf16 [B][S][Hkv][D]
  *   q, out         : device bf16 [B][S][Hq][D]
  *   pos0           : device int32 [B], >= 0
@@ -218,7 +227,7 @@ swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const i
  * proposals, then the grouped attention).  Writes the S tokens of request b
  * at positions pos0[b] .. pos0[b]+S-1 (slot = position) and computes the rows
  * of swr_global_attend with q_pos[b][i] = pos0[b] + i and key_count[b] =
- * pos0[b] + S.  Equivalent to swr_kv_append(kv, k_new, v_new, pos0, NULL, B,
+ * pos0[b] + S.  Equivalent to swr_ring_kv_append(kv, k_new, v_new, pos0, NULL, B,
  * S, Hkv, D, 0) followed by swr_global_attend: same region bytes, same
  * attention.  When the K/V of all (request, KV head) pairs spans fewer than
  * 2048 tiles of 32 keys the call is one chunked pass plus its merge: the
@@ -248,50 +257,70 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
 /* ------------------------------------------------------------ the pool */
 
 /* Host-side carve of one device buffer into K/V regions ([Gaudi] "Our
- * approach": rings and global KV share one HBM pool).  The pool only keeps
- * byte ranges; it never touches device memory.  First fit, 256-byte aligned
- * ranges.  Thread-safe. */
+ * approach": rings and global KV share one HBM pool).  The pool keeps byte
+ * ranges on the host (first fit, 256-byte aligned ranges, thread-safe); the
+ * region carves below also zero-fill what they hand out, on the caller's
+ * stream, with the zero-fill kernel (no memset node, so the fill may be
+ * captured into a graph): a fresh ring holds zeros, and a global region's
+ * tail past the key count holds the zeros the padded contraction multiplies
+ * ([Carat] "More FLOPs can be faster": the key axis is padded to a multiple
+ * of 64 with a zero-initialised tail). */
 typedef struct swr_pool swr_pool;
 
 /* Bytes of one K (or V) region of `cap` slots: (cap rounded up to 32) *
  * Hkv * D * element size (-1 if the shape is invalid). */
 int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype);
 
-swr_status swr_pool_create(size_t bytes, swr_pool** pool);
+/* A pool over `bytes` bytes of the device buffer at `base` (256-byte
+ * aligned; the caller owns it and keeps it alive while the pool is used).
+ * base == NULL makes a bookkeeping-only pool: it carves the same ranges but
+ * fills nothing and launches nothing (the caller then zero fills).
+ * SWR_ERR_INVALID for a null `pool`, bytes == 0 or a misaligned base. */
+swr_status swr_pool_create(void* base, size_t bytes, swr_pool** pool);
 void swr_pool_destroy(swr_pool* pool);
-/* Reserve `bytes` (> 0); *offset receives its 256-B aligned start. */
+/* Reserve `bytes` (> 0); *offset receives its 256-B aligned start (bytes
+ * from base).  Nothing is filled. */
 swr_status swr_pool_alloc(swr_pool* pool, size_t bytes, int64_t* offset);
-/* Release a range returned by swr_pool_alloc (SWR_ERR_INVALID if unknown). */
+/* Release a range returned by any of the carves (SWR_ERR_INVALID if unknown). */
 swr_status swr_pool_free(swr_pool* pool, int64_t offset);
-/* Reserve a K region and a V region for `tokens` tokens of one layer.
- * global == 0: a ring, cap = tokens rounded up to a multiple of 8.
- * global != 0: a contiguous region, cap = tokens rounded up to a multiple of
- * 64 ([Carat] "More FLOPs can be faster": the padded tail).  The caller zero
- * fills the two ranges on its stream (swr_zero_fill) before first use. */
-swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dtype, int global,
-                             int64_t* k_offset, int64_t* v_offset, int32_t* cap);
+/* A ring for one request of one sliding layer ([Carat] ring section: each
+ * request owns a fixed ring of W slots): a K region and a V region of
+ * cap = W rounded up to a multiple of 8 slots (Hkv x D, element type dtype),
+ * both zero-filled on `stream`.  *k_off, *v_off: the regions' offsets from
+ * base; *cap: the slots (the ring's W in swr_kv.cap).  SWR_ERR_NOMEM when
+ * the pool has no room (the pool is then as before the call); SWR_ERR_LAUNCH
+ * when the fill could not be launched (the ranges are released again). */
+swr_status swr_pool_alloc_ring(swr_pool* pool, int W, int Hkv, int D, int dtype, hipStream_t stream,
+                               int64_t* k_off, int64_t* v_off, int32_t* cap);
+/* A contiguous global-layer region for `tokens` keys of one request
+ * ([Carat] "More FLOPs can be faster"): K and V regions of cap = tokens
+ * rounded up to a multiple of 64 slots, both zero-filled on `stream`, so the
+ * padded tail of every key count up to `tokens` holds zeros.  Outputs and
+ * errors as for swr_pool_alloc_ring. */
+swr_status swr_pool_alloc_global(swr_pool* pool, int tokens, int Hkv, int D, int dtype, hipStream_t stream,
+                                 int64_t* k_off, int64_t* v_off, int32_t* cap);
 /* Bytes in use and the largest free range. */
 swr_status swr_pool_stats(const swr_pool* pool, size_t* used, size_t* largest_free);
 
 /* Admission of one request ([Gaudi] "Patching sliding window KV
  * allocation": a sliding layer only ever reads its last W tokens, so it
  * keeps W slots however long the request grows, and only the global layers
- * take KV in proportion to the context).  Carves, all or nothing, a K and a
- * V region for each of n_sliding rings of W slots (cap W rounded up to 8,
- * shape Hkv_s x D_s) and each of n_global global regions of `context`
- * tokens (cap rounded up to 64, shape Hkv_g x D_g), all of element type
- * dtype.
+ * take KV in proportion to the context).  Carves, all or nothing, the K and
+ * V regions of n_sliding rings (as swr_pool_alloc_ring, shape Hkv_s x D_s)
+ * and of n_global global regions of `context` tokens (as
+ * swr_pool_alloc_global, shape Hkv_g x D_g), all of element type dtype, and
+ * zero-fills every one of them on `stream`.
  *   k_off, v_off : host int64 [n_sliding + n_global] (out), sliding layers
  *                  first, in layer order
  *   global_cap   : host int32 (out): the global regions' cap (may be NULL
  *                  when n_global == 0)
- * SWR_ERR_NOMEM when the request does not fit; the pool is then as before
- * the call.  SWR_ERR_INVALID for a null pool or output, negative layer
- * counts, no layer at all, context < 1 or an invalid shape.  The caller zero
- * fills the regions before first use (swr_zero_fill). */
+ * SWR_ERR_NOMEM when the request does not fit, SWR_ERR_LAUNCH when a fill
+ * could not be launched; the pool is then as before the call.
+ * SWR_ERR_INVALID for a null pool or output, negative layer counts, no layer
+ * at all, context < 1 or an invalid shape. */
 swr_status swr_pool_admit(swr_pool* pool, int n_sliding, int W, int Hkv_s, int D_s, int n_global,
-                          int context, int Hkv_g, int D_g, int dtype, int64_t* k_off, int64_t* v_off,
-                          int32_t* global_cap);
+                          int context, int Hkv_g, int D_g, int dtype, hipStream_t stream, int64_t* k_off,
+                          int64_t* v_off, int32_t* global_cap);
 /* Releases the n K and n V ranges of a request (as filled by
  * swr_pool_admit); SWR_ERR_INVALID if any offset was not allocated (the
  * others are still released). */
@@ -316,7 +345,7 @@ swr_status swr_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
  * the positions max(0, pos[b]-W+1) .. pos[b] -- from its pages into ring
  * slot position mod W of `ring`, the layout swr_swa_decode reads, so that
  * a gather followed by swr_swa_decode computes what the ring computes after
- * swr_kv_append.  Slots that hold no window position (pos[b] < W-1) and
+ * swr_ring_kv_append.  Slots that hold no window position (pos[b] < W-1) and
  * slots whose page is missing keep what they held.
  *   k_pages, v_pages : device bf16 [n_pages][page_tokens][Hkv][D] (16-B
  *                      aligned): the token at position p of request b is row

@@ -30,10 +30,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace 
           4: "HIP launch error", 5: "pool exhausted"}
 
 EXPORTS = [
-    "swr_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
+    "swr_ring_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
     "swr_global_append_attend", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
-    "swr_pool_alloc_kv", "swr_pool_stats", "swr_pool_admit", "swr_pool_release", "swr_request_kv_bytes",
+    "swr_pool_alloc_ring", "swr_pool_alloc_global", "swr_pool_stats", "swr_pool_admit", "swr_pool_release", "swr_request_kv_bytes",
     "swr_zero_fill", "swr_paged_gather_window", "swr_read_ceiling",
     "swr_status_string",
 ]
@@ -63,7 +63,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     KV = ctypes.POINTER(SwrKV)
     sig = {
-        "swr_kv_append": ([KV, P, P, P, P, I, I, I, I, I, P], I),
+        "swr_ring_kv_append": ([KV, P, P, P, P, I, I, I, I, I, P], I),
         "swr_swa_decode": ([KV, P, P, P, I, I, I, I, F, P, SZ, P], I),
         "swr_swa_append_decode": ([KV, P, P, P, P, P, I, I, I, I, F, P, SZ, P], I),
         "swr_gqa_verify": ([KV, P, P, P, P, P, I, I, I, I, I, F, P, SZ, P], I),
@@ -71,14 +71,16 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "swr_global_append_attend": ([KV, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
         "swr_workspace_bytes": ([I, I, I, I, I, I, I], SZ),
         "swr_kv_region_bytes": ([I, I, I, I], I64),
-        "swr_pool_create": ([SZ, ctypes.POINTER(P)], I),
+        "swr_pool_create": ([P, SZ, ctypes.POINTER(P)], I),
         "swr_pool_destroy": ([P], None),
         "swr_pool_alloc": ([P, SZ, ctypes.POINTER(I64)], I),
         "swr_pool_free": ([P, I64], I),
-        "swr_pool_alloc_kv": ([P, I, I, I, I, I, ctypes.POINTER(I64), ctypes.POINTER(I64),
-                               ctypes.POINTER(ctypes.c_int32)], I),
+        "swr_pool_alloc_ring": ([P, I, I, I, I, P, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                 ctypes.POINTER(ctypes.c_int32)], I),
+        "swr_pool_alloc_global": ([P, I, I, I, I, P, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                   ctypes.POINTER(ctypes.c_int32)], I),
         "swr_pool_stats": ([P, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I),
-        "swr_pool_admit": ([P, I, I, I, I, I, I, I, I, I, P, P, ctypes.POINTER(ctypes.c_int32)], I),
+        "swr_pool_admit": ([P, I, I, I, I, I, I, I, I, I, P, P, P, ctypes.POINTER(ctypes.c_int32)], I),
         "swr_pool_release": ([P, I, P, P], I),
         "swr_request_kv_bytes": ([I, I, I, I, I, I, I, I, I, I], I64),
         "swr_zero_fill": ([P, SZ, P], I),
@@ -164,18 +166,19 @@ def _workspace(op, B, S, Hq, Hkv, D, n, ws, device):
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
-def kv_append(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch.Tensor,
-              n_new: Optional[torch.Tensor] = None, wrap: bool = True, stream=None) -> None:
-    """swr_kv_append: k_new, v_new bf16 [B][T][Hkv][D]; pos0 (and n_new) int32 [B]."""
+def ring_kv_append(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch.Tensor,
+                   n_new: Optional[torch.Tensor] = None, wrap: bool = True, stream=None) -> None:
+    """swr_ring_kv_append: k_new, v_new bf16 [B][T][Hkv][D]; pos0 (and n_new)
+    int32 [B]; wrap=False writes contiguous global regions (slot = position)."""
     _dev(k_new, "k_new", torch.bfloat16)
     _dev(v_new, "v_new", torch.bfloat16)
     _dev(pos0, "pos0", torch.int32)
     if n_new is not None:
         _dev(n_new, "n_new", torch.int32)
     B, T, hkv, d = k_new.shape
-    _check("swr_kv_append", lib.swr_kv_append(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(pos0),
-                                              _ptr(n_new), B, T, hkv, d, 1 if wrap else 0,
-                                              _stream(stream)))
+    _check("swr_ring_kv_append", lib.swr_ring_kv_append(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(pos0),
+                                                        _ptr(n_new), B, T, hkv, d, 1 if wrap else 0,
+                                                        _stream(stream)))
 
 
 def paged_gather_window(k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
@@ -320,14 +323,16 @@ def request_kv_bytes(n_sliding: int, W: int, hkv_s: int, d_s: int, n_global: int
 
 
 class Pool:
-    """Host bookkeeping (swr_pool_*) over one device byte buffer shared by
-    ring and global regions ("Improving Decode Throughput on Intel Gaudi 3",
-    Our approach)."""
+    """A device byte buffer shared by ring and global regions ("Improving
+    Decode Throughput on Intel Gaudi 3", Our approach), carved by the
+    library's host bookkeeping (swr_pool_*); the carves zero-fill what they
+    hand out on the stream."""
 
     def __init__(self, nbytes: int, device="cuda"):
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
         h = ctypes.c_void_p()
-        _check("swr_pool_create", lib.swr_pool_create(nbytes, ctypes.byref(h)))
+        _check("swr_pool_create", lib.swr_pool_create(ctypes.c_void_p(self.buffer.data_ptr()), nbytes,
+                                                      ctypes.byref(h)))
         self._h = h
 
     def alloc(self, nbytes: int) -> int:
@@ -338,35 +343,32 @@ class Pool:
     def free(self, offset: int) -> None:
         _check("swr_pool_free", lib.swr_pool_free(self._h, offset))
 
-    def alloc_kv(self, tokens: int, hkv: int, d: int, dtype: int = SWR_KV_BF16, global_layer: bool = False,
-                 zero: bool = True, stream=None):
-        """Reserve a K and a V region; zero-fills both on the stream.
-        Returns (k_offset, v_offset, cap)."""
+    def alloc_ring(self, W: int, hkv: int, d: int, dtype: int = SWR_KV_BF16, stream=None):
+        """swr_pool_alloc_ring: a zero-filled ring (K and V) of W slots
+        (rounded up to 8).  Returns (k_offset, v_offset, cap)."""
         ko, vo, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-        _check("swr_pool_alloc_kv", lib.swr_pool_alloc_kv(self._h, tokens, hkv, d, dtype, 1 if global_layer else 0,
-                                                          ctypes.byref(ko), ctypes.byref(vo), ctypes.byref(cap)))
-        if zero:
-            rb = region_bytes(cap.value, hkv, d, dtype)
-            zero_fill(self.buffer, ko.value, rb, stream)
-            zero_fill(self.buffer, vo.value, rb, stream)
+        _check("swr_pool_alloc_ring", lib.swr_pool_alloc_ring(self._h, W, hkv, d, dtype, _stream(stream),
+                                                              ctypes.byref(ko), ctypes.byref(vo), ctypes.byref(cap)))
+        return ko.value, vo.value, cap.value
+
+    def alloc_global(self, tokens: int, hkv: int, d: int, dtype: int = SWR_KV_BF16, stream=None):
+        """swr_pool_alloc_global: a zero-filled global region (K and V) of
+        `tokens` slots rounded up to 64.  Returns (k_offset, v_offset, cap)."""
+        ko, vo, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check("swr_pool_alloc_global", lib.swr_pool_alloc_global(self._h, tokens, hkv, d, dtype, _stream(stream),
+                                                                  ctypes.byref(ko), ctypes.byref(vo),
+                                                                  ctypes.byref(cap)))
         return ko.value, vo.value, cap.value
 
     def admit(self, n_sliding: int, W: int, hkv_s: int, d_s: int, n_global: int, context: int, hkv_g: int,
-              d_g: int, dtype: int = SWR_KV_BF16, zero: bool = True, stream=None):
+              d_g: int, dtype: int = SWR_KV_BF16, stream=None):
         """swr_pool_admit: one request's rings and global regions, all or
-        nothing; zero-fills them on the stream.  Returns (k_offsets,
-        v_offsets, global_cap), sliding layers first."""
+        nothing, zero-filled on the stream.  Returns (k_offsets, v_offsets,
+        global_cap), sliding layers first."""
         n = n_sliding + n_global
         ko, vo, gcap = (ctypes.c_int64 * max(n, 1))(), (ctypes.c_int64 * max(n, 1))(), ctypes.c_int32(0)
         _check("swr_pool_admit", lib.swr_pool_admit(self._h, n_sliding, W, hkv_s, d_s, n_global, context, hkv_g,
-                                                    d_g, dtype, ko, vo, ctypes.byref(gcap)))
-        if zero:
-            for i in range(n):
-                glob = i >= n_sliding
-                rb = region_bytes(gcap.value if glob else -(-W // 8) * 8, hkv_g if glob else hkv_s,
-                                  d_g if glob else d_s, dtype)
-                zero_fill(self.buffer, ko[i], rb, stream)
-                zero_fill(self.buffer, vo[i], rb, stream)
+                                                    d_g, dtype, _stream(stream), ko, vo, ctypes.byref(gcap)))
         return list(ko[:n]), list(vo[:n]), gcap.value
 
     def release(self, k_offsets, v_offsets) -> None:

@@ -169,9 +169,9 @@ hipError_t launch_read_ceiling(const void* src, size_t n16, uint32_t* sink, int 
 
 extern "C" {
 
-swr_status swr_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
-                         const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv, int D,
-                         int wrap, hipStream_t stream) {
+swr_status swr_ring_kv_append(const swr_kv* kv, const void* k_new, const void* v_new,
+                              const int32_t* pos0, const int32_t* n_new, int B, int T, int Hkv,
+                              int D, int wrap, hipStream_t stream) {
   if (B < 0 || T < 1 || Hkv < 1 || D < 1) return SWR_ERR_INVALID;
   if (!supported_d(D)) return SWR_ERR_UNSUPPORTED;
   swr_status st = check_kv(kv, Hkv, D);
@@ -318,6 +318,7 @@ const char* swr_status_string(swr_status s) {
 // ------------------------------------------------------------------ pool
 
 struct swr_pool {
+  uint8_t* base;                   // device buffer (null: bookkeeping only)
   size_t size;
   std::map<int64_t, size_t> used;  // offset -> bytes (sorted by offset)
   size_t used_bytes = 0;
@@ -327,14 +328,44 @@ struct swr_pool {
 namespace {
 constexpr int64_t kPoolAlign = 256;
 int64_t align_up(int64_t x) { return (x + kPoolAlign - 1) / kPoolAlign * kPoolAlign; }
+
+// Carves a K and a V region of `tokens` slots rounded up to `mult` (8 for a
+// ring, 64 for a global region) and, when the pool has a device buffer,
+// zero-fills both on the stream; on any failure the pool is as before.
+swr_status carve_kv(swr_pool* pool, int tokens, int mult, int Hkv, int D, int dtype, hipStream_t stream,
+                    int64_t* k_offset, int64_t* v_offset, int32_t* cap) {
+  if (!pool || !k_offset || !v_offset || !cap || tokens <= 0 || Hkv <= 0 || D <= 0) return SWR_ERR_INVALID;
+  const int64_t c = ((int64_t)tokens + mult - 1) / mult * mult;
+  if (c > INT32_MAX) return SWR_ERR_INVALID;
+  const int64_t rb = swr_kv_region_bytes((int)c, Hkv, D, dtype);
+  if (rb <= 0) return SWR_ERR_INVALID;
+  int64_t ko, vo;
+  swr_status st = swr_pool_alloc(pool, (size_t)rb, &ko);
+  if (st != SWR_OK) return st;
+  st = swr_pool_alloc(pool, (size_t)rb, &vo);
+  if (st == SWR_OK && pool->base) {
+    st = to_status(swr::launch_zero_fill(pool->base + ko, (size_t)rb, stream));
+    if (st == SWR_OK) st = to_status(swr::launch_zero_fill(pool->base + vo, (size_t)rb, stream));
+    if (st != SWR_OK) swr_pool_free(pool, vo);
+  }
+  if (st != SWR_OK) {
+    swr_pool_free(pool, ko);
+    return st;
+  }
+  *k_offset = ko;
+  *v_offset = vo;
+  *cap = (int32_t)c;
+  return SWR_OK;
+}
 }  // namespace
 
 extern "C" {
 
-swr_status swr_pool_create(size_t bytes, swr_pool** pool) {
-  if (!pool || bytes == 0) return SWR_ERR_INVALID;
+swr_status swr_pool_create(void* base, size_t bytes, swr_pool** pool) {
+  if (!pool || bytes == 0 || (reinterpret_cast<uintptr_t>(base) % kPoolAlign) != 0) return SWR_ERR_INVALID;
   swr_pool* p = new (std::nothrow) swr_pool();
   if (!p) return SWR_ERR_NOMEM;
+  p->base = static_cast<uint8_t*>(base);
   p->size = bytes;
   *pool = p;
   return SWR_OK;
@@ -343,7 +374,7 @@ swr_status swr_pool_create(size_t bytes, swr_pool** pool) {
 void swr_pool_destroy(swr_pool* pool) { delete pool; }
 
 swr_status swr_pool_alloc(swr_pool* pool, size_t bytes, int64_t* offset) {
-  if (!pool || !offset || bytes == 0) return SWR_ERR_INVALID;
+  if (!pool || !offset || bytes == 0 || bytes > (size_t)INT64_MAX / 2) return SWR_ERR_INVALID;
   std::lock_guard<std::mutex> lk(pool->mu);
   // first fit: walk the used ranges in address order, try each gap
   int64_t cursor = 0;
@@ -375,27 +406,14 @@ swr_status swr_pool_free(swr_pool* pool, int64_t offset) {
   return SWR_OK;
 }
 
-swr_status swr_pool_alloc_kv(swr_pool* pool, int tokens, int Hkv, int D, int dtype, int global,
-                             int64_t* k_offset, int64_t* v_offset, int32_t* cap) {
-  if (!pool || !k_offset || !v_offset || !cap || tokens <= 0 || Hkv <= 0 || D <= 0)
-    return SWR_ERR_INVALID;
-  const int mult = global ? 64 : 8;
-  const long c = ((long)tokens + mult - 1) / mult * mult;
-  if (c > INT32_MAX) return SWR_ERR_INVALID;
-  const int64_t rb = swr_kv_region_bytes((int)c, Hkv, D, dtype);
-  if (rb <= 0) return SWR_ERR_INVALID;
-  int64_t ko, vo;
-  swr_status st = swr_pool_alloc(pool, (size_t)rb, &ko);
-  if (st != SWR_OK) return st;
-  st = swr_pool_alloc(pool, (size_t)rb, &vo);
-  if (st != SWR_OK) {
-    swr_pool_free(pool, ko);
-    return st;
-  }
-  *k_offset = ko;
-  *v_offset = vo;
-  *cap = (int32_t)c;
-  return SWR_OK;
+swr_status swr_pool_alloc_ring(swr_pool* pool, int W, int Hkv, int D, int dtype, hipStream_t stream,
+                               int64_t* k_off, int64_t* v_off, int32_t* cap) {
+  return carve_kv(pool, W, 8, Hkv, D, dtype, stream, k_off, v_off, cap);
+}
+
+swr_status swr_pool_alloc_global(swr_pool* pool, int tokens, int Hkv, int D, int dtype, hipStream_t stream,
+                                 int64_t* k_off, int64_t* v_off, int32_t* cap) {
+  return carve_kv(pool, tokens, 64, Hkv, D, dtype, stream, k_off, v_off, cap);
 }
 
 int64_t swr_request_kv_bytes(int n_sliding, int W, int Hkv_s, int D_s, int n_global, int context, int Hkv_g,
@@ -429,7 +447,8 @@ swr_status swr_pool_release(swr_pool* pool, int n, const int64_t* k_off, const i
 }
 
 swr_status swr_pool_admit(swr_pool* pool, int n_sliding, int W, int Hkv_s, int D_s, int n_global, int context,
-                          int Hkv_g, int D_g, int dtype, int64_t* k_off, int64_t* v_off, int32_t* global_cap) {
+                          int Hkv_g, int D_g, int dtype, hipStream_t stream, int64_t* k_off, int64_t* v_off,
+                          int32_t* global_cap) {
   if (!pool || n_sliding < 0 || n_global < 0 || n_sliding + n_global < 1 || context < 1) return SWR_ERR_INVALID;
   if (!k_off || !v_off || (n_global > 0 && !global_cap)) return SWR_ERR_INVALID;
   if (swr_request_kv_bytes(n_sliding, W, Hkv_s, D_s, n_global, context, Hkv_g, D_g, dtype, 0) < 0)
@@ -439,8 +458,8 @@ swr_status swr_pool_admit(swr_pool* pool, int n_sliding, int W, int Hkv_s, int D
   int32_t cap = 0;
   for (; done < n_sliding + n_global; ++done) {
     const bool glob = done >= n_sliding;
-    st = swr_pool_alloc_kv(pool, glob ? context : W, glob ? Hkv_g : Hkv_s, glob ? D_g : D_s, dtype, glob ? 1 : 0,
-                           &k_off[done], &v_off[done], &cap);
+    st = glob ? carve_kv(pool, context, 64, Hkv_g, D_g, dtype, stream, &k_off[done], &v_off[done], &cap)
+              : carve_kv(pool, W, 8, Hkv_s, D_s, dtype, stream, &k_off[done], &v_off[done], &cap);
     if (st != SWR_OK) break;
     if (glob) *global_cap = cap;
   }

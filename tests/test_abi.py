@@ -25,12 +25,25 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(swr_[a-z0-9_]+)\s*\(", body)))
 
 
+# The boundary's calls by the names the hot path's step list gives them
+# (ring append, sliding decode, grouped verify, global attention, workspace
+# sizing, status text) and the shared pool's carves, plus the two fused calls.
+BOUNDARY = ["swr_ring_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend",
+            "swr_workspace_bytes", "swr_status_string", "swr_pool_create", "swr_pool_alloc_ring",
+            "swr_pool_alloc_global", "swr_pool_free", "swr_pool_destroy",
+            "swr_swa_append_decode", "swr_global_append_attend"]
+
+
 def test_header_declares_the_boundary_calls():
     names = declared_functions()
-    for n in ["swr_kv_append", "swr_swa_decode", "swr_gqa_verify", "swr_global_attend",
-              "swr_swa_append_decode", "swr_global_append_attend", "swr_workspace_bytes",
-              "swr_status_string"]:
-        assert n in names
+    for n in BOUNDARY:
+        assert n in names, n
+
+
+def test_library_exports_the_boundary_calls():
+    lib = ctypes.CDLL(swr.LIB_PATH)
+    for n in BOUNDARY:
+        assert hasattr(lib, n), n
 
 
 def test_library_exports_every_declared_function():
@@ -159,7 +172,7 @@ def test_fused_global_append_validation():
 
 def test_append_validation():
     r = kv()
-    f = swr.lib.swr_kv_append
+    f = swr.lib.swr_ring_kv_append
     assert f(ctypes.byref(r), FAKE, FAKE, FAKE, None, 56, 0, 8, 256, 1, None) == INVALID   # T == 0
     assert f(ctypes.byref(r), None, FAKE, FAKE, None, 56, 1, 8, 256, 1, None) == INVALID
     assert f(ctypes.byref(r), FAKE, FAKE, None, None, 56, 1, 8, 256, 1, None) == INVALID

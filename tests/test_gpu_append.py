@@ -34,7 +34,7 @@ def run_both(B, T, hkv, d, cap, dtype, ks, vs, pos0, n_new, wrap, seed, special=
         flat[-vals.size:] = synthetic.bf16_bits(vals[::-1].copy())
     L = layer(k_pool, v_pool, k_off, v_off, cap, dtype, ks, vs)
     import sliding_window_ring_amd as swr
-    swr.kv_append(L, dev_bf16(k_new), dev_bf16(v_new), dev_i32(pos0),
+    swr.ring_kv_append(L, dev_bf16(k_new), dev_bf16(v_new), dev_i32(pos0),
                   None if n_new is None else dev_i32(n_new), wrap=wrap)
     torch.cuda.synchronize()
     oracle.kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, ks, vs, k_new, v_new, pos0, n_new, wrap=wrap)
@@ -100,7 +100,7 @@ def test_fp8_every_bf16_value():
         off = np.zeros(1, np.int64)
         L = layer(kp, vp, off, off, 256, oracle.FP8, s, s)
         import sliding_window_ring_amd as swr
-        swr.kv_append(L, dev_bf16(vals), dev_bf16(vals), dev_i32([0]), wrap=False)
+        swr.ring_kv_append(L, dev_bf16(vals), dev_bf16(vals), dev_i32([0]), wrap=False)
         torch.cuda.synchronize()
         oracle.kv_append(kp, vp, off, off, 256, oracle.FP8, s, s, vals, vals, np.array([0], np.int32), wrap=False)
         assert np.array_equal(pool_bytes(L.k_base), kp)

@@ -49,7 +49,7 @@ def test_decode_tiny_sequence_step_by_step():
     scale = 1.0 / np.sqrt(w.D)
     for t in range(w.steps):
         pos = np.array([t], np.int32)
-        swr.kv_append(L, dev_bf16(k[None, t:t + 1]), dev_bf16(v[None, t:t + 1]), dev_i32(pos))
+        swr.ring_kv_append(L, dev_bf16(k[None, t:t + 1]), dev_bf16(v[None, t:t + 1]), dev_i32(pos))
         out = swr.swa_decode(L, dev_bf16(q[None, t]), dev_i32(pos), w.Hkv, scale)
         torch.cuda.synchronize()
         oracle.kv_append(kp, vp, off, off, w.W, oracle.BF16, 1, 1, k[None, t:t + 1], v[None, t:t + 1], pos)

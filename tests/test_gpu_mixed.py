@@ -47,14 +47,14 @@ def carve(ctx, dtype):
 
 def library_carve(ctx, dtype, total):
     h = ctypes.c_void_p()
-    assert swr.lib.swr_pool_create(total, ctypes.byref(h)) == 0
+    assert swr.lib.swr_pool_create(None, total, ctypes.byref(h)) == 0  # bookkeeping only
     out = []
     for c in ctx:
         entry = {}
         for name, tokens, hkv, d, gl in (("ring", W, SHKV, SD, 0), ("glob", int(c) + 1, GHKV, GD, 1)):
             ko, vo, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-            assert swr.lib.swr_pool_alloc_kv(h, tokens, hkv, d, dtype, gl, ctypes.byref(ko), ctypes.byref(vo),
-                                             ctypes.byref(cap)) == 0
+            carve = swr.lib.swr_pool_alloc_global if gl else swr.lib.swr_pool_alloc_ring
+            assert carve(h, tokens, hkv, d, dtype, None, ctypes.byref(ko), ctypes.byref(vo), ctypes.byref(cap)) == 0
             entry[name] = (ko.value, vo.value, cap.value)
         out.append(entry)
     swr.lib.swr_pool_destroy(h)

@@ -51,3 +51,25 @@ def test_pool_admit_zero_fills_each_region_and_nothing_else():
     assert np.all(h[mask] == 0) and np.all(h[~mask] == 0xA5)
     pool.release(ko, vo)
     assert pool.stats()[0] == 0
+
+
+@pytest.mark.gpu
+def test_ring_and_global_carves_zero_fill_their_regions_and_nothing_else():
+    # a ring of 1000 slots (rounded to 1008) and a global region of 6005
+    # tokens (rounded to 6016, the padded tail included) carved from a pool
+    # whose bytes start non-zero
+    pool = swr.Pool(32 << 20)
+    pool.buffer.fill_(0x5A)
+    rk, rv, rcap = pool.alloc_ring(1000, 2, 64)
+    gk, gv, gcap = pool.alloc_global(6005, 2, 512)
+    torch.cuda.synchronize()
+    assert (rcap, gcap) == (1008, 6016)
+    h = pool.buffer.cpu().numpy()
+    mask = np.zeros(h.size, bool)
+    for o, n in ((rk, swr.region_bytes(1008, 2, 64)), (rv, swr.region_bytes(1008, 2, 64)),
+                 (gk, swr.region_bytes(6016, 2, 512)), (gv, swr.region_bytes(6016, 2, 512))):
+        mask[o:o + n] = True
+    assert np.all(h[mask] == 0) and np.all(h[~mask] == 0x5A)
+    for o in (rk, rv, gk, gv):
+        pool.free(o)
+    assert pool.stats()[0] == 0

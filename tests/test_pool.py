@@ -1,4 +1,5 @@
-"""CPU tests of the pool carve (host bookkeeping only; no device memory).
+"""CPU tests of the pool carve (bookkeeping-only pools: no device buffer, so
+nothing is filled and no kernel is launched).
 
 "Improving Decode Throughput on Intel Gaudi 3" (Our approach): ring buffers
 are carved from the same HBM pool as global-layer KV, so their balance follows
@@ -20,7 +21,7 @@ ALIGN = 256
 class Pool:
     def __init__(self, size):
         self.h = ctypes.c_void_p()
-        assert swr.lib.swr_pool_create(size, ctypes.byref(self.h)) == 0
+        assert swr.lib.swr_pool_create(None, size, ctypes.byref(self.h)) == 0
 
     def alloc(self, n):
         off = ctypes.c_int64(-1)
@@ -113,25 +114,47 @@ def test_exhaustion_and_reuse():
     assert p.alloc(4096) == (0, 0)
 
 
-@pytest.mark.parametrize("tokens,global_layer,cap", [(1024, 0, 1024), (1000, 0, 1000), (1001, 0, 1008),
-                                                     (6005, 1, 6016), (6016, 1, 6016), (1, 1, 64)])
-def test_alloc_kv_rounds_capacity(tokens, global_layer, cap):
-    p = Pool(1 << 28)
+def carve(p, tokens, hkv, d, global_layer, dtype=0):
     ko, vo, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-    assert swr.lib.swr_pool_alloc_kv(p.h, tokens, 2, 512, 0, global_layer, ctypes.byref(ko), ctypes.byref(vo),
-                                     ctypes.byref(c)) == 0
-    assert c.value == cap
+    f = swr.lib.swr_pool_alloc_global if global_layer else swr.lib.swr_pool_alloc_ring
+    st = f(p.h, tokens, hkv, d, dtype, None, ctypes.byref(ko), ctypes.byref(vo), ctypes.byref(c))
+    return st, ko.value, vo.value, c.value
+
+
+def test_create_rejects_bad_arguments():
+    h = ctypes.c_void_p()
+    assert swr.lib.swr_pool_create(None, 0, ctypes.byref(h)) == 1
+    assert swr.lib.swr_pool_create(None, 4096, None) == 1
+    # a device base must be 256-byte aligned (never dereferenced here: the
+    # call fails before anything is carved or filled)
+    assert swr.lib.swr_pool_create(ctypes.c_void_p(0x1000 + 16), 4096, ctypes.byref(h)) == 1
+
+
+@pytest.mark.parametrize("tokens,global_layer,cap", [(1024, 0, 1024), (1000, 0, 1000), (1001, 0, 1008),
+                                                     (6005, 1, 6016), (6016, 1, 6016), (1, 1, 64), (1, 0, 8)])
+def test_carves_round_capacity(tokens, global_layer, cap):
+    p = Pool(1 << 28)
+    st, ko, vo, c = carve(p, tokens, 2, 512, global_layer)
+    assert st == 0 and c == cap
     rb = swr.region_bytes(cap, 2, 512)
-    assert vo.value >= ko.value + rb and ko.value % ALIGN == 0 and vo.value % ALIGN == 0
+    assert vo >= ko + rb and ko % ALIGN == 0 and vo % ALIGN == 0
     assert p.stats()[0] == 2 * rb
 
 
-def test_alloc_kv_failure_releases_the_first_region():
+@pytest.mark.parametrize("global_layer", [0, 1])
+def test_carve_validation(global_layer):
+    p = Pool(1 << 20)
+    assert carve(p, 0, 2, 64, global_layer)[0] == 1
+    assert carve(p, 64, 0, 64, global_layer)[0] == 1
+    assert carve(p, 64, 2, 0, global_layer)[0] == 1
+    assert carve(p, 64, 2, 64, global_layer, dtype=7)[0] == 1
+    assert p.stats()[0] == 0
+
+
+def test_carve_failure_releases_the_first_region():
     rb = swr.region_bytes(1024, 8, 256)
     p = Pool(rb + rb // 2)
-    ko, vo, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-    assert swr.lib.swr_pool_alloc_kv(p.h, 1024, 8, 256, 0, 0, ctypes.byref(ko), ctypes.byref(vo),
-                                     ctypes.byref(c)) == 5
+    assert carve(p, 1024, 8, 256, 0)[0] == 5
     assert p.stats()[0] == 0
 
 
@@ -143,13 +166,12 @@ def test_mixed_rings_and_global_regions_share_one_pool():
     ranges = []
     for n in ctx:
         for tokens, hkv, d, g in ((1024, 8, 256, 0), (n + 1, 2, 512, 1)):
-            ko, vo, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-            assert swr.lib.swr_pool_alloc_kv(p.h, tokens, hkv, d, 0, g, ctypes.byref(ko), ctypes.byref(vo),
-                                             ctypes.byref(c)) == 0
-            rb = swr.region_bytes(c.value, hkv, d)
-            ranges += [(ko.value, rb), (vo.value, rb)]
+            st, ko, vo, c = carve(p, tokens, hkv, d, g)
+            assert st == 0
+            rb = swr.region_bytes(c, hkv, d)
+            ranges += [(ko, rb), (vo, rb)]
             if g:
-                assert c.value % 64 == 0 and c.value >= n + 1
+                assert c % 64 == 0 and c >= n + 1
     ranges.sort()
     for (s, z), (s2, _) in zip(ranges, ranges[1:]):
         assert s + z <= s2
@@ -166,7 +188,7 @@ def admit(pool, context, dtype=0, g=GEMMA):
     n = g["n_sliding"] + g["n_global"]
     ko, vo, cap = (ctypes.c_int64 * n)(), (ctypes.c_int64 * n)(), ctypes.c_int32(0)
     st = swr.lib.swr_pool_admit(pool.h, g["n_sliding"], g["W"], g["hkv_s"], g["d_s"], g["n_global"], context,
-                                g["hkv_g"], g["d_g"], dtype, ko, vo, ctypes.byref(cap))
+                                g["hkv_g"], g["d_g"], dtype, None, ko, vo, ctypes.byref(cap))
     return st, list(ko), list(vo), cap.value
 
 
@@ -240,13 +262,13 @@ def test_admit_validation():
     n = 60
     ko, vo, cap = (ctypes.c_int64 * n)(), (ctypes.c_int64 * n)(), ctypes.c_int32()
     f = swr.lib.swr_pool_admit
-    assert f(None, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1
-    assert f(pool.h, -1, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1
-    assert f(pool.h, 0, 1024, 8, 256, 0, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1  # no layer
-    assert f(pool.h, 50, 1024, 8, 256, 10, 0, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1   # no context
-    assert f(pool.h, 50, 1024, 8, 0, 10, 4096, 2, 512, 0, ko, vo, ctypes.byref(cap)) == 1   # head dim
-    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 7, ko, vo, ctypes.byref(cap)) == 1  # element type
-    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, None, vo, ctypes.byref(cap)) == 1
-    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, ko, vo, None) == 1
+    assert f(None, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, None, ko, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, -1, 1024, 8, 256, 10, 4096, 2, 512, 0, None, ko, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, 0, 1024, 8, 256, 0, 4096, 2, 512, 0, None, ko, vo, ctypes.byref(cap)) == 1  # no layer
+    assert f(pool.h, 50, 1024, 8, 256, 10, 0, 2, 512, 0, None, ko, vo, ctypes.byref(cap)) == 1   # no context
+    assert f(pool.h, 50, 1024, 8, 0, 10, 4096, 2, 512, 0, None, ko, vo, ctypes.byref(cap)) == 1   # head dim
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 7, None, ko, vo, ctypes.byref(cap)) == 1  # element type
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, None, None, vo, ctypes.byref(cap)) == 1
+    assert f(pool.h, 50, 1024, 8, 256, 10, 4096, 2, 512, 0, None, ko, vo, None) == 1
     assert pool.stats()[0] == 0
     assert swr.lib.swr_pool_release(pool.h, 1, (ctypes.c_int64 * 1)(256), (ctypes.c_int64 * 1)(512)) == 1
