@@ -5,8 +5,8 @@
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this code.  The GPU library
  * never links it, includes it or calls it, and this file shares no source
- * with the GPU library: every format, layout and formula below is written
- * out again from the pages it cites.
+ * with the GPU library: every format and formula below is written out again
+ * from the pages it cites.
  *
  * Sources (the web pages this method comes from):
  *   [Carat]  "Announcing Carat: An inference engine designed for Gemma 4"
@@ -41,20 +41,13 @@
  *      saturating to +-448; element value = decode(code) * scale
  *      [Thor "Features": FP8 (e4m3) KV cache].
  *
- * Memory layout of one request's region of `cap` slots (the layout the
- * library declares; restated here, not shared).  A region stores
- * S = cap rounded up to a multiple of 32 slots per KV head; an element is
- * 2 bytes (bf16 bits) or 1 byte (fp8 e4m3 code), and a granule is 16 bytes:
- * R = 8 bf16 or 16 fp8 consecutive dims of one slot.
- *   K region: slots in tiles of 32; slot s = 32t + k of head g, dim d, at
- *             element index
- *               (g*S + 32t)*D + h*16*D + (d/R)*16*R + r*R + (d%R)
- *             with h = (k/4)%2 and r = 4*(k/8) + k%4: each tile is two
- *             halves h of 16 rows r, each half stored granule-major
- *             ([Hkv][S/32][2][D/R][16][R]).
- *   V region: element (s, g, d) at element index
- *             ((g*(S/8) + s/8)*D + d)*8 + (s%8)        ([Hkv][S/8][D][8])
- *   cap is a multiple of 8.  Global regions may have a capacity per request.
+ * Regions.  The oracle computes on logical regions: request b's K (or V)
+ * region of `cap` slots is element (s, g, d) at element index
+ * (s*Hkv + g)*D + d from its byte offset, an element being a bf16 bit
+ * pattern (2 bytes) or an E4M3 code (1 byte).  Nothing here knows how the
+ * GPU library lays a region out in device memory: that byte layout is a
+ * separate codec (swr_layout.c), used only to move regions between the two
+ * forms.
  */
 #include <math.h>
 #include <stdint.h>
@@ -135,36 +128,20 @@ uint8_t orc_e4m3_encode(uint16_t x_bits, float scale) {
 }
 
 /* ------------------------------------------------------------------ */
-/* Region layout                                                       */
+/* Logical regions                                                     */
 /* ------------------------------------------------------------------ */
 
 static int elem_size(int dtype) { return dtype == ORC_FP8 ? 1 : 2; }
 
-/* Slots stored per KV head for a region of `cap` slots. */
-static int64_t stored_slots(int64_t cap) { return (cap + 31) / 32 * 32; }
-
-/* K blocks hold four granules of each of 16 rows: D must be a multiple of
- * four granules (32 bf16 dims, 64 fp8 dims). */
-static int k_layout_ok(int D, int dtype) { return D > 0 && D % (4 * (16 / elem_size(dtype))) == 0; }
-
-static size_t k_index(int64_t s, int g, int d, int64_t cap, int D, int dtype) {
-  const int64_t S = stored_slots(cap);
-  const int64_t R = 16 / elem_size(dtype); /* dims per 16-byte granule */
-  const int64_t t = s / 32, k = s % 32;
-  const int64_t h = (k / 4) % 2, r = 4 * (k / 8) + k % 4;
-  const int64_t q = d / R; /* granule; four granules of a row sit together */
-  return (size_t)(((int64_t)g * S + 32 * t) * D + h * 16 * D + (q / 4) * 64 * R + r * 4 * R + (q % 4) * R + d % R);
+/* Element index of (slot s, KV head g, dim d) in a logical region. */
+static size_t elem_index(int64_t s, int g, int d, int Hkv, int D) {
+  return (size_t)((s * Hkv + g) * D + d);
 }
 
-static size_t v_index(int64_t s, int g, int d, int64_t cap, int D) {
-  const int64_t S = stored_slots(cap);
-  return (size_t)((((int64_t)g * (S / 8) + s / 8) * D + d) * 8 + s % 8);
-}
-
-/* Bytes of one K (or V) region holding `cap` slots. */
-int64_t orc_region_bytes(int cap, int Hkv, int D, int dtype) {
-  if (cap <= 0 || cap % 8 != 0 || Hkv <= 0 || D <= 0) return -1;
-  return stored_slots(cap) * Hkv * D * elem_size(dtype);
+/* Bytes of one logical K (or V) region of `cap` slots. */
+int64_t orc_logical_region_bytes(int cap, int Hkv, int D, int dtype) {
+  if (cap <= 0 || Hkv <= 0 || D <= 0 || (dtype != ORC_BF16 && dtype != ORC_FP8)) return -1;
+  return (int64_t)cap * Hkv * D * elem_size(dtype);
 }
 
 static double read_elem(const uint8_t* region, size_t idx, int dtype, double scale) {
@@ -200,12 +177,12 @@ int orc_kv_append(uint8_t* k_base, uint8_t* v_base, const int64_t* k_off, const 
                   int cap, const int32_t* caps, int dtype, float k_scale, float v_scale,
                   const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos0,
                   const int32_t* n_new, int B, int T, int Hkv, int D, int wrap) {
-  if (cap <= 0 || cap % 8 != 0 || B < 0 || T < 0 || Hkv <= 0 || !k_layout_ok(D, dtype)) return ORC_EINVAL;
+  if (cap <= 0 || B < 0 || T < 0 || Hkv <= 0 || D <= 0) return ORC_EINVAL;
   if (wrap && caps) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int n = n_new ? n_new[b] : T;
     int64_t cb = region_cap(cap, caps, b);
-    if (n < 0 || n > T || pos0[b] < 0 || cb <= 0 || cb % 8 != 0) return ORC_EINVAL;
+    if (n < 0 || n > T || pos0[b] < 0 || cb <= 0) return ORC_EINVAL;
     if (!wrap && (int64_t)pos0[b] + n > cb) return ORC_EINVAL;
   }
   for (int b = 0; b < B; ++b) {
@@ -219,8 +196,8 @@ int orc_kv_append(uint8_t* k_base, uint8_t* v_base, const int64_t* k_off, const 
       for (int g = 0; g < Hkv; ++g)
         for (int d = 0; d < D; ++d) {
           size_t src = (((size_t)b * T + t) * Hkv + g) * D + d;
-          write_elem(kr, k_index(s, g, d, cb, D, dtype), dtype, k_scale, k_new[src]);
-          write_elem(vr, v_index(s, g, d, cb, D), dtype, v_scale, v_new[src]);
+          write_elem(kr, elem_index(s, g, d, Hkv, D), dtype, k_scale, k_new[src]);
+          write_elem(vr, elem_index(s, g, d, Hkv, D), dtype, v_scale, v_new[src]);
         }
     }
   }
@@ -246,14 +223,13 @@ typedef struct {
   const uint16_t* k_prop; /* [S][Hkv][D] for this request, or NULL */
   const uint16_t* v_prop;
   int g, Hkv, D;
-  int64_t cap;            /* slots of this request's region */
 } unit_src;
 
 static void load_key(const unit_src* u, key_ref kr, double* kd, double* vd) {
   for (int d = 0; d < u->D; ++d) {
     if (kr.slot >= 0) {
-      kd[d] = read_elem(u->kr, k_index(kr.slot, u->g, d, u->cap, u->D, u->dtype), u->dtype, u->k_scale);
-      vd[d] = read_elem(u->vr, v_index(kr.slot, u->g, d, u->cap, u->D), u->dtype, u->v_scale);
+      kd[d] = read_elem(u->kr, elem_index(kr.slot, u->g, d, u->Hkv, u->D), u->dtype, u->k_scale);
+      vd[d] = read_elem(u->vr, elem_index(kr.slot, u->g, d, u->Hkv, u->D), u->dtype, u->v_scale);
     } else {
       int64_t i = -(kr.slot + 1);
       size_t idx = ((size_t)i * u->Hkv + u->g) * u->D + d;
@@ -353,7 +329,7 @@ int orc_swa_decode(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
                    const int64_t* v_off, int W, int dtype, double k_scale, double v_scale,
                    const uint16_t* q, const int32_t* pos, int B, int Hq, int Hkv, int D,
                    double scale, double* out) {
-  if (check_common(B, 1, Hq, Hkv, D) || !k_layout_ok(D, dtype) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, 1, Hq, Hkv, D) || W <= 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b)
     if (pos[b] < 0) return ORC_EINVAL;
   int G = Hq / Hkv, rc = ORC_OK;
@@ -362,7 +338,7 @@ int orc_swa_decode(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
     int b = un / Hkv, g = un % Hkv;
     int64_t p = pos[b];
     int nk = (int)(p + 1 < W ? p + 1 : W); /* slots ever written */
-    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D, W};
+    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)G * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)G * D);
@@ -399,7 +375,7 @@ int orc_gqa_verify(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
                    const uint16_t* k_prop, const uint16_t* v_prop, const uint16_t* q,
                    const int32_t* pos0, int B, int S, int Hq, int Hkv, int D, double scale,
                    double* out) {
-  if (check_common(B, S, Hq, Hkv, D) || !k_layout_ok(D, dtype) || W <= 0 || W % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, S, Hq, Hkv, D) || W <= 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b)
     if (pos0[b] < 0) return ORC_EINVAL;
   int G = Hq / Hkv, rows = G * S, rc = ORC_OK;
@@ -410,7 +386,7 @@ int orc_gqa_verify(const uint8_t* k_base, const uint8_t* v_base, const int64_t* 
     int nr = (int)(p0 < W ? p0 : W); /* committed ring slots */
     int nk = nr + S;
     unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale,
-                  k_prop + (size_t)b * S * Hkv * D, v_prop + (size_t)b * S * Hkv * D, g, Hkv, D, W};
+                  k_prop + (size_t)b * S * Hkv * D, v_prop + (size_t)b * S * Hkv * D, g, Hkv, D};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)rows * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)rows * D);
@@ -452,11 +428,11 @@ int orc_global_attend(const uint8_t* k_base, const uint8_t* v_base, const int64_
                       double k_scale, double v_scale, const uint16_t* q, const int32_t* q_pos,
                       const int32_t* key_count, int padded, int B, int S, int Hq, int Hkv, int D,
                       double scale, double* out) {
-  if (check_common(B, S, Hq, Hkv, D) || !k_layout_ok(D, dtype) || cap <= 0 || cap % 8 != 0) return ORC_EINVAL;
+  if (check_common(B, S, Hq, Hkv, D) || cap <= 0) return ORC_EINVAL;
   for (int b = 0; b < B; ++b) {
     int64_t kc = key_count[b], kp = padded ? (kc + 63) / 64 * 64 : kc;
     int64_t cb = region_cap(cap, caps, b);
-    if (kc <= 0 || kp > cb || cb % 8 != 0) return ORC_EINVAL;
+    if (kc <= 0 || kp > cb) return ORC_EINVAL;
     for (int i = 0; i < S; ++i)
       if (q_pos[b * S + i] < 0) return ORC_EINVAL;
   }
@@ -466,8 +442,7 @@ int orc_global_attend(const uint8_t* k_base, const uint8_t* v_base, const int64_
     int b = un / Hkv, g = un % Hkv;
     int64_t kc = key_count[b];
     int nk = (int)(padded ? (kc + 63) / 64 * 64 : kc);
-    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D,
-                  region_cap(cap, caps, b)};
+    unit_src u = {k_base + k_off[b], v_base + v_off[b], dtype, k_scale, v_scale, NULL, NULL, g, Hkv, D};
     key_ref* keys = (key_ref*)malloc(sizeof(key_ref) * nk);
     double* qd = (double*)malloc(sizeof(double) * (size_t)rows * D);
     double* od = (double*)malloc(sizeof(double) * (size_t)rows * D);

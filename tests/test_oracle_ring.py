@@ -209,3 +209,44 @@ def test_paged_gather_skips_missing_pages():
             assert np.all(kv[s] == 0x1111), p
         else:
             assert np.all(f64(kv[s]) == p + 1), p
+
+
+# --- the layout codec: the device byte layout against the numpy views above
+# (written from the declared layout, independently of the codec's index
+# arithmetic), on random bytes, ragged capacities and both element types
+
+CODEC_SHAPES = [(16, 1, 64, oracle.BF16), (40, 2, 32, oracle.BF16), (1024, 2, 256, oracle.BF16),
+                (40, 2, 64, oracle.FP8), (1000, 1, 512, oracle.FP8)]
+
+
+@pytest.mark.parametrize("cap,hkv,d,dtype", CODEC_SHAPES)
+def test_codec_unpack_matches_layout_views(cap, hkv, d, dtype):
+    g = synthetic.rng(cap + 7 * d + dtype)
+    esize = 2 if dtype == oracle.BF16 else 1
+    rb = oracle.region_bytes(cap, hkv, d, dtype)
+    assert rb == stored(cap) * hkv * d * esize
+    region = g.integers(0, 256, rb, dtype=np.uint8)
+    et = np.uint16 if esize == 2 else np.uint8
+    for is_v, view in ((False, k_view), (True, v_view)):
+        got = oracle.unpack_region(region, cap, hkv, d, dtype, is_v).view(et).reshape(cap, hkv, d)
+        assert np.array_equal(got, view(region, 0, cap, hkv, d, esize)), is_v
+
+
+@pytest.mark.parametrize("cap,hkv,d,dtype", CODEC_SHAPES)
+def test_codec_round_trips(cap, hkv, d, dtype):
+    g = synthetic.rng(3 * cap + d + dtype)
+    rb = oracle.region_bytes(cap, hkv, d, dtype)
+    lb = oracle.logical_region_bytes(cap, hkv, d, dtype)
+    assert lb == cap * hkv * d * (2 if dtype == oracle.BF16 else 1)
+    for is_v in (False, True):
+        logical = g.integers(0, 256, lb, dtype=np.uint8)
+        region = np.zeros(rb, np.uint8)
+        oracle.pack_region(logical, region, cap, hkv, d, dtype, is_v)
+        assert np.array_equal(oracle.unpack_region(region, cap, hkv, d, dtype, is_v), logical)
+        # every logical byte lands somewhere, and only the padding slots stay zero
+        assert np.count_nonzero(region) == np.count_nonzero(logical)
+        region2 = g.integers(0, 256, rb, dtype=np.uint8)
+        back = region2.copy()
+        oracle.pack_region(oracle.unpack_region(region2, cap, hkv, d, dtype, is_v), back, cap, hkv, d, dtype,
+                           is_v)
+        assert np.array_equal(back, region2)
