@@ -71,6 +71,10 @@ swr_status append_tokens(const swr_kv* kv, const void* k_new, const void* v_new,
   return to_status(swr::launch_append(p, kv->dtype == SWR_KV_FP8_E4M3, stream));
 }
 
+}  // namespace
+
+namespace swr {
+
 // Shared validation and launch of the attention calls.  mode is what the
 // caller asked for (decode, verify, global); `append` fuses the append of the
 // tokens in k_prop / v_prop (decode: the new token at pos; global: S tokens
@@ -160,6 +164,10 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
   return to_status(swr::launch_attention(pl, p, stream));
 }
 
+}  // namespace swr
+
+namespace {
+using swr::attend;
 }  // namespace
 
 namespace swr {

@@ -123,3 +123,16 @@ hipError_t launch_append(const AppendParams& p, int fp8, hipStream_t stream);
 hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace swr
+
+#include "swr.h"
+
+namespace swr {
+
+// Validation, planning and launch shared by the attention entry points
+// (swr_api.cpp): mode is MODE_DECODE, MODE_VERIFY or MODE_GLOBAL as asked
+// for; append fuses the append of the tokens in k_prop / v_prop.
+swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* out, const int32_t* pos,
+                  const int32_t* key_count, const void* k_prop, const void* v_prop, int cap_or_max_keys, int B,
+                  int S, int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace swr

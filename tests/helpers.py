@@ -8,9 +8,23 @@ import torch
 
 import oracle
 
-# Parity bar for bf16 attention outputs against the float64 oracle.
+# Parity bar for bf16 attention outputs against the float64 oracle: relative
+# L2 error over the whole output <= 5e-3, and per element |got - ref| <=
+# max(1e-2, one bf16 ulp of |ref|).  The element bound is the 1e-2 max-abs
+# bar wherever bf16 can meet it; an output of magnitude >= 2 (a row that sees
+# one to a few keys returns about a value itself) is spaced 2^-6 or more in
+# bf16, so rounding the softmax weights and the output to bf16 (2^-9
+# relative each) can pass 1e-2 alone -- there the bound is one ulp of the
+# output's binade, the size of those two roundings together.
 MAX_ABS_TOL = 1e-2
 REL_L2_TOL = 5e-3
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits); 2^-133 at 0."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
 
 
 def errors(got, ref):
@@ -25,10 +39,15 @@ def errors(got, ref):
 
 
 def assert_parity(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     max_abs, rel = errors(got, ref)
-    assert max_abs <= MAX_ABS_TOL and rel <= REL_L2_TOL, (
-        f"{what}: max-abs {max_abs:.3e} (tol {MAX_ABS_TOL}), rel-L2 {rel:.3e} (tol {REL_L2_TOL})")
+    bound = np.maximum(MAX_ABS_TOL, bf16_ulp(ref))
+    over = np.abs(got - ref) > bound
+    assert not over.any() and rel <= REL_L2_TOL, (
+        f"{what}: {int(over.sum())} elements past max(1e-2, 1 bf16 ulp) (max-abs {max_abs:.3e}), "
+        f"rel-L2 {rel:.3e} (tol {REL_L2_TOL})")
     return max_abs, rel
 
 

@@ -1,11 +1,14 @@
 """The attention calls captured in a HIP graph and replayed.
 
 A serving loop issues these short launches from a graph.  Each case runs the
-call eagerly on one copy of the inputs, captures it on a second copy, and
-replays the graph three times with other work and synchronisations in
-between; every replay must give the eager output bit for bit and leave the
-same region bytes (the library launches kernels only -- no memset or copy
-nodes -- and its workspace is the caller's, reused by every replay).
+call eagerly on one copy of the inputs, checks that eager result against the
+oracle (output at the parity bar, region bytes bit for bit), captures the
+call on a second copy, and replays the graph three times with other work and
+synchronisations in between; every replay must give the eager output bit for
+bit and leave the same region bytes (the library launches kernels only -- no
+memset or copy nodes -- and its workspace is the caller's, reused by every
+replay).  A multi-layer step in one graph is checked against the oracle in
+test_gpu_stack.py.
 """
 import numpy as np
 import pytest
@@ -14,8 +17,8 @@ import torch
 import oracle
 import sliding_window_ring_amd as swr
 import synthetic
-from gpu_common import dev_bf16, dev_i32, host_bits, layer
-from helpers import global_pools, ring_pools
+from gpu_common import dev_bf16, dev_i32, host_bits, host_f64, layer
+from helpers import assert_parity, global_pools, ring_pools
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +62,12 @@ def test_fused_decode_in_graph_split_k():
     out_e = swr.swa_append_decode(Le, kn, vn, q, pos, 0.0625, ws=ws)
     torch.cuda.synchronize()
     want = (host_bits(out_e), Le.k_base.cpu().numpy(), Le.v_base.cpu().numpy())
+    rk, rv = kp.copy(), vp.copy()
+    oracle.kv_append(rk, rv, ko, vo, w.W, oracle.BF16, 1.0, 1.0, kn.view(torch.int16).cpu().numpy().view(np.uint16)[:, None],
+                     vn.view(torch.int16).cpu().numpy().view(np.uint16)[:, None], x["pos"])
+    assert np.array_equal(want[1], rk) and np.array_equal(want[2], rv)
+    assert_parity(host_f64(out_e), oracle.swa_decode(rk, rv, ko, vo, w.W, oracle.BF16, 1.0, 1.0, x["q"], x["pos"],
+                                                      w.Hkv, 0.0625), "eager split-K fused decode")
     out_g = torch.empty_like(out_e)
     for rep, (o, kb, vb) in replay_and_check(
             lambda: swr.swa_append_decode(Lg, kn, vn, q, pos, 0.0625, out=out_g, ws=ws),
@@ -85,6 +94,14 @@ def fused_global_in_graph(x, S, cap, dtype, ks, vs):
     out_e = swr.global_append_attend(Le, kn, vn, q, p0, int(kc.max()), scale, ws=ws)
     torch.cuda.synchronize()
     want = (host_bits(out_e), Le.k_base.cpu().numpy(), Le.v_base.cpu().numpy())
+    rk, rv = kp.copy(), vp.copy()
+    kn_h = np.stack([x["k"][b, pos0[b]:kc[b]] for b in range(B)])
+    vn_h = np.stack([x["v"][b, pos0[b]:kc[b]] for b in range(B)])
+    oracle.kv_append(rk, rv, ko, vo, cap, dtype, ks, vs, kn_h, vn_h, pos0, wrap=False)
+    assert np.array_equal(want[1], rk) and np.array_equal(want[2], rv)
+    q_pos = (pos0[:, None] + np.arange(S, dtype=np.int32)[None, :]).astype(np.int32)
+    ref = oracle.global_attend(rk, rv, ko, vo, cap, dtype, ks, vs, x["q"], q_pos, kc, hkv, scale)
+    assert_parity(host_f64(out_e), ref, "eager fused global")
     out_g = torch.empty_like(out_e)
     for rep, (o, kb, vb) in replay_and_check(
             lambda: swr.global_append_attend(Lg, kn, vn, q, p0, int(kc.max()), scale, out=out_g, ws=ws),
@@ -122,6 +139,9 @@ def test_global_attend_in_graph():
     out_e = swr.global_attend(L, q, qp, kcs, w.key_count, w.Hkv, w.D ** -0.5, ws=ws)
     torch.cuda.synchronize()
     want = host_bits(out_e)
+    ref = oracle.global_attend(kp, vp, ko, vo, 6016, oracle.BF16, 1, 1, x["q"], x["q_pos"], x["key_count"], w.Hkv,
+                               w.D ** -0.5)
+    assert_parity(host_f64(out_e), ref, "eager global")
     out_g = torch.empty_like(out_e)
     for rep, (o,) in replay_and_check(
             lambda: swr.global_attend(L, q, qp, kcs, w.key_count, w.Hkv, w.D ** -0.5, out=out_g, ws=ws),

@@ -55,12 +55,12 @@ def test_pool_admit_zero_fills_each_region_and_nothing_else():
 
 @pytest.mark.gpu
 def test_ring_and_global_carves_zero_fill_their_regions_and_nothing_else():
-    # a ring of 1000 slots (rounded to 1008) and a global region of 6005
+    # a ring of 1001 slots (rounded to 1008) and a global region of 6005
     # tokens (rounded to 6016, the padded tail included) carved from a pool
     # whose bytes start non-zero
     pool = swr.Pool(32 << 20)
     pool.buffer.fill_(0x5A)
-    rk, rv, rcap = pool.alloc_ring(1000, 2, 64)
+    rk, rv, rcap = pool.alloc_ring(1001, 2, 64)
     gk, gv, gcap = pool.alloc_global(6005, 2, 512)
     torch.cuda.synchronize()
     assert (rcap, gcap) == (1008, 6016)
