@@ -247,6 +247,23 @@ swr_status swr_global_append_attend(const swr_kv* kv, const void* k_new, const v
                                     int max_key_count, int B, int S, int Hq, int Hkv, int D,
                                     float scale, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* swr_global_append_attend without a caller workspace, for callers that
+ * cannot allocate device memory (code under graph capture, serving loops
+ * that forbid allocation).  Same arguments, semantics and results as
+ * swr_global_append_attend minus ws / ws_bytes: the workspace is a static
+ * device array of the library, 16 MiB per device, held from module load
+ * until the process ends (its device address is looked up once per device,
+ * with that device current).  Allocates nothing.  SWR_ERR_WORKSPACE when
+ * the call needs more than 16 MiB (swr_workspace_bytes(
+ * SWR_OP_GLOBAL_APPEND_ATTEND, ...) > 16 MiB), checked before any launch.
+ * All calls on one device share the array and each call's partials are
+ * left in it: calls that may overlap on one device (other streams, other
+ * host threads) race and must not be issued. */
+swr_status swr_global_append_attend_noalloc(const swr_kv* kv, const void* k_new, const void* v_new,
+                                            const void* q, void* out, const int32_t* pos0,
+                                            int max_key_count, int B, int S, int Hq, int Hkv, int D,
+                                            float scale, hipStream_t stream);
+
 /* Workspace bytes an attention call needs (0 when it needs none).  For
  * decode and verify `cap_or_max_keys` is the window W; for global attention it
  * is max_key_count.  Returns 0 for unsupported shapes as well (the call then

@@ -31,7 +31,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace 
 
 EXPORTS = [
     "swr_ring_kv_append", "swr_swa_decode", "swr_swa_append_decode", "swr_gqa_verify", "swr_global_attend",
-    "swr_global_append_attend", "swr_workspace_bytes",
+    "swr_global_append_attend", "swr_global_append_attend_noalloc", "swr_workspace_bytes",
     "swr_kv_region_bytes", "swr_pool_create", "swr_pool_destroy", "swr_pool_alloc", "swr_pool_free",
     "swr_pool_alloc_ring", "swr_pool_alloc_global", "swr_pool_stats", "swr_pool_admit", "swr_pool_release", "swr_request_kv_bytes",
     "swr_zero_fill", "swr_paged_gather_window", "swr_read_ceiling",
@@ -69,6 +69,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "swr_gqa_verify": ([KV, P, P, P, P, P, I, I, I, I, I, F, P, SZ, P], I),
         "swr_global_attend": ([KV, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
         "swr_global_append_attend": ([KV, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P], I),
+        "swr_global_append_attend_noalloc": ([KV, P, P, P, P, P, I, I, I, I, I, I, F, P], I),
         "swr_workspace_bytes": ([I, I, I, I, I, I, I], SZ),
         "swr_kv_region_bytes": ([I, I, I, I], I64),
         "swr_pool_create": ([P, SZ, ctypes.POINTER(P)], I),
@@ -288,6 +289,25 @@ def global_append_attend(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, 
            lib.swr_global_append_attend(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
                                         _ptr(pos0), max_key_count, B, S, hq, hkv, d, scale, _ptr(ws), wsb,
                                         _stream(stream)))
+    return out
+
+
+def global_append_attend_noalloc(kv: KVLayer, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                                 pos0: torch.Tensor, max_key_count: int, scale: float,
+                                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """swr_global_append_attend_noalloc: global_append_attend with the
+    library's static device scratch as workspace (no allocation by the
+    library; `out` given by the caller allocates nothing here either)."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(q, "q", torch.bfloat16)
+    _dev(pos0, "pos0", torch.int32)
+    B, S, hq, d = q.shape
+    hkv = k_new.shape[2]
+    out = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16)
+    _check("swr_global_append_attend_noalloc",
+           lib.swr_global_append_attend_noalloc(ctypes.byref(kv.c()), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                                _ptr(pos0), max_key_count, B, S, hq, hkv, d, scale, _stream(stream)))
     return out
 
 

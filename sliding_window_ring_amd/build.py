@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswr.so")
-SOURCES = ["attn.hip", "chunked.hip", "append.hip", "gather.hip", "read_ceiling.hip", "swr_api.cpp"]
+SOURCES = ["attn.hip", "chunked.hip", "append.hip", "gather.hip", "read_ceiling.hip", "noalloc.hip", "swr_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
