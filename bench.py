@@ -40,28 +40,40 @@ B, HKV, G, D, W = 56, 8, 8, 256, 1024          # sliding decode layer
 GB_, GHKV, GG, GD, GS, KC = 1, 2, 8, 512, 4, 6005  # global verify layer
 N_SLIDING_SETS, N_GLOBAL_SETS = 3, 24
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "swa_decode_b56_hbm_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "sliding_window_ring_amd", "csrc", f)
-                  for f in ("attn.hip", "swr_device.h", "swr_internal.h")]
+# Counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a 1 GiB
+# copy) of the kernels each roofline entry covers, and the sources those
+# kernels are built from: a summary is reported only while the sources still
+# hash to the value recorded in it.
+CSRC = os.path.join(ROOT, "sliding_window_ring_amd", "csrc")
+TRAFFIC = {
+    "decode": (os.path.join(ROOT, "profiles", "swa_decode_b56_hbm_traffic.json"),
+               [os.path.join(CSRC, f) for f in ("attn.hip", "swr_device.h", "swr_internal.h")]),
+    "global": (os.path.join(ROOT, "profiles", "global_verify_6005_hbm_traffic.json"),
+               [os.path.join(CSRC, f) for f in ("chunked.hip", "swr_device.h", "swr_internal.h")]),
+    "verify": (os.path.join(ROOT, "profiles", "sliding_verify_b8_hbm_traffic.json"),
+               [os.path.join(CSRC, f) for f in ("chunked.hip", "swr_device.h", "swr_internal.h")]),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch_algo):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def measured_traffic(which):
+    """HBM bytes per launch (per layer for the two-launch forms) from the
+    committed counter summary, if it was taken on the current kernel
+    sources; else None."""
+    path, sources = TRAFFIC[which]
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(path) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
-    if s.get("kernel_source_hash") != kernel_source_hash():
+    if s.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return s.get("hbm_bytes_per_launch")
 
@@ -121,53 +133,137 @@ def algorithmic_bytes():
     return decode, append_s, glob, append_g
 
 
-def cpu_baseline(seconds: float = 12.0):
-    """The oracle on a bounded sample of the same workload: 16 of the 56
-    decode requests plus the global verify, repeated for about `seconds`."""
+def cpu_baseline():
+    """The oracle as it stands (binary64 C, OpenMP over (request, KV head)
+    units) on the host's cores, per workload: the median of 3 runs with all
+    threads and of 3 with one thread, in us per layer, on the same synthetic
+    inputs the tests use.  The large layers are timed on stated samples and
+    scaled by the keys they hold (the oracle's time is linear in units x
+    keys); the regions are built in the oracle's own logical form.  `value`
+    is the headline step's rate on this baseline: the B=56 decode layer plus
+    the 6005-key verify layer."""
+    import statistics
+
     import numpy as np
 
     import oracle
     import synthetic
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from helpers import global_pools, ring_pools
+    oracle.build()
+    threads = oracle.num_threads()
 
-    nb = 16
-    w = synthetic.Workload("sample", B=nb, Hkv=HKV, G=G, D=D, W=W, pos_lo=1024, pos_hi=4096)
-    x = synthetic.sliding_decode(w, seed=synthetic.SEED_BASE + 2)
-    kp, vp, ko, vo = ring_pools(x["k"], x["v"], x["start"], x["n"], W)
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts) * 1e6
+
+    def both(fn):
+        t_all = med3(fn)
+        prev = oracle.set_threads(1)
+        t_one = med3(fn)
+        oracle.set_threads(prev)
+        return t_all, t_one
+
+    def ring_logical(k, v, start, n, w, dtype=oracle.BF16, ks=1.0, vs=1.0):
+        B = k.shape[0]
+        lrb = oracle.logical_region_bytes(w, k.shape[2], k.shape[3], dtype)
+        kl, vl = np.zeros(B * lrb, np.uint8), np.zeros(B * lrb, np.uint8)
+        offs = np.arange(B, dtype=np.int64) * lrb
+        oracle.kv_append_logical(kl, vl, offs, w, dtype, ks, vs, k, v, start, n, wrap=True)
+        return kl, vl, offs
+
+    res = {}
+    # sliding decode B=56 (W=1024, 8 x 256): 8 of the 56 requests, x 7
+    ws2 = synthetic.Workload("sample", B=8, Hkv=HKV, G=G, D=D, W=W, pos_lo=1024, pos_hi=4096)
+    x = synthetic.sliding_decode(ws2, seed=synthetic.SEED_BASE + 2)
+    kl, vl, offs = ring_logical(x["k"], x["v"], x["start"], x["n"], W)
+    t_all, t_one = both(lambda: oracle.swa_decode_logical(kl, vl, offs, W, oracle.BF16, 1, 1, x["q"], x["pos"],
+                                                          HKV, D ** -0.5))
+    res["sliding_decode_b56"] = {"oracle_us_per_layer": round(t_all * 7, 1), "oracle_us_per_layer_1_thread":
+                                 round(t_one * 7, 1), "threads": min(threads, 8 * HKV),
+                                 "sample": "8 of the 56 requests (full windows), time x 7"}
+    # sliding verify B=8 (S=4, 32 rows per KV head): whole
+    wv = synthetic.SWA_VERIFY
+    x = synthetic.sliding_verify()
+    kl, vl, offs = ring_logical(x["k"], x["v"], x["start"], x["n"], wv.W)
+    t_all, t_one = both(lambda: oracle.gqa_verify_logical(kl, vl, offs, wv.W, oracle.BF16, 1, 1, x["k_prop"],
+                                                          x["v_prop"], x["q"], x["p0"], wv.Hkv, wv.D ** -0.5))
+    res["sliding_verify_b8"] = {"oracle_us_per_layer": round(t_all, 1), "oracle_us_per_layer_1_thread": round(t_one, 1),
+                                "threads": min(threads, wv.B * wv.Hkv), "sample": "whole layer"}
+    # global verify, 6005 keys (padded contraction over 6016): whole
     gx = synthetic.global_verify()
-    gk, gv, gko, gvo = global_pools(gx["k"], gx["v"], gx["key_count"], 6016)
-    per_rep = nb * HKV * W * D * 4 + 2 * nb * HKV * G * D * 2 + algorithmic_bytes()[2]
-    def run(budget):
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.swa_decode(kp, vp, ko, vo, W, oracle.BF16, 1, 1, x["q"], x["pos"], HKV, 1 / 16)
-            oracle.global_attend(gk, gv, gko, gvo, 6016, oracle.BF16, 1, 1, gx["q"], gx["q_pos"], gx["key_count"],
-                                 GHKV, GD ** -0.5)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget:
-                return reps, el
-
-    cores = oracle.num_threads()
-    reps, el = run(seconds)
-    prev = oracle.set_threads(1)
-    reps1, el1 = run(seconds / 2)
-    oracle.set_threads(prev)
+    lrb = oracle.logical_region_bytes(6016, GHKV, GD, oracle.BF16)
+    gk, gv, goff = np.zeros(lrb, np.uint8), np.zeros(lrb, np.uint8), np.zeros(1, np.int64)
+    oracle.kv_append_logical(gk, gv, goff, 6016, oracle.BF16, 1, 1, gx["k"], gx["v"], np.zeros(1, np.int32),
+                             gx["key_count"], wrap=False)
+    t_all, t_one = both(lambda: oracle.global_attend_logical(gk, gv, goff, 6016, oracle.BF16, 1, 1, gx["q"],
+                                                             gx["q_pos"], gx["key_count"], GHKV, GD ** -0.5))
+    res["global_verify_6005"] = {"oracle_us_per_layer": round(t_all, 1), "oracle_us_per_layer_1_thread":
+                                 round(t_one, 1), "threads": min(threads, GHKV), "sample": "whole layer"}
+    # mixed step (16 requests, contexts log-uniform [512, 65536]): the sliding
+    # layer whole, the global layer on every eighth request, scaled by keys
+    ctx = [int(c) for c in synthetic.mixed_contexts()]
+    seed = synthetic.SEED_BASE + 5
+    msw, mgw = synthetic.MIXED_SLIDING, synthetic.MIXED_GLOBAL
+    sample = list(range(0, len(ctx), 8))
+    key_scale = sum(c + 1 for c in ctx) / sum(ctx[b] + 1 for b in sample)
+    g = synthetic.rng(seed)
+    qs = synthetic.normal_bf16(g, (len(ctx), msw.Hq, msw.D))
+    qg = synthetic.normal_bf16(g, (len(sample), 1, mgw.Hq, mgw.D))
+    ring = [synthetic.request_tokens(seed, 2 * b, min(c + 1, msw.W), msw.Hkv, msw.D) for b, c in enumerate(ctx)]
+    glob = [synthetic.request_tokens(seed, 2 * b + 1, ctx[b] + 1, mgw.Hkv, mgw.D) for b in sample]
+    for dtype, name in ((oracle.BF16, "mixed_step_bf16"), (oracle.FP8, "mixed_step_fp8")):
+        amax = lambda arrs: float(max(np.abs(synthetic.bf16_to_f32(a)).max() for a in arrs)) / 448.0
+        sks, svs = (amax([r[0] for r in ring]), amax([r[1] for r in ring])) if dtype else (1.0, 1.0)
+        gks, gvs = (amax([r[0] for r in glob]), amax([r[1] for r in glob])) if dtype else (1.0, 1.0)
+        lrb = oracle.logical_region_bytes(msw.W, msw.Hkv, msw.D, dtype)
+        skl, svl = np.zeros(len(ctx) * lrb, np.uint8), np.zeros(len(ctx) * lrb, np.uint8)
+        soff = np.arange(len(ctx), dtype=np.int64) * lrb
+        for b, c in enumerate(ctx):
+            n = ring[b][0].shape[0]
+            oracle.kv_append_logical(skl, svl, soff[b:b + 1], msw.W, dtype, sks, svs, ring[b][0][None],
+                                     ring[b][1][None], [c - n + 1])
+        caps = [-(-(ctx[b] + 1) // 64) * 64 for b in sample]
+        glr = [oracle.logical_region_bytes(cp, mgw.Hkv, mgw.D, dtype) for cp in caps]
+        goffs = np.concatenate([[0], np.cumsum(glr)[:-1]]).astype(np.int64)
+        gkl, gvl = np.zeros(int(sum(glr)), np.uint8), np.zeros(int(sum(glr)), np.uint8)
+        for i, b in enumerate(sample):
+            oracle.kv_append_logical(gkl, gvl, goffs[i:i + 1], caps[i], dtype, gks, gvs, glob[i][0][None],
+                                     glob[i][1][None], [0], wrap=False, caps=[caps[i]])
+        pos = np.asarray(ctx, np.int32)
+        gpos = np.asarray([ctx[b] for b in sample], np.int32)
+        ts_all, ts_one = both(lambda: oracle.swa_decode_logical(skl, svl, soff, msw.W, dtype, sks, svs, qs, pos,
+                                                                msw.Hkv, msw.D ** -0.5))
+        tg_all, tg_one = both(lambda: oracle.global_attend_logical(gkl, gvl, goffs, max(caps), dtype, gks, gvs, qg,
+                                                                   gpos[:, None], gpos + 1, mgw.Hkv, mgw.D ** -0.5,
+                                                                   caps=caps))
+        res[name] = {"oracle_us_per_layer": round(ts_all + tg_all * key_scale, 1),
+                     "oracle_us_per_layer_1_thread": round(ts_one + tg_one * key_scale, 1),
+                     "threads": {"sliding": min(threads, len(ctx) * msw.Hkv),
+                                 "global_sample": min(threads, len(sample) * mgw.Hkv)},
+                     "sample": f"one sliding layer (16 requests) + one global layer timed on requests {sample} "
+                               f"({len(sample) * mgw.Hkv} units, so at most that many threads) and scaled by keys "
+                               f"(x {key_scale:.2f})"}
+    b_dec, b_app_s, b_glob, b_app_g = algorithmic_bytes()
+    step_us = res["sliding_decode_b56"]["oracle_us_per_layer"] + res["global_verify_6005"]["oracle_us_per_layer"]
+    step_us1 = res["sliding_decode_b56"]["oracle_us_per_layer_1_thread"] + \
+        res["global_verify_6005"]["oracle_us_per_layer_1_thread"]
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    return {"value": round(per_rep * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+    return {"value": round((b_dec + b_glob) / (step_us * 1e-6) / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} repetitions of: sliding decode for 16 of the 56 requests (full 1024-key windows, "
-                      f"8 KV heads x 256) + the 6005-key global verify; binary64 C oracle, {el:.1f} s",
-            "value_1_thread": round(per_rep * reps1 / el1 / 1e9, 4),
-            "sample_1_thread": f"{reps1} repetitions of the same, one OpenMP thread, {el1:.1f} s",
-            "host": {"cpu": cpu, "logical_cpus": os.cpu_count()}}
+            "sample": "the step's two layers: sliding decode B=56 (timed on 8 of the 56 requests, x 7) + the "
+                      "6005-key global verify; binary64 C oracle, median of 3 runs",
+            "value_1_thread": round((b_dec + b_glob) / (step_us1 * 1e-6) / 1e9, 4),
+            "per_config": res,
+            "host": {"cpu": cpu, "logical_cpus": os.cpu_count(), "oracle_threads": threads}}
 
 
 def _timed(torch, fn, reps, sets):
@@ -215,7 +311,7 @@ def paged_baseline(swr, torch, randn, gen, dev, page_tokens=16):
         L = swr.KVLayer(kb, vb, off, off.clone(), w.W)
         q = randn(w.B, w.Hq, w.D)
         sets.append((kp, vp, torch.from_numpy(bt).to(dev), pos, L, q, torch.empty_like(q)))
-    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W)),
+    ws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W)),
                      dtype=torch.uint8, device=dev)
 
     def gather(i):
@@ -318,9 +414,9 @@ def decode_stack(swr, torch, randn, dev):
     kn_s, vn_s = randn(B, HKV, D), randn(B, HKV, D)
     kn_g, vn_g = randn(B, 1, GHKV, GD), randn(B, 1, GHKV, GD)
     out_s, out_g = torch.empty_like(q_s), torch.empty_like(q_g)
-    dws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W)),
+    dws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W)),
                       dtype=torch.uint8, device=dev)
-    gws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, GHKV * GG, GHKV, GD,
+    gws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, GHKV * GG, GHKV, GD,
                                                   max(ctx) + 1)), dtype=torch.uint8, device=dev)
 
     def step():
@@ -357,6 +453,62 @@ def decode_stack(swr, torch, randn, dev):
             "note": "one HIP graph of the 60 fused append + attention calls; every layer on K/V of its own"}
 
 
+def global_verify_fp8(swr, torch, randn, dev, n_layers=48):
+    """The 6005-key global verify layer over fp8 e4m3 regions: 48 layers of
+    12.3 MB (590 MB, more than twice the last-level cache), each captured in
+    one HIP graph as the bf16 layers are; the attention call alone and the
+    call that appends its 4 proposals first (bf16 tokens in, codes stored)."""
+    fp8 = swr.SWR_KV_FP8_E4M3
+    sc = 4.5 / 448
+    pool = swr.Pool(n_layers * 2 * swr.region_bytes(6016, GHKV, GD, fp8) + (1 << 20))
+    layers = []
+    for _ in range(n_layers):
+        k_off, v_off, cap = pool.alloc_global(KC, GHKV, GD, fp8)
+        L = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor([k_off], device=dev), torch.tensor([v_off], device=dev),
+                        cap, fp8, sc, sc)
+        ctx = KC - GS
+        swr.ring_kv_append(L, randn(1, ctx, GHKV, GD), randn(1, ctx, GHKV, GD),
+                           torch.zeros(1, device=dev, dtype=torch.int32), wrap=False)
+        q = randn(1, GS, GHKV * GG, GD)
+        layers.append(dict(L=L, ctx=torch.tensor([ctx], device=dev, dtype=torch.int32),
+                           q_pos=torch.arange(ctx, KC, device=dev, dtype=torch.int32).view(1, GS),
+                           kc=torch.tensor([KC], device=dev, dtype=torch.int32), k_prop=randn(1, GS, GHKV, GD),
+                           v_prop=randn(1, GS, GHKV, GD), q=q, out=torch.empty_like(q)))
+    ws = torch.zeros(max(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC),
+                         swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC), 16),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def graph_us(layer_fn):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for g in layers:
+                layer_fn(g)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / (reps * len(layers)) * 1e3
+
+    us_attn = graph_us(lambda g: swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, GD ** -0.5,
+                                                   out=g["out"], ws=ws))
+    us_fused = graph_us(lambda g: swr.global_append_attend(g["L"], g["k_prop"], g["v_prop"], g["q"], g["ctx"], KC,
+                                                           GD ** -0.5, out=g["out"], ws=ws))
+    attn_bytes = KC * GHKV * GD * 2 + 2 * GS * GHKV * GG * GD * 2
+    fused_bytes = attn_bytes + GS * GHKV * GD * (2 + 1) * 2
+    del layers, pool
+    torch.cuda.empty_cache()
+    return ({"us": round(us_attn, 2), "GB/s": round(attn_bytes / us_attn / 1e3, 1), "algorithmic_bytes": attn_bytes,
+             "layers_in_graph": n_layers},
+            {"us": round(us_fused, 2), "GB/s": round(fused_bytes / us_fused / 1e3, 1), "algorithmic_bytes": fused_bytes,
+             "layers_in_graph": n_layers})
+
+
 def other_workloads(swr, torch, sweep=True):
     """The remaining workloads, each timed on its own (us per call, GB/s of
     algorithmic bytes): sliding verify B=8, fp8 sliding decode B=56, the B=56
@@ -386,19 +538,39 @@ def other_workloads(swr, torch, sweep=True):
         swr.ring_kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
         q = randn(w.B, w.S, w.Hq, w.D)
         sets.append((L, randn(w.B, w.S, w.Hkv, w.D), randn(w.B, w.S, w.Hkv, w.D), q, p0, torch.empty_like(q)))
-    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, w.B, w.S, w.Hq, w.Hkv, w.D, w.W)),
+    ws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, w.B, w.S, w.Hq, w.Hkv, w.D, w.W)),
                      dtype=torch.uint8, device=dev)
     us = _timed(torch, lambda i: swr.gqa_verify(sets[i][0], sets[i][1], sets[i][2], sets[i][3], sets[i][4],
                                                 w.D ** -0.5, out=sets[i][5], ws=ws), 100, len(sets))
-    nbytes = w.B * w.Hkv * w.W * w.D * 4 + 2 * w.B * w.S * w.Hkv * w.D * 2 + 2 * w.B * w.S * w.Hq * w.D * 2
+    nbytes = w.B * w.Hkv * (w.W - 1) * w.D * 4 + 2 * w.B * w.S * w.Hkv * w.D * 2 + 2 * w.B * w.S * w.Hq * w.D * 2
     res["sliding_verify_b8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
-                                "algorithmic_bytes": nbytes}
+                                "algorithmic_bytes": nbytes, "sets": len(sets)}
+    del sets
+
+    # --- the same verify over fp8 rings (16 sets of 33.6 MB: twice the last-level cache)
+    sets = []
+    for _ in range(16):
+        rb = swr.region_bytes(w.W, w.Hkv, w.D, swr.SWR_KV_FP8_E4M3)
+        kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
+        vb = torch.empty_like(kb)
+        off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+        L = swr.KVLayer(kb, vb, off, off.clone(), w.W, swr.SWR_KV_FP8_E4M3, 4.5 / 448, 4.5 / 448)
+        p0 = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+        swr.ring_kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
+        q = randn(w.B, w.S, w.Hq, w.D)
+        sets.append((L, randn(w.B, w.S, w.Hkv, w.D), randn(w.B, w.S, w.Hkv, w.D), q, p0, torch.empty_like(q)))
+    us = _timed(torch, lambda i: swr.gqa_verify(sets[i][0], sets[i][1], sets[i][2], sets[i][3], sets[i][4],
+                                                w.D ** -0.5, out=sets[i][5], ws=ws), 100, len(sets))
+    nbytes = w.B * w.Hkv * (w.W - 1) * w.D * 2 + 2 * w.B * w.S * w.Hkv * w.D * 2 + 2 * w.B * w.S * w.Hq * w.D * 2
+    res["sliding_verify_b8_fp8"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                    "algorithmic_bytes": nbytes, "sets": len(sets)}
     del sets, ws
 
-    # --- one GPU's share of the B=56 decode under KV-head sharding (8 GPUs, one KV head each)
+    # --- one GPU's share of the B=56 decode under KV-head sharding (8 GPUs, one KV head each):
+    # 10 sets of 58.7 MB, more than twice the 256 MB last-level cache
     w = synthetic.SWA_DECODE
     sets = []
-    for _ in range(3):
+    for _ in range(10):
         rb = swr.region_bytes(w.W, 1, w.D)
         kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
         vb = torch.empty_like(kb)
@@ -408,13 +580,13 @@ def other_workloads(swr, torch, sweep=True):
         swr.ring_kv_append(L, randn(w.B, w.W, 1, w.D), randn(w.B, w.W, 1, w.D), (pos - w.W + 1).to(torch.int32))
         q = randn(w.B, w.G, w.D)
         sets.append((L, q, pos, torch.empty_like(q)))
-    hws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.G, 1, w.D, w.W)),
+    hws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, w.B, 1, w.G, 1, w.D, w.W)),
                       dtype=torch.uint8, device=dev)
     us = _timed(torch, lambda i: swr.swa_decode(sets[i][0], sets[i][1], sets[i][2], 1, w.D ** -0.5, out=sets[i][3],
                                                 ws=hws), 60, len(sets))
     nbytes = w.B * w.W * w.D * 4 + 2 * w.B * w.G * w.D * 2
     res["sliding_decode_b56_one_kv_head_share"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
-                                                   "algorithmic_bytes": nbytes}
+                                                   "algorithmic_bytes": nbytes, "sets": len(sets)}
     del sets, hws
 
     # --- fp8 sliding decode, B=56
@@ -449,6 +621,10 @@ def other_workloads(swr, torch, sweep=True):
     # window in 16-token pages scattered over a page pool, gathered into a
     # ring-layout workspace every step, then the same decode kernel
     res["sliding_decode_b56_paged_gather_baseline"] = paged_baseline(swr, torch, randn, gen, dev)
+
+    # --- the global verify layer over fp8 regions, in a layer graph
+    res["global_verify_6005_fp8_attention_only_in_graph"], res["global_verify_6005_fp8_in_layer_graph"] = \
+        global_verify_fp8(swr, torch, randn, dev)
 
     # --- mixed step: 16 requests, contexts log-uniform [512, 65536], one pool
     ctx = [int(c) for c in synthetic.mixed_contexts()]
@@ -490,9 +666,9 @@ def other_workloads(swr, torch, sweep=True):
         qs = randn(B, ws_s.Hq, ws_s.D)
         qg = randn(B, 1, ws_g.Hq, ws_g.D)
         kc = pos + 1
-        dws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, ws_s.Hq, ws_s.Hkv, ws_s.D,
+        dws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, ws_s.Hq, ws_s.Hkv, ws_s.D,
                                                       ws_s.W)), dtype=torch.uint8, device=dev)
-        gws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv, ws_g.D,
+        gws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv, ws_g.D,
                                                       max(ctx) + 1)), dtype=torch.uint8, device=dev)
         outs, outg = torch.empty_like(qs), torch.empty_like(qg)
         torch.cuda.synchronize()
@@ -512,7 +688,7 @@ def other_workloads(swr, torch, sweep=True):
         # at position ctx, already in the regions above, is written again)
         kn_s, vn_s = randn(B, ws_s.Hkv, ws_s.D), randn(B, ws_s.Hkv, ws_s.D)
         kn_g, vn_g = randn(B, 1, ws_g.Hkv, ws_g.D), randn(B, 1, ws_g.Hkv, ws_g.D)
-        fws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv,
+        fws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, ws_g.Hq, ws_g.Hkv,
                                                       ws_g.D, max(ctx) + 1)), dtype=torch.uint8, device=dev)
 
         def mixed_fused(_i):
@@ -544,7 +720,7 @@ def other_workloads(swr, torch, sweep=True):
     qpos = (counts.view(-1, 1) - GS + torch.arange(GS, device=dev, dtype=torch.int32).view(1, -1)).contiguous()
     q = randn(1, GS, GHKV * GG, GD)
     out = torch.empty_like(q)
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, hi), dtype=torch.uint8,
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, hi), dtype=torch.uint8,
                      device=dev)
     n = counts.numel()
     # three launches back to back per key count, each between its own events;
@@ -607,10 +783,10 @@ def main():
         N_GLOBAL_SETS * 2 * swr.region_bytes(6016, GHKV, GD) + (1 << 20)
     pool = swr.Pool(per_layer_pool)
     sliding, glob = build_layers(swr, torch, pool)
-    gws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC),
+    gws = torch.zeros(max(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC),
                           swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 1, GS, GHKV * GG, GHKV, GD, KC), 16),
                       dtype=torch.uint8, device="cuda")
-    dws = torch.empty(max(swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W), 16),
+    dws = torch.zeros(max(swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, HKV * G, HKV, D, W), 16),
                       dtype=torch.uint8, device="cuda")
     scale_s, scale_g = D ** -0.5, GD ** -0.5
 
@@ -701,7 +877,8 @@ def main():
     step_bytes = b_dec + b_app_s + b_glob + b_app_g
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = (b_dec + b_app_s) / (sliding_b2b_us * 1e-6) / 1e9
-    traffic = measured_traffic(b_dec + b_app_s)
+    glob_achieved = (b_glob + b_app_g) / (global_graph_us * 1e-6) / 1e9
+    traffic = measured_traffic("decode")
     ceiling = read_ceiling(swr, torch)
 
     result = {
@@ -754,12 +931,49 @@ def main():
             "algorithmic_bytes_per_launch": b_dec + b_app_s,
             "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4),
         },
+        # the other target: the global verify layer (chunk pass + merge, with
+        # its append), its own algorithmic bytes over its time per layer in a
+        # 24-layer graph
+        "roofline_global_verify": {
+            "kernel": "chunk_kernel<512,2,bf16,global> + merge_grouped<512> (swr_global_append_attend, 6005 keys, "
+                      "per layer of a 24-layer graph)",
+            "bound": "hbm",
+            "achieved": round(glob_achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(glob_achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("global"),
+            "algorithmic_bytes_per_launch": b_glob + b_app_g,
+            "us_per_layer": round(global_graph_us, 2),
+            "floor_us": round((b_glob + b_app_g) / HBM_PEAK_GBS / 1e3, 2),
+        },
         "host_wall_s": round(wall, 3),
     }
     if not args.no_extra:
-        result["other_workloads"] = other_workloads(swr, torch, sweep=not args.no_sweep)
+        result["other_workloads"] = ow = other_workloads(swr, torch, sweep=not args.no_sweep)
+        v = ow["sliding_verify_b8"]
+        result["roofline_sliding_verify"] = {
+            "kernel": "chunk_kernel<256,2,bf16,verify> + merge_flat (swr_gqa_verify, B=8, W=1024, S=4)",
+            "bound": "hbm",
+            "achieved": v["GB/s"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(v["GB/s"] / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("verify"),
+            "algorithmic_bytes_per_launch": v["algorithmic_bytes"],
+            "us_per_layer": v["us"],
+            "floor_us": round(v["algorithmic_bytes"] / HBM_PEAK_GBS / 1e3, 2),
+        }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cb = cpu_baseline()
+        pc = cb["per_config"]
+        pc["sliding_decode_b56"]["gpu_us_per_layer"] = round(decode_only_us, 2)
+        pc["global_verify_6005"]["gpu_us_per_layer"] = round(global_attn_graph_us, 2)
+        if not args.no_extra:
+            ow = result["other_workloads"]
+            pc["sliding_verify_b8"]["gpu_us_per_layer"] = ow["sliding_verify_b8"]["us"]
+            pc["mixed_step_bf16"]["gpu_us_per_layer"] = ow["mixed_step_bf16"]["us"]
+            pc["mixed_step_fp8"]["gpu_us_per_layer"] = ow["mixed_step_fp8"]["us"]
     print(json.dumps(result))
 
 

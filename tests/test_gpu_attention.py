@@ -262,7 +262,7 @@ def test_global_sweep_each_count_as_launched(group):
     q = synthetic.normal_bf16(synthetic.rng(37 + group), (1, 4, 16, 512))
     qd = dev_bf16(q)
     scale = 512 ** -0.5
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, 4, 16, 2, 512, 8192), dtype=torch.uint8,
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, 4, 16, 2, 512, 8192), dtype=torch.uint8,
                      device="cuda")
     outs = []
     for kc in counts:

@@ -55,7 +55,7 @@ def test_fused_decode_in_graph_split_k():
     kn = dev_bf16(np.ascontiguousarray(x["k"][np.arange(w.B), x["n"] - 1]))
     vn = dev_bf16(np.ascontiguousarray(x["v"][np.arange(w.B), x["n"] - 1]))
     q, pos = dev_bf16(x["q"]), dev_i32(x["pos"])
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W),
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W),
                      dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0
     Le, Lg = copies(kp, vp, ko, vo, w.W)
@@ -87,7 +87,7 @@ def fused_global_in_graph(x, S, cap, dtype, ks, vs):
     vn = dev_bf16(np.stack([x["v"][b, pos0[b]:kc[b]] for b in range(B)]))
     q, p0 = dev_bf16(x["q"]), dev_i32(pos0)
     Hq = x["q"].shape[2]
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, S, Hq, hkv, D, int(kc.max())),
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, S, Hq, hkv, D, int(kc.max())),
                      dtype=torch.uint8, device="cuda")
     Le, Lg = copies(kp, vp, ko, vo, cap, dtype, ks, vs)
     scale = D ** -0.5
@@ -134,7 +134,7 @@ def test_global_attend_in_graph():
     kp, vp, ko, vo = global_pools(x["k"], x["v"], x["key_count"], 6016)
     L = layer(kp, vp, ko, vo, 6016)
     q, qp, kcs = dev_bf16(x["q"]), dev_i32(x["q_pos"]), dev_i32(x["key_count"])
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, w.S, w.Hq, w.Hkv, w.D, w.key_count),
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 1, w.S, w.Hq, w.Hkv, w.D, w.key_count),
                      dtype=torch.uint8, device="cuda")
     out_e = swr.global_attend(L, q, qp, kcs, w.key_count, w.Hkv, w.D ** -0.5, ws=ws)
     torch.cuda.synchronize()
@@ -173,7 +173,7 @@ def test_paged_gather_then_decode_in_graph():
     start = g.integers(0, 256, B * rb, dtype=np.uint8)
     off = np.arange(B, dtype=np.int64) * rb
     Le, Lg = copies(start, start, off, off, W)
-    ws = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, hkv * G, hkv, d, W)),
+    ws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_DECODE, B, 1, hkv * G, hkv, d, W)),
                      dtype=torch.uint8, device="cuda")  # 10 units: split-K with its combine
     swr.paged_gather_window(kpages, vpages, bt, pos_d, Le)
     out_e = swr.swa_decode(Le, q, pos_d, hkv, d ** -0.5, ws=ws)

@@ -135,7 +135,7 @@ def test_global_back_to_back_calls_share_a_workspace():
     different inputs and one workspace both match the oracle."""
     kc = 3000
     w = synthetic.Workload("t", B=2, Hkv=2, G=8, D=512, S=4, key_count=kc)
-    ws = torch.empty(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 2, 4, 16, 2, 512, kc), dtype=torch.uint8,
+    ws = torch.zeros(swr.workspace_bytes(swr.SWR_OP_GLOBAL_ATTEND, 2, 4, 16, 2, 512, kc), dtype=torch.uint8,
                      device="cuda")
     for seed in (51, 52, 53):
         x = synthetic.global_verify(w, seed=seed)

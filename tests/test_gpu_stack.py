@@ -87,9 +87,9 @@ def test_decode_stack_in_one_graph_matches_oracle(dtype):
                                 q=torch.empty(B, 1, hq_g, GD, dtype=torch.bfloat16, device="cuda"),
                                 out=torch.empty(B, 1, hq_g, GD, dtype=torch.bfloat16, device="cuda"))
     pos = dev_i32(POS0)
-    ws_s = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, hq_s, SHKV, SD, W)),
+    ws_s = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, hq_s, SHKV, SD, W)),
                        dtype=torch.uint8, device="cuda")
-    ws_g = torch.empty(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, hq_g, GHKV, GD, cap_g)),
+    ws_g = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, B, 1, hq_g, GHKV, GD, cap_g)),
                        dtype=torch.uint8, device="cuda")
     assert swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, B, 1, hq_s, SHKV, SD, W) > 0  # split combine runs
 
