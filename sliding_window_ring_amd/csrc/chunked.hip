@@ -25,8 +25,10 @@
 //     the page on its chunk -- scores (bf16 MFMA, fp32), the masked softmax
 //     over the chunk, and P x V (bf16 MFMA, fp32) -- with Q, the scores and
 //     P kept in LDS, and writes the chunk's unnormalised rows with their
-//     (max, sum).  In a verify call chunk 0 of each (request, KV head) holds
-//     the proposals (read from their own buffers) and chunks 1.. the ring.
+//     (max, sum).  In a verify call ring chunk 0 of each (request, KV head)
+//     also takes the S proposals (read from their own buffers) as one more
+//     step: a separate proposal workgroup would start only when a ring
+//     chunk leaves its CU, a second round at the end of the pass.
 //   pass 2: merges the chunk partials, weights 2^(m_c - M), sums in a fixed
 //     order, division by the weighted row sum.  With many chunks per row
 //     (global) one workgroup per (request, KV head, row, quarter of the
@@ -87,7 +89,7 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
   }
   const int ck = MODE == MODE_VERIFY ? kVerifyChunkKeys : kChunkKeys;
   const int n = (region_keys<MODE>(p, b) + ck - 1) / ck;
-  return min(n + (MODE == MODE_VERIFY ? 1 : 0), p.nchunk);
+  return min(MODE == MODE_VERIFY ? max(n, 1) : n, p.nchunk);  // verify: chunk 0 holds the proposals
 }
 
 // One workgroup per (request, KV head, chunk), sixteen waves.  Every K and
@@ -108,8 +110,8 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 //   values   waves w < PVW: O^T(dims w*DPW .. +DPW, rows) = V^T . P^T over
 //            the chunk, bf16 MFMA into fp32; the unnormalised rows go to the
 //            workspace for pass 2 with streaming stores.
-// A verify ring chunk is 256 keys taken as two 128-key halves in turn (K of
-// both on entry, V of both after the first half's scores), the softmax
+// A verify ring chunk is 256 keys taken as two 128-key halves in turn (Q,
+// then K of both on entry, V of both after the first half's scores), the softmax
 // lanes carrying each row's running (max, sum) from one half to the next
 // and the value waves rescaling their rows by the factor the softmax lanes
 // leave in LDS: one partial per 256 keys, so pass 1 writes and pass 2 reads
@@ -117,10 +119,10 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 // Masks: global -- key < key_count and key <= q_pos of the row's position;
 // verify ring chunk -- a committed slot no older than W-2-i positions before
 // pos0-1 for proposal i (position pos0+i sees positions >= pos0+i-W+1);
-// verify proposal chunk -- proposal j <= i.  Over an fp8 ring the proposals
+// verify proposal step -- proposal j <= i.  Over an fp8 ring the proposals
 // are bf16 values: their scores take scale * log2(e) without k_scale, and
-// their accumulated values are divided by v_scale (in fp32) before the
-// store, since pass 2 multiplies every chunk by v_scale.
+// their P is divided by v_scale before its bf16 rounding, since pass 2
+// multiplies every chunk by v_scale.
 // Fused append (a global call storing its own S tokens at pos0 .. pos0+S-1):
 // the chunk holding their slots takes them in place of the slots' old
 // contents, and the merge pass stores them (below).
@@ -176,6 +178,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   constexpr int NDT = DPW / 16;                      // 16-dim value tiles per value wave
   constexpr int KS = CK / 32;                        // 32-key k steps of the value product
   constexpr int NH = MODE == MODE_VERIFY ? 2 : 1;    // 128-key halves per ring chunk (verify: 256 keys)
+  constexpr int NS = MODE == MODE_VERIFY ? NH + 1 : NH;  // steps: the halves (verify: then the proposals)
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr bool KPAIR = FP8 && NCH % 2 == 0;        // 16-byte fp8 K loads (two k chunks)
   constexpr bool VPAIR = FP8 && NDT % 2 == 0;        // 16-byte fp8 V loads (two adjacent dims)
@@ -192,10 +195,14 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int Hkv = p.Hkv, G = p.G, S = p.S;
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
-  const bool prop = MODE == MODE_VERIFY && chunk == 0;           // the proposals' chunk
-  const int k0 = (MODE == MODE_VERIFY ? chunk - 1 : chunk) * CK * NH;  // region slot of key 0
-  const int64_t k_off = p.k_off[b], v_off = p.v_off[b];
-  const int cap_r = region_slots(p, b);
+  // verify: ring chunk 0 of each (request, KV head) also takes the S
+  // proposals, as one more step after its ring halves
+  const bool with_prop = MODE == MODE_VERIFY && chunk == 0;
+  const int k0 = chunk * CK * NH;  // region slot of key 0
+  // one request per workgroup: its region offsets and slot count are
+  // workgroup-uniform
+  const int64_t k_off = wave_uniform(p.k_off[b]), v_off = wave_uniform(p.v_off[b]);
+  const int cap_r = wave_uniform(region_slots(p, b));
   const int S_r = stored_slots(cap_r);  // slots stored per KV head (region layout: swr_device.h)
   const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(Hkv * D * ESZ);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + k_off, region_bytes);
@@ -219,8 +226,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // where the bf16 operands let all of them fly at once.
   const int kq = wave % KQ, dh = wave / KQ;
   // Operands of half h (keys k0 + 128h ..) of the chunk.
-  bf16x8 kop[NH][NCH];
-  bf16x8 vop[NH][KS][NDT];
+  bf16x8 kop[NS][NCH];
+  bf16x8 vop[NS][KS][NDT];
   u32x4 kraw[NH][FP8 ? NCH : 1];  // paired: entries 0 .. NCH/2-1; else the low halves
   u32x4 vraw[NH][KS][FP8 ? NDT : 1];
   auto load_v = [&](int h) {
@@ -291,6 +298,9 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // the regions receive them from the merge pass, after every chunk has read.
   // Over an fp8 region the staged values are those of the codes the merge
   // will store, exactly as a later call reads them.
+  // Verify: the proposal-carrying chunk stages the S proposals' K and V the
+  // same way (bf16, as they arrive, also over an fp8 ring), and its
+  // proposal step takes its operands from there.
   constexpr bool SUBP = stages_tokens<MODE>();
   __bf16* const tok_k = chunk_tokens;
   __bf16* const tok_v = chunk_tokens + S * D;
@@ -315,7 +325,45 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
     }
   }
-  if (!prop) {
+  if constexpr (MODE == MODE_VERIFY) {
+    tok_piece = with_prop && (int)threadIdx.x < S * (D / 8);
+    if (tok_piece) {
+      const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
+      const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
+      tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
+      tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+    }
+  }
+  // Q of the group's rows, once per workgroup, into LDS (rows past p.rows
+  // load row 0 and store zeros).  Verify loads it ahead of K, so that the
+  // scores of the first half wait for that half's keys alone (loads return
+  // in issue order); the global chunk, whose one half needs every K load
+  // anyway, loads it after.
+  constexpr int QPIECES = ROWS * D / 8;
+  constexpr int QPT = (QPIECES + 64 * NW - 1) / (64 * NW);  // Q pieces per thread
+  bf16x8 qv[QPT];
+  auto load_q = [&] {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = threadIdx.x + k * 64 * NW;
+      const int row = min(idx, QPIECES - 1) / (D / 8), d8 = (min(idx, QPIECES - 1) - row * (D / 8)) * 8;
+      const int rr = row < p.rows ? row : 0;
+      const int i = rr / G, hq = rr - (rr / G) * G;
+      qv[k] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)(b * S + i) * p.Hq + g * G + hq) * D + d8);
+    }
+  };
+  auto store_q = [&] {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = threadIdx.x + k * 64 * NW;
+      if (idx < QPIECES) {
+        const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = row < p.rows ? qv[k] : bf16x8{};
+      }
+    }
+  };
+  if (MODE == MODE_VERIFY) load_q();
+  {  // K of every half
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       // row lr of half kq%2 of tile kq/2; granule (dh*DH + kdim(c)) / R of it
@@ -339,52 +387,9 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         }
       }
     }
-  } else {
-    // proposals j = 0..S-1 are keys 0..S-1 of the chunk: row r of the
-    // wave's subtile is key 32*(kq/2) + 8*(r/4) + 4*(kq%2) + r%4 (so j < 8
-    // lands in subtiles 0 and 1), and value k step 0, lane group 0; every
-    // other operand element is zero
-    const int pj = 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kop[0][c] = bf16x8{};
-    if (pj < S) {
-      const uint16_t* src = p.k_prop + ((size_t)(b * S + pj) * Hkv + g) * D + dh * DH;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) kop[0][c] = *reinterpret_cast<const bf16x8*>(src + kdim(c));
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vop[0][ks][dt] = bf16x8{};
-    if (wave < PVW && lq == 0) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bf16x8 v;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          uint16_t bits = 0;
-          if (j < S) bits = p.v_prop[((size_t)(b * S + j) * Hkv + g) * D + vdim(dt)];
-          v[j] = __builtin_bit_cast(__bf16, bits);
-        }
-        vop[0][0][dt] = v;
-      }
-    }
   }
-  // Q of the group's rows, once per workgroup, into LDS (rows past p.rows
-  // load row 0 and store zeros)
-  constexpr int QPIECES = ROWS * D / 8;
-#pragma unroll
-  for (int k = 0; k < (QPIECES + 64 * NW - 1) / (64 * NW); ++k) {
-    const int idx = threadIdx.x + k * 64 * NW;
-    if (idx < QPIECES) {
-      const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
-      const bool ok = row < p.rows;
-      const int rr = ok ? row : 0;
-      const int i = rr / G, h = rr - (rr / G) * G;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d8);
-      *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = ok ? v : bf16x8{};
-    }
-  }
+  if (MODE != MODE_VERIFY) load_q();
+  store_q();
   if constexpr (SUBP) {
     if (FP8) {
       // piece t: values 4t .. 4t+3 of K's S*D then V's (token j = 4t/D of
@@ -393,6 +398,12 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       for (int t = threadIdx.x + 64 * NW; tok_chunk && t < 2 * S * (D / 4); t += 64 * NW)
         stage_token_piece4(p, chunk_tokens, S, D, t, load_token_piece4(p, b, g, D, t));
     } else if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
+      *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
+      *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
+    }
+  }
+  if constexpr (MODE == MODE_VERIFY) {
+    if (tok_piece) {  // proposal j, head dims 8*d8 .. +7
       *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
       *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
     }
@@ -406,20 +417,19 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int qp = MODE == MODE_GLOBAL ? qpos_of(p, b, si) : 0;
 
   const int n_keys = region_keys<MODE>(p, b);
-  if (!prop && k0 >= n_keys) return;  // past this request's keys (uniform over the workgroup)
+  if (!with_prop && k0 >= n_keys) return;  // past this request's keys (uniform over the workgroup)
 
   // ---------------------------------------------------------- scores
-  __syncthreads();  // Q in LDS
+  __syncthreads();  // Q (and the staged proposals) in LDS
   const size_t slot = ((size_t)unit * p.nchunk + chunk) * p.rows;
-  const bool bf16_prop = FP8 && prop;  // proposals as bf16 values, not codes
-  const float qs = bf16_prop ? p.qk_scale_prop : p.qk_scale;
   // verify: slot age of the newest committed position, and the oldest age
   // row i still sees
   const int ring_head = (MODE == MODE_VERIFY && p.pos[b] > 0) ? (p.pos[b] - 1) % p.cap : 0;
   const int age_lim = p.cap - 2 - si;
-  // halves this chunk computes: a second half wholly past the key count
-  // adds nothing (uniform over the workgroup)
-  const int nh = (prop || k0 + CK >= n_keys) ? 1 : NH;
+  // halves this chunk computes: a half wholly past the key count adds
+  // nothing (uniform over the workgroup; verify's proposal-carrying chunk
+  // can have none)
+  const int nh = k0 >= n_keys ? 0 : (k0 + CK >= n_keys ? 1 : NH);
   float m_run = -INFINITY, l_run = 0.f;  // softmax lanes: the row's running (max, sum)
   f32x4 o[NCT][NDT];                     // value lanes: rows ct*16 + lr, unnormalised
 #pragma unroll
@@ -428,10 +438,25 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    if (h >= nh) break;
+  for (int h = 0; h < NS; ++h) {
+    // step NH (verify): the proposals, keys 0 .. S-1 of the step, bf16
+    // values over any ring (over an fp8 ring their scores take scale *
+    // log2(e) without k_scale, and their P is divided by v_scale before
+    // it is rounded to bf16, since the merge multiplies by v_scale)
+    const bool ph = MODE == MODE_VERIFY && h == NH;
+    if (ph ? !with_prop : h >= nh) continue;
     const int kh = k0 + CK * h;  // region slot of the half's key 0
-    if (!prop) cvt_k(h);
+    const float qs = (FP8 && ph) ? p.qk_scale_prop : p.qk_scale;
+    if (ph) {
+      // row lr of subtile kq is key 32*(kq/2) + 8*(lr/4) + 4*(kq%2) + lr%4
+      // (so proposals j < 8 land in subtiles 0 and 1); rows past S are zero
+      const int pj = 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        kop[h][c] = pj < S ? *reinterpret_cast<const bf16x8*>(&tok_k[pj * D + dh * DH + kdim(c)]) : bf16x8{};
+    } else {
+      cvt_k(h);
+    }
     if constexpr (SUBP) {
       if (tok_chunk) {  // this lane's K row is token j of the call
         const int j = kh + 32 * (kq >> 1) + 8 * (lr >> 2) + 4 * (kq & 1) + (lr & 3) - pos0;
@@ -455,7 +480,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     // computed rather than on entry: a smaller first burst of requests
     // across all workgroups streams faster, and the value loads still
     // overlap the softmax.
-    if (h == 0 && !prop) {
+    if (h == 0) {
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
         if (hh < nh) load_v(hh);
@@ -477,7 +502,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           bool vis;
           if (MODE == MODE_GLOBAL) {
             vis = kh + j < n_keys && kh + j <= qp;
-          } else if (prop) {
+          } else if (ph) {
             vis = j < S && j <= si;
           } else {
             int age = ring_head - (kh + j);
@@ -498,8 +523,14 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         bf16x4 pb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[e] = (__bf16)fast_exp2(sv[e4 + e] - m_use);
-          ps += (float)pb[e];
+          const float pe = fast_exp2(sv[e4 + e] - m_use);
+          if (FP8 && ph) {
+            pb[e] = (__bf16)(pe * p.inv_v_scale);
+            ps += (float)(__bf16)pe;
+          } else {
+            pb[e] = (__bf16)pe;
+            ps += (float)pb[e];
+          }
         }
         *reinterpret_cast<bf16x4*>(&pbuf[srow][kk + e4]) = pb;
       }
@@ -511,7 +542,24 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
     // --------------------------------------------------------- values
     if (wave < PVW) {
-      if (!prop) cvt_v(h);
+      if (ph) {
+        // k step 0, lane group 0 holds keys 0..7: proposal j at element j
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vop[h][ks][dt] = bf16x8{};
+        if (lq == 0) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            bf16x8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = j < S ? tok_v[j * D + vdim(dt)] : (__bf16)0.f;
+            vop[h][0][dt] = v;
+          }
+        }
+      } else {
+        cvt_v(h);
+      }
       if constexpr (SUBP) {
         if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
 #pragma unroll
@@ -531,7 +579,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
             }
         }
       }
-      if (!prop && kh + CK > n_keys) {  // last half: zero values of keys past the count
+      if (!ph && kh + CK > n_keys) {  // last half: zero values of keys past the count
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           u32x4 keep;
@@ -569,9 +617,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   }
   if (wave >= PVW) return;
   // Lane (lr, lq) holds rows ct*16 + lr; group q of four consecutive dims
-  // starts at qdim(q).  Proposal values are bf16, not codes: divided by
-  // v_scale here so that the merge's v_scale restores them.
-  const float vs = bf16_prop ? p.inv_v_scale : 1.f;
+  // starts at qdim(q).
   auto qdim = [&](int q) { return vw * DPW + (VPAIR ? 32 * (q >> 1) + 8 * lq + 4 * (q & 1) : 16 * q + 4 * lq); };
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -587,16 +633,15 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       } else {
         v = o[ct][q];
       }
-      __builtin_nontemporal_store(v * vs, reinterpret_cast<f32x4*>(dst + qdim(q)));
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + qdim(q)));
     }
   }
 }
 
 // Global: workgroup j takes chunk j % nchunk of unit j / nchunk.  Verify:
-// the ring chunks of every unit come first and the small proposal chunks
-// last.  When the units are a multiple of the 8 XCDs (workgroup j runs on
-// XCD j % 8), all ring chunks of a unit go to one XCD, whose L2 then serves
-// the unit's Q to all of them after one read.
+// when the units are a multiple of the 8 XCDs (workgroup j runs on XCD
+// j % 8), all ring chunks of a unit go to one XCD, whose L2 then serves the
+// unit's Q to all of them after one read.
 // Up to 256 head dims two global workgroups stay resident per CU (eight
 // waves per SIMD, 64 registers a lane); 512 dims, and verify with its two
 // halves' operands, need more registers and keep one.
@@ -605,22 +650,17 @@ __global__ void __launch_bounds__(64 * kChunkWaves)
 __attribute__((amdgpu_waves_per_eu(D <= 256 && MODE != MODE_VERIFY ? 8 : 4))) chunk_kernel(const AttnParams p) {
   __shared__ ChunkSmem<D, NCT> sm;
   if (MODE == MODE_VERIFY) {
-    const int nring = p.nchunk - 1;
-    const int ring_wgs = p.B * p.Hkv * nring;
-    if ((int)blockIdx.x < ring_wgs) {
-      int unit, rc;
-      if ((p.B * p.Hkv) % 8 == 0) {
-        const int x = blockIdx.x & 7, sl = blockIdx.x >> 3;
-        unit = x + 8 * (sl / nring);
-        rc = sl - (sl / nring) * nring;
-      } else {
-        unit = blockIdx.x / nring;
-        rc = blockIdx.x - unit * nring;
-      }
-      chunk_item<D, NCT, FP8, MODE>(p, sm, unit, 1 + rc);
+    const int nring = p.nchunk;
+    int unit, rc;
+    if ((p.B * p.Hkv) % 8 == 0) {
+      const int x = blockIdx.x & 7, sl = blockIdx.x >> 3;
+      unit = x + 8 * (sl / nring);
+      rc = sl - (sl / nring) * nring;
     } else {
-      chunk_item<D, NCT, FP8, MODE>(p, sm, blockIdx.x - ring_wgs, 0);
+      unit = blockIdx.x / nring;
+      rc = blockIdx.x - unit * nring;
     }
+    chunk_item<D, NCT, FP8, MODE>(p, sm, unit, rc);
   } else {
     const int unit = blockIdx.x / p.nchunk;
     chunk_item<D, NCT, FP8, MODE>(p, sm, unit, blockIdx.x - unit * p.nchunk);
@@ -660,14 +700,36 @@ __device__ __forceinline__ CallToken load_call_token(const AttnParams& p, int D,
   return t;
 }
 
+// Region of request b for a token store.  UNIFORM: b is the same in every
+// lane of the wave (merge_grouped: one request per workgroup), so the
+// resource goes to scalar registers; merge_flat's waves can span two
+// requests and keep the compiler's per-resource loop.
+template <bool UNIFORM>
+struct TokenRegion {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int cap_r, S_r;
+  __device__ __forceinline__ TokenRegion(const AttnParams& p, int D, int b, int esize) {
+    int64_t ko = p.k_off[b], vo = p.v_off[b];
+    cap_r = region_slots(p, b);
+    if (UNIFORM) {
+      ko = wave_uniform(ko);
+      vo = wave_uniform(vo);
+      cap_r = wave_uniform(cap_r);
+    }
+    S_r = stored_slots(cap_r);
+    const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * esize);
+    rk = make_rsrc(p.k_base + ko, region_bytes);
+    rv = make_rsrc(p.v_base + vo, region_bytes);
+  }
+};
+
+template <bool UNIFORM>
 __device__ __forceinline__ void store_call_token(const AttnParams& p, int D, int b, int g, const CallToken& t) {
-  const int cap_r = region_slots(p, b);
+  const TokenRegion<UNIFORM> r(p, D, b, 2);
   const int slot = p.pos[b] + t.j;
-  if (t.j < 0 || slot < 0 || slot >= cap_r) return;
-  const int S_r = stored_slots(cap_r);
-  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+  if (t.j < 0 || slot < 0 || slot >= r.cap_r) return;
+  const int S_r = r.S_r;
+  const __amdgpu_buffer_rsrc_t rk = r.rk, rv = r.rv;
   store_token_piece<false>(rk, rv, slot, g, S_r, D, t.d8, t.k, t.v, p.k_scale_store, p.v_scale_store);
 }
 
@@ -694,14 +756,13 @@ __device__ __forceinline__ CallTokenCode load_call_token_code(const AttnParams& 
   return t;
 }
 
+template <bool UNIFORM>
 __device__ __forceinline__ void store_call_token_code(const AttnParams& p, int D, int b, int g, const CallTokenCode& t) {
-  const int cap_r = region_slots(p, b);
+  const TokenRegion<UNIFORM> r(p, D, b, 1);
   const int slot = p.pos[b] + t.j;
-  if (t.j < 0 || slot < 0 || slot >= cap_r) return;
-  const int S_r = stored_slots(cap_r);
-  const uint32_t region_bytes = (uint32_t)S_r * (uint32_t)(p.Hkv * D);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_base + p.k_off[b], region_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_base + p.v_off[b], region_bytes);
+  if (t.j < 0 || slot < 0 || slot >= r.cap_r) return;
+  const int S_r = r.S_r;
+  const __amdgpu_buffer_rsrc_t rk = r.rk, rv = r.rv;
   const uint8_t code = e4m3_encode(__builtin_bit_cast(float, (uint32_t)t.bits << 16),
                                    t.is_v ? p.v_scale_store : p.k_scale_store);
   store_token_code(rk, rv, slot, g, S_r, D, t.d, t.is_v, code);
@@ -801,9 +862,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   auto store_tokens = [&] {
     if (MODE == MODE_GLOBAL && p.append && !tokens_stored) {
       if constexpr (FP8)
-        store_call_token_code(p, D, b, g, tcode);
+        store_call_token_code<true>(p, D, b, g, tcode);
       else
-        store_call_token(p, D, b, g, tok);
+        store_call_token<true>(p, D, b, g, tok);
     }
     tokens_stored = true;
   };
@@ -818,7 +879,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
     if (MODE == MODE_GLOBAL && p.append)
       for (int k = tid + kMergeThreads; k < per; k += kMergeThreads)
         if (row * per + k < tok_values)
-          store_call_token_code(p, D, b, g, load_call_token_code(p, D, PART, quarter, b, g, row * per + k));
+          store_call_token_code<true>(p, D, b, g, load_call_token_code(p, D, PART, quarter, b, g, row * per + k));
   }
   if (tid - grp * TPG == 0) {
     gml[grp][0] = r.M;
@@ -868,9 +929,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   if (MODE == MODE_GLOBAL && p.append) {
     if constexpr (FP8) {
       for (int v = rem; v < 2 * p.S * D; v += per_unit)
-        store_call_token_code(p, D, b, g, load_call_token_code(p, D, D, 0, b, g, v));
+        store_call_token_code<false>(p, D, b, g, load_call_token_code(p, D, D, 0, b, g, v));
     } else if (row == 0 && d % 8 == 0) {
-      for (int j = 0; j < p.S; ++j) store_call_token(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
+      for (int j = 0; j < p.S; ++j) store_call_token<false>(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
     }
   }
   store_row4(p, D, b, g, row, d, r.L, r.O);
@@ -886,7 +947,8 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 template <int D, int NCT, int MODE>
 hipError_t launch_chunks(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   const dim3 grid(pl.units * pl.nchunk), block(64 * kChunkWaves);
-  const size_t tok_bytes = (MODE == MODE_GLOBAL && p.append) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
+  const size_t tok_bytes =
+      (MODE == MODE_VERIFY || (MODE == MODE_GLOBAL && p.append)) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
   if (pl.fp8)
     hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, tok_bytes, s, p);
   else
@@ -945,7 +1007,7 @@ bool plan_chunked(int mode, int B, int S, int Hq, int Hkv, int D, int keys, Attn
   if (D != 64 && D != 128 && D != 256 && D != 512) return false;
   const int rows = (Hq / Hkv) * S;
   if (rows > 32) return false;
-  const int nchunk = mode == MODE_VERIFY ? cdiv(keys, kVerifyChunkKeys) + 1 : cdiv(keys, kChunkKeys);
+  const int nchunk = mode == MODE_VERIFY ? cdiv(keys, kVerifyChunkKeys) : cdiv(keys, kChunkKeys);
   if (nchunk > kMaxChunks) return false;
   pl->mode = mode;
   pl->chunked = 1;

@@ -27,6 +27,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
+// A value the caller knows is the same in every lane of the wave (a load
+// whose address depends only on the workgroup), moved to scalar registers.
+// Without it a buffer resource built from a vector load's result lives in
+// vector registers, and the compiler wraps each buffer access in a loop over
+// the distinct resources of the wave -- one pass, but a dozen extra
+// instructions per access.  Wrong if the lanes differ: only for values
+// uniform by construction.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t wave_uniform(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Streaming read: the non-temporal cache policy (bit 1 of the aux operand on
 // gfx94x/gfx950) marks lines read once, so K/V streams do not evict reused data.
 __device__ __forceinline__ u32x4 load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {

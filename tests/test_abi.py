@@ -221,9 +221,10 @@ def test_zero_batch_attention_is_a_no_op():
 
 
 def test_verify_workspace_is_one_partial_per_256_ring_keys():
-    # B=8 x 8 KV heads, W=1024: 4 ring chunks of 256 keys + 1 proposal chunk
-    # per unit, 32 rows of 256 fp32 dims each, plus a (max, sum) per row
-    units, chunks, rows, d = 8 * 8, 1024 // 256 + 1, 8 * 4, 256
+    # B=8 x 8 KV heads, W=1024: 4 ring chunks of 256 keys per unit (the
+    # first also takes the proposals), 32 rows of 256 fp32 dims each, plus a
+    # (max, sum) per row
+    units, chunks, rows, d = 8 * 8, 1024 // 256, 8 * 4, 256
     want = units * chunks * rows * d * 4 + units * chunks * rows * 2 * 4
     assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 4, 64, 8, 256, 1024) == want
 
