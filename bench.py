@@ -366,10 +366,24 @@ def read_ceiling(swr, torch):
             best = max(best, (gbs, grid, pattern))
     del bufs
     torch.cuda.empty_cache()
+    # One-shot reads of the sizes of the chunked calls' K/V: what the chip
+    # gives a job that is one burst, not a stream.  12 rotating buffers
+    # (more than the last-level cache), launches back to back.
+    one_shot = {}
+    for label, nbytes, grids in (("sliding_verify_b8_kv_64MiB", 64 << 20, (256, 512)),
+                                 ("global_verify_6005_kv_24.6MB", KC * GHKV * GD * 2 * 2, (94, 188, 256))):
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(12)]
+        for grid in grids:
+            for pattern in (0, 1):
+                us = _timed(torch, lambda i: swr.read_ceiling(bufs[i], sink, grid, pattern), 48, len(bufs))
+                one_shot[f"{label}_{('sweep', 'span')[pattern]}_{grid}"] = {
+                    "us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del bufs
+        torch.cuda.empty_cache()
     return {"GB/s": round(best[0], 1), "bytes_per_launch": nb, "grid": best[1],
             "pattern": ("grid-wide sweep", "contiguous span per workgroup")[best[2]],
             "kernel": "read_ceiling_kernel (swr_read_ceiling), 256 threads, 16-byte non-temporal loads",
-            "GB/s_by_pattern_and_grid": sweep}
+            "GB/s_by_pattern_and_grid": sweep, "one_shot_reads": one_shot}
 
 
 def decode_stack(swr, torch, randn, dev):

@@ -55,6 +55,32 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+_SAN_LIB = os.path.join(_HERE, "_build_san", "liboracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(force: bool = False) -> str:
+    """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc), for the sanitized run of the pins (tests/test_sanitizers.py);
+    loading it needs gcc's libasan preloaded (sanitizer_runtime())."""
+    srcs = [os.path.join(_HERE, f) for f in SOURCES]
+    if force or not os.path.exists(_SAN_LIB) or os.path.getmtime(_SAN_LIB) < max(map(os.path.getmtime, srcs)):
+        os.makedirs(os.path.dirname(_SAN_LIB), exist_ok=True)
+        tmp = _SAN_LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, *_SAN_FLAGS, *srcs, "-o", tmp, "-lm"])
+        os.replace(tmp, _SAN_LIB)
+    return _SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """gcc's ASan runtime, for LD_PRELOAD into an uninstrumented Python."""
+    out = subprocess.run(["gcc", "-print-file-name=libasan.so"], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise FileNotFoundError("gcc's libasan not found")
+    return out
+
+
 _lib = None
 
 
