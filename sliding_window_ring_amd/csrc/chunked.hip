@@ -334,11 +334,14 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
     }
   }
-  // Q of the group's rows, once per workgroup, into LDS (rows past p.rows
-  // load row 0 and store zeros).  Verify loads it ahead of K, so that the
-  // scores of the first half wait for that half's keys alone (loads return
-  // in issue order); the global chunk, whose one half needs every K load
-  // anyway, loads it after.
+  // Q of the group's rows, once per workgroup, into LDS.  Rows past p.rows
+  // take row 0's values: their scores are masked and their outputs never
+  // stored, so any finite values do, and no select on the loaded data
+  // (which the compiler places right after the load, holding every later
+  // load of the wave behind a full round trip) is needed.  Verify loads it
+  // ahead of K, so that the scores of the first half wait for that half's
+  // keys alone (loads return in issue order); the global chunk, whose one
+  // half needs every K load anyway, loads it after.
   constexpr int QPIECES = ROWS * D / 8;
   constexpr int QPT = (QPIECES + 64 * NW - 1) / (64 * NW);  // Q pieces per thread
   bf16x8 qv[QPT];
@@ -358,7 +361,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       const int idx = threadIdx.x + k * 64 * NW;
       if (idx < QPIECES) {
         const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = row < p.rows ? qv[k] : bf16x8{};
+        *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = qv[k];
       }
     }
   };
