@@ -26,9 +26,10 @@
 //     over the chunk, and P x V (bf16 MFMA, fp32) -- with Q, the scores and
 //     P kept in LDS, and writes the chunk's unnormalised rows with their
 //     (max, sum).  In a verify call ring chunk 0 of each (request, KV head)
-//     also takes the S proposals (read from their own buffers) as one more
-//     step: a separate proposal workgroup would start only when a ring
-//     chunk leaves its CU, a second round at the end of the pass.
+//     also takes the S proposals (read from their own buffers) as a step
+//     of their own, run while its ring loads are in flight: a separate
+//     proposal workgroup would start only when a ring chunk leaves its CU,
+//     a second round at the end of the pass.
 //   pass 2: merges the chunk partials, weights 2^(m_c - M), sums in a fixed
 //     order, division by the weighted row sum.  With many chunks per row
 //     (global) one workgroup per (request, KV head, row, quarter of the
@@ -196,7 +197,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
   // verify: ring chunk 0 of each (request, KV head) also takes the S
-  // proposals, as one more step after its ring halves
+  // proposals, as a step of their own before its ring halves
   const bool with_prop = MODE == MODE_VERIFY && chunk == 0;
   const int k0 = chunk * CK * NH;  // region slot of key 0
   // one request per workgroup: its region offsets and slot count are
@@ -440,12 +441,18 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Verify: the proposals' step (h = NH), keys 0 .. S-1 of the step, bf16
+  // values over any ring (over an fp8 ring their scores take scale *
+  // log2(e) without k_scale, and their P is divided by v_scale before it is
+  // rounded to bf16, since the merge multiplies by v_scale).  Up to 256
+  // head dims it comes first: its operands are in LDS already, so it needs
+  // no K of the ring's and runs while the last waves' K loads are still in
+  // flight.  At 512 dims the ring's K registers in flight leave it no room,
+  // and it comes after the ring halves.
+  constexpr bool PROP_FIRST = MODE == MODE_VERIFY && D <= 256;
 #pragma unroll
-  for (int h = 0; h < NS; ++h) {
-    // step NH (verify): the proposals, keys 0 .. S-1 of the step, bf16
-    // values over any ring (over an fp8 ring their scores take scale *
-    // log2(e) without k_scale, and their P is divided by v_scale before
-    // it is rounded to bf16, since the merge multiplies by v_scale)
+  for (int step = 0; step < NS; ++step) {
+    const int h = PROP_FIRST ? (step == 0 ? NH : step - 1) : step;
     const bool ph = MODE == MODE_VERIFY && h == NH;
     if (ph ? !with_prop : h >= nh) continue;
     const int kh = k0 + CK * h;  // region slot of the half's key 0
@@ -472,6 +479,10 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
+      // the proposals (S <= 8) are keys of subtiles 0 and 1 only: the other
+      // waves' scores would be masked, and their part of sbuf is not read
+      // unmasked, so they skip the product
+      if (ph && kq >= 2) continue;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
@@ -539,7 +550,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
       l_run = l_run * alpha + sum16lanes(ps);
       m_run = m_new;
-      if (NH > 1 && lr == 0) sm.alpha[srow] = alpha;
+      if (NS > 1 && lr == 0) sm.alpha[srow] = alpha;
     }
     __syncthreads();
 
@@ -598,13 +609,14 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        if (NH > 1 && h > 0) {  // rescale to the running maximum of the row
+        if (NS > 1 && step > 0) {  // rescale to the running maximum of the row
           const float a = sm.alpha[ct * 16 + lr];
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[ct][dt] *= a;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+          if (ph && ks > 0) continue;  // the proposals' P is zero past key 31
           const bf16x8 pt = *reinterpret_cast<const bf16x8*>(&pbuf[ct * 16 + lr][32 * ks + 8 * lq]);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = mfma16x16x32(vop[h][ks][dt], pt, o[ct][dt]);
