@@ -285,18 +285,24 @@ attn_kernel(const AttnParams p) {
 
   // Fused append (decode): the new token, position pos in slot pos % W, is
   // written by the waves that read its tile, each its own head-dim slice; no
-  // other workgroup reads the tile.  The split walks its tiles in rotated
-  // order, starting after the token's tile, so that this tile comes last
-  // (the writes then fall at the end of the read stream).
+  // other workgroup reads the tile.
   //  bf16: the wave loads the tile as it is (the slot still holds the token
   //   it evicts), puts the new token into its operand registers, and stores
-  //   back every cache line of the tile that holds a byte of the slot, whole:
-  //   a line left partly written costs its next reader a merge with memory,
-  //   which over a batch's 64 lines per (request, KV head) measured about as
-  //   much as a separate append launch.
+  //   back every cache line of the tile that holds a byte of the slot, whole
+  //   (a line left partly written costs its next reader a merge with memory,
+  //   which over a batch measured about as much as a separate append launch).
+  //   The stores go out after the tile's score product: ahead of it they
+  //   would sit in front of the loads that the product waits for, and that
+  //   wait (the load counter counts stores as well) would hold the wave until
+  //   they were acknowledged.  The tiles are walked in storage order, as the
+  //   decode walks them: rotating each split to end on the token's tile
+  //   measured 1-3 us slower at B=56 over rings carved from one pool (74.2 -
+  //   74.5 us against 75.3 - 77.6 us for three sets of positions).
   //  fp8 (the registers hold decoded values, not the stored codes): the
   //   stores go out with the first loads and the wave waits for them once,
-  //   before the tile's loads.
+  //   before the token tile's loads; the split walks its tiles in rotated
+  //   order, starting after the token's tile, so that the wait falls at the
+  //   end of the wave's read stream.
   constexpr bool SUBST = APP && !FP8;
   constexpr bool FIRST = APP && FP8;
   const int nt = t_end - t_begin;
@@ -307,9 +313,13 @@ attn_kernel(const AttnParams p) {
     slot_new = p.pos[b] % p.cap;
     t_new = slot_new >> 5;
     if (t_new >= t_begin && t_new < t_end) {
-      rot = t_new - t_begin + 1;
-      if (rot == nt) rot = 0;
-      writer = kw == (nt - 1) % KW;
+      if (FIRST) {
+        rot = t_new - t_begin + 1;
+        if (rot == nt) rot = 0;
+        writer = kw == (nt - 1) % KW;
+      } else {
+        writer = kw == (t_new - t_begin) % KW;  // the wave whose tile it is
+      }
     }
   }
   auto tile_at = [&](int lam) {
@@ -383,24 +393,17 @@ attn_kernel(const AttnParams p) {
     };
 
     if (subst) {
-      // K: row r_new of half h_new is the new token; the lanes of the two
-      // rows sharing its lines store their granules back (one whole 128-byte
-      // line per chunk)
-      const uint32_t hb = k_half_base(g, S_r, kb, h_new, D, ESZ);
+      // K: row r_new of half h_new is the new token
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (sub != h_new) continue;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
+        for (int c = 0; c < NCH; ++c)
           if (lr == r_new) kop[sub][c] = *reinterpret_cast<const bf16x8*>(&stage_k[d_base + kdim(c)]);
-          if ((lr >> 1) == (r_new >> 1))
-            store16(rk, hb + k_granule_offset((d_base + kdim(c)) / 8, lr), __builtin_bit_cast(u32x4, kop[sub][c]));
-        }
       }
       // V: lane group k32/8 holds the slot's 8-key blocks; element k32%8 of
-      // each is the new token; the 16 lanes of the group store 256 bytes
+      // each is the new token
       if (lq == (k32_new >> 3)) {
-        const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + (kb >> 3) + lq) * D;
         const int e = k32_new & 7;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -411,7 +414,6 @@ attn_kernel(const AttnParams p) {
             if (j == (e >> 1)) w[j] = (e & 1) ? ((w[j] & 0x0000FFFFu) | (nv << 16)) : ((w[j] & 0xFFFF0000u) | nv);
           }
           vop[dt] = __builtin_bit_cast(bf16x8, w);
-          store16(rv, (vblock + (uint32_t)vdim(dt)) * 16, w);
         }
       }
     }
@@ -435,6 +437,28 @@ attn_kernel(const AttnParams p) {
         for (int c = 0; c < NCH; ++c) acc = mfma16x16x32(kop[sub][c], qop[ct][c], acc);
         sc[sub][ct] = acc;
       }
+    if (subst) {
+      // the slot's lines, whole, now that the score product has read the
+      // operands: K, the lanes of the two rows sharing the token row's lines
+      // (one 128-byte line per chunk); V, the 16 lanes of the token's lane
+      // group (256 bytes per tile of 16 dims), before the value product's
+      // mask of keys past the count touches the registers
+      const uint32_t hb = k_half_base(g, S_r, kb, h_new, D, ESZ);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (sub != h_new) continue;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          if ((lr >> 1) == (r_new >> 1))
+            store16(rk, hb + k_granule_offset((d_base + kdim(c)) / 8, lr), __builtin_bit_cast(u32x4, kop[sub][c]));
+      }
+      if (lq == (k32_new >> 3)) {
+        const uint32_t vblock = (uint32_t)(g * (S_r >> 3) + (kb >> 3) + lq) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          store16(rv, (vblock + (uint32_t)vdim(dt)) * 16, __builtin_bit_cast(u32x4, vop[dt]));
+      }
+    }
     if (!RAW && has_next) next_k();
 
     if (DSPLIT > 1) {  // add the head-dim slices of the scores, in slice order
