@@ -136,10 +136,16 @@ struct ChunkSmem {
 };
 
 // The call's own tokens, staged by the global chunk that holds their slots
-// when a global call appends them itself: dynamic LDS of [2][S][D] bf16 (K,
-// then V; over an fp8 region the values its stored codes decode to, in units
-// of the scale), sized at launch -- none for the other calls.
+// when a global call appends them itself (over an fp8 region the values its
+// stored codes decode to, in units of the scale): dynamic LDS of [S][D] bf16
+// for K, then V in the region's 8-slot block form, [2][D][8] bf16 -- the
+// block holding key pos0 and the next, a token at slot (pos0 + j) % 8 of
+// block (pos0 + j) / 8 - pos0 / 8 (S <= 8 tokens span at most two), so that
+// a lane takes a key group's tokens with one 16-byte read per value tile.  A
+// verify call stages its proposals as [2][S][D] bf16 (K, then V).  Sized at
+// launch; none for the other calls.
 extern __shared__ __attribute__((aligned(16))) __bf16 chunk_tokens[];
+constexpr int kTokenBlocks = 2;  // 8-slot V blocks a global call's S <= 8 tokens span
 
 // Piece t of a global call's tokens over an fp8 region: values 4t .. 4t+3
 // of K's S*D values then V's ((token j, head dim d) at j*D + d), as bf16
@@ -154,19 +160,29 @@ __device__ __forceinline__ u32x4 load_token_piece4(const AttnParams& p, int b, i
 }
 
 // Writes piece t's values, as the region will hold them, to the staged
-// tokens (K's S*D values, then V's).
-__device__ __forceinline__ void stage_token_piece4(const AttnParams& p, __bf16* tok, int S, int D, int t, u32x4 bits) {
+// tokens: K's token-major, V's into the 8-slot blocks.
+__device__ __forceinline__ void stage_token_piece4(const AttnParams& p, __bf16* tok, int S, int D, int pos0, int t,
+                                                   u32x4 bits) {
   const bool is_v = 4 * t >= S * D;
-  *reinterpret_cast<u32x2*>(&tok[4 * t]) =
-      fp8_stored_values4(u32x2{bits[0], bits[1]}, is_v ? p.v_scale_store : p.k_scale_store);
+  const u32x2 vals = fp8_stored_values4(u32x2{bits[0], bits[1]}, is_v ? p.v_scale_store : p.k_scale_store);
+  if (!is_v) {
+    *reinterpret_cast<u32x2*>(&tok[4 * t]) = vals;
+    return;
+  }
+  const int r = 4 * t - S * D, j = r / D, d = r - j * D;
+  const int key = pos0 + j, bi = (key >> 3) - (pos0 >> 3), slot = key & 7;
+  uint16_t* vb = reinterpret_cast<uint16_t*>(tok + S * D);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vb[(bi * D + d + i) * 8 + slot] = (uint16_t)(vals[i >> 1] >> (16 * (i & 1)));
 }
-template <int MODE>
-constexpr bool stages_tokens() { return MODE == MODE_GLOBAL; }
-
 // One chunk of one (request, KV head); every wave of the workgroup calls it
 // with the same arguments.  Returns early (all waves alike) for a chunk past
 // the request's keys; waves without value work return after the softmax.
-template <int D, int NCT, bool FP8, int MODE>
+// TOK (global calls that append their own tokens): the chunk holding the
+// tokens' slots stages them; a kernel of its own, since the staging code,
+// present but switched off, measured about 0.5 us slower on the calls that
+// append nothing.
+template <int D, int NCT, bool FP8, int MODE, bool TOK>
 __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT>& sm, int unit, int chunk) {
   constexpr int CK = kChunkKeys;
   constexpr int NW = kChunkWaves;
@@ -295,14 +311,19 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   // ahead of the region's loads and written to LDS after the Q loads have
   // gone out (the load counter drains in order: the staging then waits for
   // the tokens alone, and an LDS write placed before the Q loads would hold
-  // them back until the tokens arrived); the Q barrier covers the writes.  The operands take them in place of the slots' old contents, and
-  // the regions receive them from the merge pass, after every chunk has read.
-  // Over an fp8 region the staged values are those of the codes the merge
-  // will store, exactly as a later call reads them.
+  // them back until the tokens arrived); the Q barrier covers the writes.
+  // V goes into the 8-slot block form (chunk_tokens), so that the value
+  // operands take a key group's tokens with one 16-byte read and a mask per
+  // tile: taken element by element, the 2-byte reads and their waits ran in
+  // turn and cost the call about 1 us.  The operands take the tokens in
+  // place of the slots' old contents, and the regions receive them from the
+  // merge pass, after every chunk has read.  Over an fp8 region the staged
+  // values are those of the codes the merge will store, exactly as a later
+  // call reads them.
   // Verify: the proposal-carrying chunk stages the S proposals' K and V the
   // same way (bf16, as they arrive, also over an fp8 ring), and its
   // proposal step takes its operands from there.
-  constexpr bool SUBP = stages_tokens<MODE>();
+  constexpr bool SUBP = MODE == MODE_GLOBAL && TOK;
   __bf16* const tok_k = chunk_tokens;
   __bf16* const tok_v = chunk_tokens + S * D;
   int pos0 = 0;
@@ -398,12 +419,17 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (FP8) {
       // piece t: values 4t .. 4t+3 of K's S*D then V's (token j = 4t/D of
       // K or V); LDS holds K then V, so piece t lands at tok_k[4t]
-      if (tok_piece) stage_token_piece4(p, chunk_tokens, S, D, threadIdx.x, tok_kbits);
+      if (tok_piece) stage_token_piece4(p, chunk_tokens, S, D, pos0, threadIdx.x, tok_kbits);
       for (int t = threadIdx.x + 64 * NW; tok_chunk && t < 2 * S * (D / 4); t += 64 * NW)
-        stage_token_piece4(p, chunk_tokens, S, D, t, load_token_piece4(p, b, g, D, t));
+        stage_token_piece4(p, chunk_tokens, S, D, pos0, t, load_token_piece4(p, b, g, D, t));
     } else if (tok_piece) {  // the thread's piece: token j, head dims 8*d8 .. +7
       *reinterpret_cast<u32x4*>(&tok_k[threadIdx.x * 8]) = tok_kbits;
-      *reinterpret_cast<u32x4*>(&tok_v[threadIdx.x * 8]) = tok_vbits;
+      const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
+      const int key = pos0 + j, bi = (key >> 3) - (pos0 >> 3), slot = key & 7;
+      uint16_t* vb = reinterpret_cast<uint16_t*>(tok_v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vb[(bi * D + d8 * 8 + i) * 8 + slot] = (uint16_t)(tok_vbits[i >> 1] >> (16 * (i & 1)));
     }
   }
   if constexpr (MODE == MODE_VERIFY) {
@@ -575,22 +601,27 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         cvt_v(h);
       }
       if constexpr (SUBP) {
-        if (tok_chunk) {  // values of the call's own tokens: element e of key group lq
+        if (tok_chunk) {  // values of the call's own tokens
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
+          for (int ks = 0; ks < KS; ++ks) {
+            // lane group lq's keys are the 8-slot block starting at `base`;
+            // m: its slots that hold the call's tokens
+            const int base = kh + 32 * ks + 8 * lq;
+            u32x4 m;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-              u32x4 w = __builtin_bit_cast(u32x4, vop[h][ks][dt]);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int j = kh + 32 * ks + 8 * lq + e - pos0;
-                if (j >= 0 && j < S) {
-                  const uint32_t nv = __builtin_bit_cast(uint16_t, tok_v[j * D + vdim(dt)]);
-                  w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | (nv << 16)) : ((w[e >> 1] & 0xFFFF0000u) | nv);
-                }
-              }
-              vop[h][ks][dt] = __builtin_bit_cast(bf16x8, w);
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const unsigned j0 = (unsigned)(base + 2 * e2 - pos0);
+              m[e2] = (j0 < (unsigned)S ? 0x0000FFFFu : 0u) | (j0 + 1u < (unsigned)S ? 0xFFFF0000u : 0u);
             }
+            if ((m[0] | m[1] | m[2] | m[3]) != 0u) {
+              const int bi = (base >> 3) - (pos0 >> 3);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(&tok_v[(bi * D + vdim(dt)) * 8]);
+                vop[h][ks][dt] = __builtin_bit_cast(bf16x8, (__builtin_bit_cast(u32x4, vop[h][ks][dt]) & ~m) | (w & m));
+              }
+            }
+          }
         }
       }
       if (!ph && kh + CK > n_keys) {  // last half: zero values of keys past the count
@@ -660,7 +691,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 // Up to 256 head dims two global workgroups stay resident per CU (eight
 // waves per SIMD, 64 registers a lane); 512 dims, and verify with its two
 // halves' operands, need more registers and keep one.
-template <int D, int NCT, bool FP8, int MODE>
+template <int D, int NCT, bool FP8, int MODE, bool TOK>
 __global__ void __launch_bounds__(64 * kChunkWaves)
 __attribute__((amdgpu_waves_per_eu(D <= 256 && MODE != MODE_VERIFY ? 8 : 4))) chunk_kernel(const AttnParams p) {
   __shared__ ChunkSmem<D, NCT> sm;
@@ -675,10 +706,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 256 && MODE != MODE_VERIFY ? 8 : 4))) ch
       unit = blockIdx.x / nring;
       rc = blockIdx.x - unit * nring;
     }
-    chunk_item<D, NCT, FP8, MODE>(p, sm, unit, rc);
+    chunk_item<D, NCT, FP8, MODE, TOK>(p, sm, unit, rc);
   } else {
     const int unit = blockIdx.x / p.nchunk;
-    chunk_item<D, NCT, FP8, MODE>(p, sm, unit, blockIdx.x - unit * p.nchunk);
+    chunk_item<D, NCT, FP8, MODE, TOK>(p, sm, unit, blockIdx.x - unit * p.nchunk);
   }
 }
 
@@ -959,15 +990,29 @@ namespace {
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+template <int D, int NCT, bool FP8, int MODE>
+void launch_chunk_kernel(bool tok, dim3 grid, dim3 block, size_t lds, hipStream_t s, const AttnParams& p) {
+  if constexpr (MODE == MODE_GLOBAL) {
+    if (tok) {
+      hipLaunchKernelGGL((chunk_kernel<D, NCT, FP8, MODE, true>), grid, block, lds, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((chunk_kernel<D, NCT, FP8, MODE, false>), grid, block, lds, s, p);
+}
+
 template <int D, int NCT, int MODE>
 hipError_t launch_chunks(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
   const dim3 grid(pl.units * pl.nchunk), block(64 * kChunkWaves);
-  const size_t tok_bytes =
-      (MODE == MODE_VERIFY || (MODE == MODE_GLOBAL && p.append)) ? (size_t)2 * p.S * D * sizeof(uint16_t) : 0;
+  const size_t tok_bytes = MODE == MODE_VERIFY ? (size_t)2 * p.S * D * sizeof(uint16_t)
+                           : (MODE == MODE_GLOBAL && p.append)
+                               ? ((size_t)p.S * D + (size_t)kTokenBlocks * D * 8) * sizeof(uint16_t)
+                               : 0;
+  const bool tok = MODE == MODE_GLOBAL && p.append;
   if (pl.fp8)
-    hipLaunchKernelGGL((chunk_kernel<D, NCT, true, MODE>), grid, block, tok_bytes, s, p);
+    launch_chunk_kernel<D, NCT, true, MODE>(tok, grid, block, tok_bytes, s, p);
   else
-    hipLaunchKernelGGL((chunk_kernel<D, NCT, false, MODE>), grid, block, tok_bytes, s, p);
+    launch_chunk_kernel<D, NCT, false, MODE>(tok, grid, block, tok_bytes, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool fp8_tokens = MODE == MODE_GLOBAL && p.append && pl.fp8;  // the merge stores codes
