@@ -185,10 +185,13 @@ def test_fused_global_verify_6005_keys(dtype):
 @pytest.mark.parametrize("S,G,D", [(4, 8, 512), (1, 8, 512), (2, 4, 64), (3, 4, 256), (1, 16, 128), (8, 4, 128)])
 def test_fused_global_shapes(S, G, D, dtype):
     # key counts: no context (proposals only), proposals across a 128-key
-    # chunk boundary and a 32-key tile boundary, chunk-aligned context.
-    # Over fp8 the value codes load in pairs of dims only at D=512, so the
-    # smaller head dims take the unpaired substitution of the call's tokens.
-    kc = np.array([S, 126 + S, 128 + S, 131, 700, 2000], np.int32)
+    # chunk boundary and a 32-key tile boundary, chunk-aligned context, and
+    # proposals from pos0 = 6, 317 (across an 8-slot value block inside a
+    # chunk: the staged tokens fill two blocks) and 254 (across a chunk
+    # boundary from an uneven slot).  Over fp8 the value codes load in pairs
+    # of dims only at D=512, so the smaller head dims take the unpaired
+    # substitution of the call's tokens.
+    kc = np.array([S, 126 + S, 128 + S, 131, 700, 2000, 6 + S, 317 + S, 254 + S], np.int32)
     kc = np.maximum(kc, S)
     B = kc.size
     g = synthetic.rng(73)
