@@ -909,10 +909,28 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
                    kStreamSplitTiles);
     tps = std::min(tps, pl->max_tiles);
   } else if (pl->units > 0 && pl->units < kNumCU) {
-    if (dec)
-      tps = std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 2 * kNumCU));
-    else
+    if (dec) {
+      // The split count that puts the fewest tiles on the busiest CU: with
+      // the splits spread evenly over the CUs, ceil(units * nsplit / CUs)
+      // splits of ceil(max_tiles / nsplit) tiles; ties go to fewer splits
+      // (less to combine), and a split keeps at least two tiles per wave.
+      // Against a fixed target of two splits per CU, at W=1024 (32 tiles),
+      // 8 KV heads x 256: B=12 24.8 -> 23.1 us, B=16 29.2 -> 28.7, B=20 39.0
+      // -> 35.5, B=24 43.5 -> 41.2, B=28 47.4 -> 38.4 (unsplit: at 224 units
+      // one round of whole units beats three splits per unit).
+      long best = -1;
+      for (int ns = 1; ns <= pl->max_tiles; ++ns) {
+        const int t = ceil_div(pl->max_tiles, ns);
+        if (ns > 1 && t < 2 * sh.kw) break;
+        const long load = (long)ceil_div((long)pl->units * ns, kNumCU) * t;
+        if (best < 0 || load < best) {
+          best = load;
+          tps = t;
+        }
+      }
+    } else {
       tps = std::max(4, ceil_div((long)pl->max_tiles * pl->units, 4 * kNumCU));
+    }
     tps = std::min(tps, pl->max_tiles);
   }
   pl->tiles_per_split = std::max(tps, 1);

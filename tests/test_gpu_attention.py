@@ -99,6 +99,19 @@ def test_decode_small_batch_uses_split_k():
     assert_parity(host_f64(out), ref, "B=16 split-K decode")
 
 
+@pytest.mark.parametrize("B", [12, 20, 28])
+def test_decode_split_counts(B):
+    # the split count minimises the busiest CU's tiles: B=12 two splits of
+    # 16 tiles, B=20 three splits (11, 11 and a ragged 10), B=28 none (224
+    # units in one round); positions include partial windows
+    w = synthetic.Workload("t", B=B, Hkv=8, G=8, D=256, W=1024)
+    g = synthetic.rng(24)
+    positions = synthetic.uniform_int(g, 0, 4096, B)
+    positions[:3] = (0, 300, 1023)
+    out, ref = decode_case(w, synthetic.sliding_decode(w, seed=24 + B, positions=positions))
+    assert_parity(host_f64(out), ref, f"B={B} decode")
+
+
 @pytest.mark.parametrize("ks,vs", [(2.0 ** -6, 2.0 ** -6), (0.00917, 0.01033)])
 def test_decode_fp8_ring(ks, vs):
     w = synthetic.Workload("t", B=12, Hkv=8, G=8, D=256, W=1024)

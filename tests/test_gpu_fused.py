@@ -123,6 +123,14 @@ def test_fused_decode_many_requests_no_split():
     check_decode(w, synthetic.sliding_decode(w, seed=65), "fused decode B=40")
 
 
+@pytest.mark.parametrize("B", [12, 20, 28])
+def test_fused_decode_split_counts(B):
+    # two, three (the last one ragged) and no splits per (request, KV head):
+    # the new token's tile falls in any split
+    w = synthetic.Workload("t", B=B, Hkv=8, G=8, D=256, W=1024, pos_lo=0, pos_hi=4096)
+    check_decode(w, synthetic.sliding_decode(w, seed=67 + B), f"fused decode B={B}")
+
+
 def test_fused_decode_small_batch_split_k():
     w = synthetic.MIXED_SLIDING
     assert swr.workspace_bytes(swr.SWR_OP_SWA_APPEND_DECODE, w.B, 1, w.Hq, w.Hkv, w.D, w.W) > 0
