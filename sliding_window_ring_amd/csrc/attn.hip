@@ -922,7 +922,7 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
       for (int ns = 1; ns <= pl->max_tiles; ++ns) {
         const int t = ceil_div(pl->max_tiles, ns);
         if (ns > 1 && t < 2 * sh.kw) break;
-        const long load = (long)ceil_div((long)pl->units * ns, kNumCU) * t;
+        const long load = (long)ceil_div((long)pl->units * ceil_div(pl->max_tiles, t), kNumCU) * t;
         if (best < 0 || load < best) {
           best = load;
           tps = t;
