@@ -27,9 +27,10 @@
 //     P kept in LDS, and writes the chunk's unnormalised rows with their
 //     (max, sum).  In a verify call ring chunk 0 of each (request, KV head)
 //     also takes the S proposals (read from their own buffers) as a step
-//     of their own, run while its ring loads are in flight: a separate
-//     proposal workgroup would start only when a ring chunk leaves its CU,
-//     a second round at the end of the pass.
+//     of their own (up to 256 head dims ahead of its ring halves, while
+//     their loads are in flight): a separate proposal workgroup would start
+//     only when a ring chunk leaves its CU, a second round at the end of the
+//     pass.
 //   pass 2: merges the chunk partials, weights 2^(m_c - M), sums in a fixed
 //     order, division by the weighted row sum.  With many chunks per row
 //     (global) one workgroup per (request, KV head, row, quarter of the
@@ -418,7 +419,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
   if constexpr (SUBP) {
     if (FP8) {
       // piece t: values 4t .. 4t+3 of K's S*D then V's (token j = 4t/D of
-      // K or V); LDS holds K then V, so piece t lands at tok_k[4t]
+      // K or V); a K piece lands at tok_k[4t], a V piece in the V blocks
       if (tok_piece) stage_token_piece4(p, chunk_tokens, S, D, pos0, threadIdx.x, tok_kbits);
       for (int t = threadIdx.x + 64 * NW; tok_chunk && t < 2 * S * (D / 4); t += 64 * NW)
         stage_token_piece4(p, chunk_tokens, S, D, pos0, t, load_token_piece4(p, b, g, D, t));
