@@ -76,8 +76,20 @@ attn_kernel(const AttnParams p) {
   const int lr = lane & 15;  // row within a 16-row column tile; also key row of the K operand
   const int lq = lane >> 4;  // lane group: which 8 keys / 8 dims of the k axis
 
-  const int unit = blockIdx.x / p.nsplit;
-  const int split = blockIdx.x - unit * p.nsplit;
+  // gstream: the split balanced from the requests' key counts (split tiles
+  // [st_lo, st_hi)); the workgroups past the last split exit here
+  int unit, split, st_lo = 0, st_hi = 0;
+  if constexpr (MODE == MODE_GSTREAM) {
+    const StreamSplit x = stream_split(p, blockIdx.x);
+    if (x.unit < 0) return;
+    unit = x.unit;
+    split = x.split;
+    st_lo = (int)((long)x.split * x.tiles / x.n);
+    st_hi = (int)((long)(x.split + 1) * x.tiles / x.n);
+  } else {
+    unit = blockIdx.x / p.nsplit;
+    split = blockIdx.x - unit * p.nsplit;
+  }
   const int Hkv = p.Hkv, G = p.G, S = p.S;
   const int b = unit / Hkv;
   const int g = unit - b * Hkv;
@@ -103,8 +115,8 @@ attn_kernel(const AttnParams p) {
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
   const int nt_total = nt_region + (MODE == MODE_VERIFY ? 1 : 0);
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min(nt_total, t_begin + p.tiles_per_split);
+  const int t_begin = MODE == MODE_GSTREAM ? st_lo : split * p.tiles_per_split;
+  const int t_end = min(nt_total, MODE == MODE_GSTREAM ? st_hi : t_begin + p.tiles_per_split);
   if (t_begin >= t_end) return;  // empty split: the combine step skips it
   const int n_it = (t_end - t_begin + KW - 1) / KW;
 
@@ -581,7 +593,8 @@ attn_kernel(const AttnParams p) {
     return f32x4{o[ct][t][h], o[ct][t + 1][h], o[ct][t][h + 1], o[ct][t + 1][h + 1]};
   };
 
-  const size_t part = (size_t)unit * p.nsplit + split;
+  // partial slot: gstream, the split's number (the workgroup); else by unit
+  const size_t part = MODE == MODE_GSTREAM ? (size_t)blockIdx.x : (size_t)unit * p.nsplit + split;
   if (KW == 1) {
     // This wave holds rows ct*16+lr, dims d_base + 16*dt + 4*lq + 0..3.
 #pragma unroll
@@ -678,13 +691,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const AttnParams p, int D,
   const int d4 = (rem - row * per_row) * 4;
   const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
 
-  int n_keys;
-  if (MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND)
-    n_keys = min(p.pos[b] + 1, p.cap);
-  else if (MODE == MODE_VERIFY)
-    n_keys = min(p.pos[b], p.cap);
-  else
-    n_keys = min(key_count_of(p, b), region_cap(p, b));
+  static_assert(MODE == MODE_DECODE || MODE == MODE_VERIFY, "a streamed call's splits go to merge_grouped");
+  int n_keys = MODE == MODE_VERIFY ? min(p.pos[b], p.cap) : min(p.pos[b] + 1, p.cap);
   n_keys = max(n_keys, 0);
   const int nt_total = ((n_keys + 31) >> 5) + (MODE == MODE_VERIFY ? 1 : 0);
   const int nvalid = min(p.nsplit, (nt_total + p.tiles_per_split - 1) / p.tiles_per_split);
@@ -844,14 +852,15 @@ hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
 // least this many 32-key tiles: the split-K partials are then a small
 // fraction of the bytes read, and there are enough splits to fill the chip.
 constexpr long kStreamTiles = 2048;
-// Most tiles per split of a streamed global call: short enough that the
-// splits of unequal requests balance across the compute units, long enough
-// that the splits of a batch of long contexts fit the chip's workgroup slots
-// in about one round.  Measured on the 16-request mixed step (contexts
-// log-uniform in 512 .. 65536, 2 KV heads x 512): 8 / 16 / 24 / 32 / 40 / 48
-// tiles gave 241 / 227 / 231 / 213 / 227 / 248 us (bf16) and 142 / 130 /
-// 151 / 114 / 128 / 144 us (fp8).
-constexpr int kStreamSplitTiles = 32;
+// Workgroups of a streamed global call's split pass (at least): two
+// resident per CU, so that its splits, balanced from the requests' key
+// counts on the device (stream_split), run in one round.  Against fixed
+// splits of up to 32 tiles (spread over about four per CU if every unit had
+// the longest one's tiles), same box: the 16-request mixed step's global
+// layer (contexts log-uniform in 512 .. 65536, 2 KV heads x 512) 213 ->
+// 201 us, a B=56 layer with contexts U[1024, 4096] 120.5 -> 104.3 us; 768,
+// 1024 and 1536 workgroups (smaller splits, more rounds) were slower on both.
+constexpr long kStreamWorkgroups = 2 * kNumCU;
 
 bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int cap_or_max_keys,
                     AttnPlan* pl) {
@@ -900,14 +909,9 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   // Split-K across workgroups only when the units alone do not fill the chip.
   int tps = pl->max_tiles;
   if (mode == MODE_GSTREAM) {
-    // about four splits per CU if every unit had max_tiles; real requests are
-    // shorter (their splits past the key count exit at once), so aiming at
-    // two left the non-empty splits too few to spread evenly: B=56 decode
-    // contexts U[1024, 4096] took 123 us per global layer against 108 us,
-    // the 16-request mixed step 222 us either way; eight made both slower
-    tps = std::min(std::max(2 * sh.kw, ceil_div((long)pl->max_tiles * pl->units, 4 * kNumCU)),
-                   kStreamSplitTiles);
-    tps = std::min(tps, pl->max_tiles);
+    // the split sizes come from the key counts, on the device (stream_split);
+    // here only the grid: units * nsplit workgroups, nsplit >= 2
+    tps = 1;
   } else if (pl->units > 0 && pl->units < kNumCU) {
     if (dec) {
       // The split count that puts the fewest tiles on the busiest CU: with
@@ -935,6 +939,8 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
   }
   pl->tiles_per_split = std::max(tps, 1);
   pl->nsplit = ceil_div(pl->max_tiles, pl->tiles_per_split);
+  if (mode == MODE_GSTREAM)
+    pl->nsplit = pl->units > 0 ? (int)ceil_div(std::max(kStreamWorkgroups, 2L * pl->units), pl->units) : 1;
   pl->ws_bytes =
       pl->nsplit > 1 ? (size_t)pl->units * pl->nsplit * rows * (size_t)(D + 2) * sizeof(float) + 256 : 0;
 
@@ -969,17 +975,15 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  // many splits per row (a long streamed global call): spread each row's
-  // splits over thread groups instead of one thread walking them all
-  if (pl.mode == MODE_GSTREAM && pl.nsplit > 16) return launch_split_merge(pl, p, s);
+  // a streamed global call: its splits, numbered from the key counts, merged
+  // with each row's splits spread over thread groups
+  if (pl.mode == MODE_GSTREAM) return launch_split_merge(pl, p, s);
   const long total = (long)pl.units * pl.rows * (pl.D / 4);
   const int blocks = ceil_div(total, 256);
   if (pl.mode == MODE_DECODE || pl.mode == MODE_DECODE_APPEND)
     hipLaunchKernelGGL(combine_kernel<MODE_DECODE>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
-  else if (pl.mode == MODE_VERIFY)
-    hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
   else
-    hipLaunchKernelGGL(combine_kernel<MODE_GSTREAM>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
+    hipLaunchKernelGGL(combine_kernel<MODE_VERIFY>, dim3(blocks), dim3(256), 0, s, p, pl.D, pl.units);
   return hipGetLastError();
 }
 

@@ -80,15 +80,12 @@ constexpr int kChunkWaves = kChunkKeys / 8;     // 16 waves: two per 16-key subt
 constexpr int kVerifyChunkKeys = 2 * kChunkKeys;  // verify ring chunks: two halves in turn
 
 // Chunks of one (request, KV head) that pass 1 filled, a prefix of the
-// launch's chunks: the region chunks up to the key count (verify: after the
-// proposal chunk).  A streamed global call (attn.hip) fills one partial per
-// non-empty split of tiles_per_split 32-key tiles, in the same layout.
+// launch's chunks: the region chunks up to the key count (verify: the ring
+// chunks, chunk 0 holding the proposals).  A streamed global call (attn.hip)
+// fills one partial per split, numbered by stream_split; merge_grouped
+// finds a unit's run of them there.
 template <int MODE>
 __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
-  if (MODE == MODE_GSTREAM) {
-    const int tiles = (region_keys<MODE_GLOBAL>(p, b) + 31) / 32;
-    return min((tiles + p.tiles_per_split - 1) / p.tiles_per_split, p.nchunk);
-  }
   const int ck = MODE == MODE_VERIFY ? kVerifyChunkKeys : kChunkKeys;
   const int n = (region_keys<MODE>(p, b) + ck - 1) / ck;
   return min(MODE == MODE_VERIFY ? max(n, 1) : n, p.nchunk);  // verify: chunk 0 holds the proposals
@@ -821,12 +818,15 @@ struct RunningRow {
 };
 
 // Adds chunks c = c0 + j*step (j < kMergeBatch, c < nvalid) of the row at
-// `slot0` (+ c*rows), four dims at `d`.  On the first batch the request's
-// chunk count is read, and `issued` runs, after the batch's loads are
-// issued: work that waits only for earlier loads then overlaps them.
+// `slot0` (+ c*rows), four dims at `d`; `navail` partials are stored for the
+// row.  On the first batch the request's chunk count is read (the chunked
+// form; a streamed call's count is known), and `issued` runs, after the
+// batch's loads are issued: work that waits only for earlier loads then
+// overlaps them.
 template <int MODE, typename F>
 __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, size_t slot0, int d, int c0,
-                                            int step, bool first, int& nvalid, RunningRow& r, F&& issued) {
+                                            int step, int navail, bool first, int& nvalid, RunningRow& r,
+                                            F&& issued) {
   float m[kMergeBatch], l[kMergeBatch];
   f32x4 a[kMergeBatch];
 #pragma unroll
@@ -834,7 +834,7 @@ __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, s
     m[j] = -INFINITY;
     l[j] = 0.f;
     a[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (c0 + j * step < p.nchunk) {  // past the launch's chunks: no load at all
+    if (c0 + j * step < navail) {  // past the stored partials: no load at all
       const size_t at = slot0 + (size_t)(c0 + j * step) * p.rows;
       m[j] = p.ws_pml[at * 2];
       l[j] = p.ws_pml[at * 2 + 1];
@@ -842,7 +842,7 @@ __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, s
     }
   }
   if (first) {
-    nvalid = valid_chunks<MODE>(p, b);
+    if (MODE != MODE_GSTREAM) nvalid = valid_chunks<MODE>(p, b);
     issued();
   }
   float mb = r.M;
@@ -890,7 +890,15 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
   const int grp = tid / TPG;
   const int d = quarter * PART + (tid - grp * TPG) * 4;
-  const size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
+  // the row's partials: the chunked form stores nchunk per unit; a streamed
+  // call's unit has n splits from its first one on (stream_split)
+  size_t slot0 = (size_t)unit * p.nchunk * p.rows + row;
+  int navail = p.nchunk;
+  if constexpr (MODE == MODE_GSTREAM) {
+    const StreamSplit x = stream_split(p, 0, unit);
+    slot0 = (size_t)x.first * p.rows + row;
+    navail = x.n;
+  }
 
   // the call's tokens, this quarter's dims: bf16 as 8-dim pieces in the
   // row-0 workgroup; fp8 one value per thread, `per` values to a row
@@ -916,10 +924,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
     tokens_stored = true;
   };
   RunningRow r;
-  int nvalid = p.nchunk;
+  int nvalid = navail;
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
     // the tokens' stores go out once the first batch's loads are in flight
-    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, c0 == grp, nvalid, r, [&] { store_tokens(); });
+    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, navail, c0 == grp, nvalid, r, [&] { store_tokens(); });
   }
   store_tokens();  // a group with no chunk to merge
   if constexpr (FP8) {  // rows * kMergeThreads < tok_values: the rest in turn
@@ -971,7 +979,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
-    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, c0 == 0, nvalid, r, [] {});
+    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, p.nchunk, c0 == 0, nvalid, r, [] {});
   }
   if (MODE == MODE_GLOBAL && p.append) {
     if constexpr (FP8) {
@@ -981,6 +989,27 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
       for (int j = 0; j < p.S; ++j) store_call_token<false>(p, D, b, g, load_call_token(p, D, b, g, j, d / 8));
     }
   }
+  store_row4(p, D, b, g, row, d, r.L, r.O);
+}
+
+// A streamed global call with few splits per unit: one thread per four
+// output dims of one row takes every split of its unit in order (kMergeBatch
+// loads at a time), one unit per workgroup (`chunks` workgroups each), so
+// that the split numbering (stream_split) is workgroup-uniform.
+__global__ void __launch_bounds__(kMergeThreads) merge_stream_flat(const AttnParams p, int D, int chunks) {
+  const int unit = blockIdx.x / chunks;
+  const int local = (blockIdx.x - unit * chunks) * kMergeThreads + threadIdx.x;
+  const StreamSplit x = stream_split(p, 0, unit);  // every lane takes part
+  const int per_row = D / 4;
+  if (local >= p.rows * per_row) return;
+  const int row = local / per_row;
+  const int d = (local - row * per_row) * 4;
+  const int b = unit / p.Hkv, g = unit - (unit / p.Hkv) * p.Hkv;
+  const size_t slot0 = (size_t)x.first * p.rows + row;
+  RunningRow r;
+  int nvalid = x.n;
+  for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch)
+    merge_batch<MODE_GSTREAM>(p, D, b, slot0, d, c0, 1, x.n, c0 == 0, nvalid, r, [] {});
   store_row4(p, D, b, g, row, d, r.L, r.O);
 }
 
@@ -1050,7 +1079,15 @@ hipError_t launch_split_merge(const AttnPlan& pl, const AttnParams& p0, hipStrea
   AttnParams p = p0;
   p.ws_part = p0.ws_acc;
   p.ws_pml = p0.ws_ml;
-  p.nchunk = pl.nsplit;
+  p.nchunk = pl.nsplit;  // unused by the streamed merges: each unit's splits come from stream_split
+  if (pl.nsplit <= 16) {
+    // few splits per unit on average: a thread per four dims walks them
+    // (at B=56 x 2 KV heads x 512, about 5 per unit: 6.6 us, against 32 us
+    // for the grouped merge's 3584 mostly idle workgroups)
+    const int chunks = cdiv((long)pl.rows * (pl.D / 4), kMergeThreads);
+    hipLaunchKernelGGL(merge_stream_flat, dim3(pl.units * chunks), dim3(kMergeThreads), 0, s, p, pl.D, chunks);
+    return hipGetLastError();
+  }
   const dim3 grid(pl.units * pl.rows * 4), block(kMergeThreads);
   switch (pl.D) {
     case 64: hipLaunchKernelGGL((merge_grouped<64, MODE_GSTREAM>), grid, block, 0, s, p); break;

@@ -63,6 +63,78 @@ __device__ __forceinline__ int qpos_of(const AttnParams& p, int b, int i) {
   return p.qpos_from_pos0 ? p.pos[b] + i : p.pos[b * p.S + i];
 }
 
+// Streamed global calls: the splits, balanced over the grid from the
+// requests' key counts.  Request b has stream_tiles(b) tiles of 32 keys (its
+// keys up to its region's capacity); T is the tiles of all (request, KV head)
+// units and P = units * nsplit the grid's workgroups.  A split takes at most
+// R = ceil(T / (P - units)) tiles, unit u takes n_u = ceil(tiles_u / R)
+// splits (so that sum n_u <= T / R + units <= P), split s the tiles
+// [s * tiles_u / n_u, (s + 1) * tiles_u / n_u), and the splits are numbered
+// request by request, KV head by KV head: workgroup w computes split w (the
+// rest exit), and the merge finds unit u's partials at first_u .. first_u +
+// n_u - 1.  The split pass and the merge compute the numbering alike.
+__device__ __forceinline__ int stream_tiles(const AttnParams& p, int b) {
+  const int cap = p.cap_b ? max(min(p.cap_b[b], p.cap), 0) : p.cap;
+  return (max(min(key_count_of(p, b), cap), 0) + 31) >> 5;
+}
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+struct StreamSplit {
+  int unit = -1;  // -1: past the last split
+  int split = 0, first = 0, n = 0, tiles = 0;
+};
+// The split numbered w (unit < 0), or unit's first split and split count
+// (w ignored).  Every lane of the wave takes part (64 requests at a time, one
+// per lane: the key counts load together, and wave scans number the splits);
+// the result is wave-uniform.
+__device__ __forceinline__ StreamSplit stream_split(const AttnParams& p, int w, int unit = -1) {
+  const int lane = threadIdx.x & 63;
+  long t = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int tb = b < p.B ? stream_tiles(p, b) : 0;
+    t += __builtin_amdgcn_readlane(wave_prefix_sum(tb), 63);
+  }
+  t *= p.Hkv;
+  const long room = (long)p.B * p.Hkv * (p.nsplit - 1);  // P - units > 0: nsplit >= 2
+  const int r = (int)max(1L, (t + room - 1) / room);
+  StreamSplit x;
+  int first = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int tb = b < p.B ? stream_tiles(p, b) : 0;
+    const int n = (tb + r - 1) / r;
+    const int cnt = p.Hkv * n;
+    const int incl = first + wave_prefix_sum(cnt);
+    const int excl = incl - cnt;
+    const bool here = b < p.B && (unit >= 0 ? b == unit / p.Hkv : (w >= excl && w < incl));
+    const unsigned long long m = __ballot(here);
+    if (m) {
+      const int src = __ffsll(m) - 1;
+      const int nb = __builtin_amdgcn_readlane(n, src);
+      const int eb = __builtin_amdgcn_readlane(excl, src);
+      const int bb = b0 + src;
+      const int g = unit >= 0 ? unit - bb * p.Hkv : (w - eb) / nb;
+      x.unit = bb * p.Hkv + g;
+      x.first = eb + g * nb;
+      x.n = nb;
+      x.tiles = __builtin_amdgcn_readlane(tb, src);
+      x.split = unit >= 0 ? 0 : w - x.first;
+      return x;
+    }
+    first = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return x;
+}
+
 // Launch geometry chosen on the host for one attention call.
 struct AttnPlan {
   int mode, D, fp8;
