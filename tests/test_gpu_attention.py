@@ -337,6 +337,39 @@ def test_global_streamed_shapes(S, G, D):
     assert_parity(host_f64(out), ref, f"streamed global S={S} G={G} D={D}")
 
 
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+def test_global_streamed_many_requests(dtype):
+    # 70 requests (the split numbering reads the key counts 64 at a time, one
+    # per lane), some with a single key or a single tile, each region with a
+    # capacity of its own; streamed: units x tiles >= 2048
+    S, G, D, hkv = 1, 8, 128, 2
+    g = synthetic.rng(38)
+    B = 70
+    kc = synthetic.uniform_int(g, 1, 2000, B)
+    kc[:5] = (1, 1, 31, 2000, 33)
+    caps = np.maximum((kc + 63) // 64 * 64, 64).astype(np.int32)
+    assert B * hkv * -(-int(kc.max()) // 32) >= 2048
+    cap = int(caps.max())
+    k = synthetic.normal_bf16(g, (B, cap, hkv, D))
+    v = synthetic.normal_bf16(g, (B, cap, hkv, D))
+    q = synthetic.normal_bf16(g, (B, S, hkv * G, D))
+    q_pos = np.maximum(kc - 1, 0).astype(np.int32).reshape(B, S)
+    ks, vs = (4.4 / 448, 4.1 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    rbs = [oracle.region_bytes(int(c), hkv, D, dtype) for c in caps]
+    ko = np.concatenate([[0], np.cumsum(rbs)[:-1]]).astype(np.int64)
+    vo = ko.copy()
+    kp = np.zeros(int(sum(rbs)), np.uint8)
+    vp = np.zeros(int(sum(rbs)), np.uint8)
+    oracle.kv_append(kp, vp, ko, vo, cap, dtype, ks, vs, k, v, np.zeros(B, np.int32), kc, wrap=False, caps=caps)
+    scale = 1.0 / np.sqrt(D)
+    ref = oracle.global_attend(kp, vp, ko, vo, cap, dtype, ks, vs, q, q_pos, kc, hkv, scale, caps=caps)
+    L = layer(kp, vp, ko, vo, cap, dtype, ks, vs)
+    L.cap_b = dev_i32(caps)
+    out = swr.global_attend(L, dev_bf16(q), dev_i32(q_pos), dev_i32(kc), int(kc.max()), hkv, scale)
+    torch.cuda.synchronize()
+    assert_parity(host_f64(out), ref, "streamed global, 70 requests")
+
+
 def test_global_streamed_fp8():
     S, G, D = 4, 8, 512
     x = streamed_inputs(S, G, D, seed=37)
