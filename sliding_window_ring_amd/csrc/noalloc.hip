@@ -19,7 +19,9 @@ namespace {
 
 // Largest workspace the static array serves: 16 MiB, enough for the
 // chunked global form of a 2-KV-head x 512-dim layer of 32 rows up to about
-// 16,000 keys at B = 1 (64 KB of partials per 128 keys and KV head).
+// 16,000 keys at B = 1 (64 KB of partials per 128 keys and KV head).  A
+// streamed call (units x tiles >= 2048) keeps at least 512 partial slots,
+// about 32 MiB at that shape, and gets SWR_ERR_WORKSPACE here.
 constexpr size_t kScratchBytes = size_t(16) << 20;
 constexpr int kMaxDevices = 64;
 
