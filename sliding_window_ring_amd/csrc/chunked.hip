@@ -120,7 +120,7 @@ __device__ __forceinline__ int valid_chunks(const AttnParams& p, int b) {
 // pos0-1 for proposal i (position pos0+i sees positions >= pos0+i-W+1);
 // verify proposal step -- proposal j <= i.  Over an fp8 ring the proposals
 // are bf16 values: their scores take scale * log2(e) without k_scale, and
-// their P is divided by v_scale before its bf16 rounding, since pass 2
+// their value product is multiplied by 1/v_scale in fp32, since pass 2
 // multiplies every chunk by v_scale.
 // Fused append (a global call storing its own S tokens at pos0 .. pos0+S-1):
 // the chunk holding their slots takes them in place of the slots' old
@@ -339,8 +339,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         if (tok_piece) {
           const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
           const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
-          tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
-          tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+          tok_kbits = load16_global(p.k_prop + src);
+          tok_vbits = load16_global(p.v_prop + src);
         }
       }
     }
@@ -350,8 +350,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
     if (tok_piece) {
       const int j = threadIdx.x / (D / 8), d8 = threadIdx.x - j * (D / 8);
       const size_t src = ((size_t)(b * S + j) * Hkv + g) * D + (size_t)d8 * 8;
-      tok_kbits = *reinterpret_cast<const u32x4*>(p.k_prop + src);
-      tok_vbits = *reinterpret_cast<const u32x4*>(p.v_prop + src);
+      tok_kbits = load16_global(p.k_prop + src);
+      tok_vbits = load16_global(p.v_prop + src);
     }
   }
   // Q of the group's rows, once per workgroup, into LDS.  Rows past p.rows
@@ -372,7 +372,7 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       const int row = min(idx, QPIECES - 1) / (D / 8), d8 = (min(idx, QPIECES - 1) - row * (D / 8)) * 8;
       const int rr = row < p.rows ? row : 0;
       const int i = rr / G, hq = rr - (rr / G) * G;
-      qv[k] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)(b * S + i) * p.Hq + g * G + hq) * D + d8);
+      qv[k] = as_bf16x8(load16_global(p.q + ((size_t)(b * S + i) * p.Hq + g * G + hq) * D + d8));
     }
   };
   auto store_q = [&] {
@@ -467,8 +467,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
 
   // Verify: the proposals' step (h = NH), keys 0 .. S-1 of the step, bf16
   // values over any ring (over an fp8 ring their scores take scale *
-  // log2(e) without k_scale, and their P is divided by v_scale before it is
-  // rounded to bf16, since the merge multiplies by v_scale).  Up to 256
+  // log2(e) without k_scale, and their value product is multiplied by
+  // 1/v_scale in fp32, since the merge multiplies by v_scale).  Up to 256
   // head dims it comes first: its operands are in LDS already, so it needs
   // no K of the ring's and runs while the last waves' K loads are still in
   // flight.  At 512 dims the ring's K registers in flight leave it no room,
@@ -561,14 +561,8 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
         bf16x4 pb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = fast_exp2(sv[e4 + e] - m_use);
-          if (FP8 && ph) {
-            pb[e] = (__bf16)(pe * p.inv_v_scale);
-            ps += (float)(__bf16)pe;
-          } else {
-            pb[e] = (__bf16)pe;
-            ps += (float)pb[e];
-          }
+          pb[e] = (__bf16)fast_exp2(sv[e4 + e] - m_use);
+          ps += (float)pb[e];
         }
         *reinterpret_cast<bf16x4*>(&pbuf[srow][kk + e4]) = pb;
       }
@@ -642,6 +636,17 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
           const float a = sm.alpha[ct * 16 + lr];
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[ct][dt] *= a;
+        }
+        if (FP8 && ph) {
+          // over an fp8 ring the rows hold values in units of v_scale: the
+          // proposals' product (bf16 values, P as for any key; zero past
+          // key 31) is taken on its own and scaled by 1/v_scale in fp32, so
+          // that a row seeing one proposal alone returns its value exactly
+          const bf16x8 pt = *reinterpret_cast<const bf16x8*>(&pbuf[ct * 16 + lr][8 * lq]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            o[ct][dt] += mfma16x16x32(vop[h][0][dt], pt, f32x4{0.f, 0.f, 0.f, 0.f}) * p.inv_v_scale;
+          continue;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {

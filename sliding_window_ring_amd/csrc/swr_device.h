@@ -27,6 +27,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufferWord3);
 }
 
+// A 16-byte load from global memory through a pointer the compiler is told
+// is global.  Where its address-space inference loses track of a pointer
+// taken from the kernel's arguments it emits a flat load instead, which also
+// counts on the LDS counter: the next LDS access then waits for every load
+// in flight, not just this one (measured 0.2 us on a verify call).
+__device__ __forceinline__ u32x4 load16_global(const void* ptr) {
+  return *(const __attribute__((address_space(1))) u32x4*)ptr;
+}
+
 // A value the caller knows is the same in every lane of the wave (a load
 // whose address depends only on the workgroup), moved to scalar registers.
 // Without it a buffer resource built from a vector load's result lives in

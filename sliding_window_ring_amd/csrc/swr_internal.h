@@ -31,7 +31,7 @@ struct AttnParams {
   float qk_scale;          // scale * k_scale * log2(e): scores in the base-2 domain
   float v_scale;           // applied to the normalised output
   float qk_scale_prop;     // verify: scale * log2(e) for the bf16 proposal keys (no k_scale)
-  float inv_v_scale;       // verify: 1 / v_scale, applied to the bf16 proposal values
+  float inv_v_scale;       // verify: 1 / v_scale, applied to the bf16 proposals' value product
   const uint16_t* q;       // bf16 [B][S][Hq][D]
   uint16_t* out;           // bf16 [B][S][Hq][D]
   const int32_t* pos;      // decode: pos[B]; verify: pos0[B]; global (both forms): q_pos[B][S]

@@ -143,6 +143,14 @@ def verify_case(w, x, dtype=oracle.BF16, ks=1.0, vs=1.0):
     return out, ref
 
 
+def assert_lone_proposal_exact(out, x, w):
+    """Request 0 starts at position 0: its ring holds nothing yet, so the
+    rows of its first proposal see that proposal alone and return its value
+    bits exactly (over an fp8 ring too: the proposals are bf16)."""
+    assert int(x["p0"][0]) == 0
+    assert np.array_equal(host_bits(out)[0, 0], np.repeat(x["v_prop"][0, 0], w.G, axis=0))
+
+
 def test_verify_b8_full_workload():
     w = synthetic.SWA_VERIFY
     out, ref = verify_case(w, synthetic.sliding_verify(w))
@@ -156,6 +164,7 @@ def test_verify_proposal_counts(S, G):
     x = synthetic.sliding_verify(w, seed=31, positions=(0, 1, 5, 126, 127, 128, 129, 1000))
     out, ref = verify_case(w, x)
     assert_parity(host_f64(out), ref, f"verify S={S} G={G}")
+    assert_lone_proposal_exact(out, x, w)
 
 
 @pytest.mark.parametrize("D", [256, 512])
@@ -171,6 +180,7 @@ def test_verify_ring_chunk_halves(dtype, D):
     ks, vs = (4.2 / 448, 4.4 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
     out, ref = verify_case(w, x, dtype, ks, vs)
     assert_parity(host_f64(out), ref, "verify ring chunk halves")
+    assert_lone_proposal_exact(out, x, w)
 
 
 @pytest.mark.parametrize("D", [64, 128, 512])
@@ -198,6 +208,7 @@ def test_verify_fp8_ring(D, S, G):
     x = synthetic.sliding_verify(w, seed=38, positions=(0, 5, 256, 1000))
     out, ref = verify_case(w, x, oracle.FP8, 0.0102, 0.0089)
     assert_parity(host_f64(out), ref, f"fp8 verify D={D} S={S} G={G}")
+    assert_lone_proposal_exact(out, x, w)
 
 
 # ------------------------------------------------------------------ global
