@@ -921,7 +921,10 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
       // Against a fixed target of two splits per CU, at W=1024 (32 tiles),
       // 8 KV heads x 256: B=12 24.8 -> 23.1 us, B=16 29.2 -> 28.7, B=20 39.0
       // -> 35.5, B=24 43.5 -> 41.2, B=28 47.4 -> 38.4 (unsplit: at 224 units
-      // one round of whole units beats three splits per unit).
+      // one round of whole units beats three splits per unit).  Counting two
+      // workgroups per CU in this model, or letting a split go down to one
+      // tile per wave, measured slower: B=12 23.1 -> 24.9 us, B=28 38.3 ->
+      // 44.3, 56 units of one KV head 17.7 -> 18.3.
       long best = -1;
       for (int ns = 1; ns <= pl->max_tiles; ++ns) {
         const int t = ceil_div(pl->max_tiles, ns);
