@@ -47,3 +47,25 @@ def test_algorithmic_bytes_of_the_step():
     # the padded tail the kernels may touch is not counted
     padded = FACTS["global_key_count"]["padded_to"]
     assert (padded - bench.KC) * bench.GHKV * bench.GD * BF16 * 2 == 45_056
+
+
+def test_traffic_is_tied_to_the_kernel_code_not_its_comments(tmp_path):
+    """The roofline's counter traffic is reported only while the kernel
+    sources hash to the value recorded with the counters: a comment or blank
+    line edit keeps the hash, any code edit changes it."""
+    src = ("// kernel\n__global__ void k(float* x) {\n  /* two\n     lines */ x[0] = 1.f;  // store\n\n}\n")
+    variants = {
+        "same": src,
+        "comment": src.replace("// store", "// the store").replace("/* two", "/* three"),
+        "blank": src.replace("\n\n", "\n\n\n"),
+        "code": src.replace("1.f", "2.f"),
+        "code_in_comment_line": src.replace("// kernel\n", "// kernel\nint z;\n"),
+    }
+    hashes = {}
+    for name, text in variants.items():
+        f = tmp_path / f"{name}.hip"
+        f.write_text(text)
+        hashes[name] = bench.kernel_source_hash([str(f)])
+    assert hashes["comment"] == hashes["same"] == hashes["blank"]
+    assert hashes["code"] != hashes["same"]
+    assert hashes["code_in_comment_line"] != hashes["same"]
