@@ -403,7 +403,10 @@ def decode_stack(swr, torch, randn, dev):
     one global, at B=56 with contexts U[1024, 4096].  Every layer appends its
     token and attends (swr_swa_append_decode, swr_global_append_attend with
     S=1) over rings and regions of its own, 30 GB in all, so nothing is read
-    from the caches; the 60 calls are one HIP graph, timed over 5 replays."""
+    from the caches; all of them are carved from one pool by the library
+    (swr_pool_alloc_ring / swr_pool_alloc_global, layer by layer, request by
+    request), as a server holds them.  The 60 calls are one HIP graph, timed
+    over 5 replays."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(1006)
     pos = torch.randint(1024, 4097, (B,), device=dev, dtype=torch.int32, generator=gen)
@@ -413,25 +416,28 @@ def decode_stack(swr, torch, randn, dev):
     hk, hv = randn(B, W, HKV, D), randn(B, W, HKV, D)
     gkh, gvh = randn(B, max(ctx) + 1, GHKV, GD), randn(B, max(ctx) + 1, GHKV, GD)
     rb = swr.region_bytes(W, HKV, D)
-    roff = torch.arange(B, device=dev, dtype=torch.int64) * rb
     grb = [swr.region_bytes(c, GHKV, GD) for c in caps]
-    starts, at = [], 0
-    for n in grb:
-        starts.append(at)
-        at += n
-    goff = torch.tensor(starts, device=dev, dtype=torch.int64)
-    capb = torch.tensor(caps, device=dev, dtype=torch.int32)
+    pool = swr.Pool(50 * B * 2 * rb + 10 * 2 * sum(grb) + (64 << 20))
     sliding, glob = [], []
     for _ in range(50):
-        k = torch.empty(B * rb, dtype=torch.uint8, device=dev)
-        v = torch.empty_like(k)
-        L = swr.KVLayer(k, v, roff, roff, W)
+        ko, vo = [], []
+        for _b in range(B):
+            k_off, v_off, _cap = pool.alloc_ring(W, HKV, D)
+            ko.append(k_off)
+            vo.append(v_off)
+        L = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor(ko, device=dev), torch.tensor(vo, device=dev), W)
         swr.ring_kv_append(L, hk, hv, (pos - W).to(torch.int32))
         sliding.append(L)
     for _ in range(10):
-        k = torch.zeros(sum(grb), dtype=torch.uint8, device=dev)
-        v = torch.zeros_like(k)
-        L = swr.KVLayer(k, v, goff, goff, max(caps), cap_b=capb)
+        ko, vo, cb = [], [], []
+        for c in ctx:
+            k_off, v_off, cap = pool.alloc_global(c + 1, GHKV, GD)
+            ko.append(k_off)
+            vo.append(v_off)
+            cb.append(cap)
+        assert cb == caps
+        L = swr.KVLayer(pool.buffer, pool.buffer, torch.tensor(ko, device=dev), torch.tensor(vo, device=dev),
+                        max(caps), cap_b=torch.tensor(caps, device=dev, dtype=torch.int32))
         swr.ring_kv_append(L, gkh, gvh, torch.zeros(B, device=dev, dtype=torch.int32), n_new=pos, wrap=False)
         glob.append(L)
     q_s, q_g = randn(B, HKV * G, D), randn(B, 1, GHKV * GG, GD)
@@ -469,12 +475,13 @@ def decode_stack(swr, torch, randn, dev):
     global_bytes = sum(c + 1 for c in ctx) * GHKV * GD * 2 * 2 + 2 * B * GHKV * GG * GD * 2 + \
         B * GHKV * GD * 2 * 2 * 2
     nbytes = 50 * sliding_bytes + 10 * global_bytes
-    del sliding, glob, hk, hv, gkh, gvh
+    del sliding, glob, pool, hk, hv, gkh, gvh
     torch.cuda.empty_cache()
     return {"us": round(us, 1), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
             "layers": "50 sliding (W=1024, 8 KV heads x 256) + 10 global (2 KV heads x 512), five sliding to one global",
             "batch": B, "contexts": "U[1024, 4096], seed 1006",
-            "note": "one HIP graph of the 60 fused append + attention calls; every layer on K/V of its own"}
+            "note": "one HIP graph of the 60 fused append + attention calls; every layer on K/V of its own, "
+                    "carved from one pool"}
 
 
 def global_verify_fp8(swr, torch, randn, dev, n_layers=48):
