@@ -233,8 +233,10 @@ swr_status swr_global_attend(const swr_kv* kv, const void* q, void* out, const i
  * 2048 tiles of 32 keys the call is one chunked pass plus its merge: the
  * chunk holding the tokens' slots takes them from k_new/v_new (over fp8, as
  * the values of the codes that will be stored) and the merge stores them
- * once every chunk has read; longer calls run the append and then the
- * streamed pass.
+ * once every chunk has read.  Longer calls stream in one split-K pass; with
+ * one token per request (S = 1) the split that reads the token's tile takes
+ * it in place of the slot's old contents and stores it (over fp8, its
+ * codes), with more the append runs first.
  *   k_new, v_new  : device bf16 [B][S][Hkv][D]
  *   q, out        : device bf16 [B][S][Hq][D]
  *   pos0          : device int32 [B], pos0[b] >= 0, pos0[b] + S <= max_key_count and

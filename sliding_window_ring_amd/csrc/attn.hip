@@ -65,7 +65,8 @@ attn_kernel(const AttnParams p) {
   constexpr int RED = 2 * NCT * 4;  // score floats per lane per tile
   constexpr int RS = D + 4;         // padded LDS row stride (floats)
   constexpr bool DEC = MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND;
-  constexpr bool APP = MODE == MODE_DECODE_APPEND;
+  constexpr bool GS = MODE == MODE_GSTREAM || MODE == MODE_GSTREAM_APPEND;
+  constexpr bool APP = MODE == MODE_DECODE_APPEND || MODE == MODE_GSTREAM_APPEND;
   static_assert(!(APP && FP8) || DS <= 256, "an fp8 append writes a slice's K and V from one wave's lanes");
   extern __shared__ float smem[];
 
@@ -79,7 +80,7 @@ attn_kernel(const AttnParams p) {
   // gstream: the split balanced from the requests' key counts (split tiles
   // [st_lo, st_hi)); the workgroups past the last split exit here
   int unit, split, st_lo = 0, st_hi = 0;
-  if constexpr (MODE == MODE_GSTREAM) {
+  if constexpr (GS) {
     const StreamSplit x = stream_split(p, blockIdx.x);
     if (x.unit < 0) return;
     unit = x.unit;
@@ -115,8 +116,8 @@ attn_kernel(const AttnParams p) {
   n_keys = max(n_keys, 0);
   const int nt_region = (n_keys + 31) >> 5;
   const int nt_total = nt_region + (MODE == MODE_VERIFY ? 1 : 0);
-  const int t_begin = MODE == MODE_GSTREAM ? st_lo : split * p.tiles_per_split;
-  const int t_end = min(nt_total, MODE == MODE_GSTREAM ? st_hi : t_begin + p.tiles_per_split);
+  const int t_begin = GS ? st_lo : split * p.tiles_per_split;
+  const int t_end = min(nt_total, GS ? st_hi : t_begin + p.tiles_per_split);
   if (t_begin >= t_end) return;  // empty split: the combine step skips it
   const int n_it = (t_end - t_begin + KW - 1) / KW;
 
@@ -133,7 +134,7 @@ attn_kernel(const AttnParams p) {
     const int i = row_ok[ct] ? row / G : 0;
     const int h = row_ok[ct] ? row - i * G : 0;
     row_i[ct] = i;
-    row_lim[ct] = (MODE == MODE_GSTREAM) ? min(qpos_of(p, b, i), n_keys - 1) : p.cap - 2 - i;
+    row_lim[ct] = GS ? min(qpos_of(p, b, i), n_keys - 1) : p.cap - 2 - i;
     const uint16_t* qrow = p.q + ((size_t)(b * S + i) * p.Hq + g * G + h) * D + d_base;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -295,7 +296,8 @@ attn_kernel(const AttnParams p) {
     }
   };
 
-  // Fused append (decode): the new token, position pos in slot pos % W, is
+  // Fused append (decode; a streamed global call of one token per request):
+  // the new token, position pos in slot pos % W (global: slot pos), is
   // written by the waves that read its tile, each its own head-dim slice; no
   // other workgroup reads the tile.
   //  bf16: the wave loads the tile as it is (the slot still holds the token
@@ -322,9 +324,11 @@ attn_kernel(const AttnParams p) {
   bool writer = false;
   int t_new = -1, slot_new = 0;
   if (APP) {
-    slot_new = p.pos[b] % p.cap;
+    // a ring slot is the position mod W; a global region's slot is the
+    // position itself, stored only below the request's capacity
+    slot_new = DEC ? p.pos[b] % p.cap : p.pos[b];
     t_new = slot_new >> 5;
-    if (t_new >= t_begin && t_new < t_end) {
+    if (t_new >= t_begin && t_new < t_end && (DEC || slot_new < cap_r)) {
       if (FIRST) {
         rot = t_new - t_begin + 1;
         if (rot == nt) rot = 0;
@@ -511,7 +515,7 @@ attn_kernel(const AttnParams p) {
           bool vis;
           if (DEC) {
             vis = key < n_keys;
-          } else if (MODE == MODE_GSTREAM) {
+          } else if (GS) {
             vis = key <= row_lim[ct];
           } else if (prop_tile) {
             const int pi = 8 * lq + e;  // proposal index
@@ -594,7 +598,7 @@ attn_kernel(const AttnParams p) {
   };
 
   // partial slot: gstream, the split's number (the workgroup); else by unit
-  const size_t part = MODE == MODE_GSTREAM ? (size_t)blockIdx.x : (size_t)unit * p.nsplit + split;
+  const size_t part = GS ? (size_t)blockIdx.x : (size_t)unit * p.nsplit + split;
   if (KW == 1) {
     // This wave holds rows ct*16+lr, dims d_base + 16*dt + 4*lq + 0..3.
 #pragma unroll
@@ -748,7 +752,8 @@ struct Shape {
 // mixed step, 225 us (bf16) and 130 us (fp8) against 241 and 187 us for two
 // 256-dim slices x two key-split waves at one wave per SIMD.
 Shape pick_shape(int mode, int D, int nct) {
-  if (mode == MODE_DECODE || mode == MODE_DECODE_APPEND || (mode == MODE_GSTREAM && nct == 1)) {
+  if (mode == MODE_DECODE || mode == MODE_DECODE_APPEND ||
+      ((mode == MODE_GSTREAM || mode == MODE_GSTREAM_APPEND) && nct == 1)) {
     switch (D) {
       case 64: return {64, 4};
       case 128: return {128, 4};
@@ -811,8 +816,8 @@ hipError_t launch_fixed(const AttnPlan& pl, const AttnParams& p, hipStream_t s) 
 // up to 16 rows and the grouped shapes above.
 template <int MODE>
 hipError_t launch_mode(const AttnPlan& pl, const AttnParams& p, hipStream_t s) {
-  const bool decode_shape =
-      MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND || (MODE == MODE_GSTREAM && pl.nct == 1);
+  const bool decode_shape = MODE == MODE_DECODE || MODE == MODE_DECODE_APPEND ||
+                            ((MODE == MODE_GSTREAM || MODE == MODE_GSTREAM_APPEND) && pl.nct == 1);
   if constexpr (MODE != MODE_VERIFY) {
     if (decode_shape) {
       switch (pl.D) {
@@ -975,12 +980,13 @@ hipError_t launch_attention(const AttnPlan& pl, const AttnParams& p, hipStream_t
     case MODE_DECODE_APPEND: e = launch_mode<MODE_DECODE_APPEND>(pl, p, s); break;
     case MODE_VERIFY: e = launch_mode<MODE_VERIFY>(pl, p, s); break;
     case MODE_GSTREAM: e = launch_mode<MODE_GSTREAM>(pl, p, s); break;
+    case MODE_GSTREAM_APPEND: e = launch_mode<MODE_GSTREAM_APPEND>(pl, p, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || pl.nsplit == 1) return e;
   // a streamed global call: its splits, numbered from the key counts, merged
   // with each row's splits spread over thread groups
-  if (pl.mode == MODE_GSTREAM) return launch_split_merge(pl, p, s);
+  if (pl.mode == MODE_GSTREAM || pl.mode == MODE_GSTREAM_APPEND) return launch_split_merge(pl, p, s);
   const long total = (long)pl.units * pl.rows * (pl.D / 4);
   const int blocks = ceil_div(total, 256);
   if (pl.mode == MODE_DECODE || pl.mode == MODE_DECODE_APPEND)

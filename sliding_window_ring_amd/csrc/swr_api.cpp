@@ -135,14 +135,18 @@ swr_status attend(int mode, int append, const swr_kv* kv, const void* q, void* o
   if (mode == swr::MODE_GLOBAL && append) {
     if (pl.chunked) {
       p.append = 1;  // taken by the chunk holding the slots, stored by the merge
-      p.qpos_from_pos0 = 1;
+    } else if (S == 1) {
+      // long call of one token per request: the split holding the token's
+      // tile takes it in place of the slot's old contents and stores it, as
+      // the fused decode does
+      pl.mode = swr::MODE_GSTREAM_APPEND;
     } else {
-      // long call: the append kernel first, then the streamed pass with the
-      // positions and key counts derived from pos0
+      // long call of several tokens: the append kernel first, then the
+      // streamed pass
       const swr_status st2 = append_tokens(kv, k_prop, v_prop, pos, nullptr, B, S, Hkv, D, 0, stream);
       if (st2 != SWR_OK) return st2;
-      p.qpos_from_pos0 = 1;
     }
+    p.qpos_from_pos0 = 1;  // positions and key counts derived from pos0
   }
   if (pl.chunked) {
     uint8_t* w = static_cast<uint8_t*>(ws);

@@ -13,8 +13,16 @@ namespace swr {
 // single-pass split-K kernel of the ring calls over a contiguous region.
 // MODE_VERIFY runs in chunked form when the batch is small.
 // MODE_DECODE_APPEND is a decode that first writes the new token into its
-// ring slot (the fused append + decode call).
-enum Mode { MODE_DECODE = 0, MODE_VERIFY = 1, MODE_GLOBAL = 2, MODE_GSTREAM = 3, MODE_DECODE_APPEND = 4 };
+// ring slot (the fused append + decode call); MODE_GSTREAM_APPEND the same
+// for a streamed global call of one token per request (slot = position).
+enum Mode {
+  MODE_DECODE = 0,
+  MODE_VERIFY = 1,
+  MODE_GLOBAL = 2,
+  MODE_GSTREAM = 3,
+  MODE_DECODE_APPEND = 4,
+  MODE_GSTREAM_APPEND = 5
+};
 
 // Slots a region stores per KV head: its capacity rounded up to whole
 // 32-slot K tiles (region layout: swr_device.h).

@@ -240,10 +240,12 @@ def test_fused_global_per_request_capacities(dtype):
     assert_parity(host_f64(out), ref, "fused global, per-request capacities")
 
 
-@pytest.mark.parametrize("dtype,S", [(oracle.BF16, 4), (oracle.FP8, 4), (oracle.BF16, 1)], ids=["bf16", "fp8", "S1"])
+@pytest.mark.parametrize("dtype,S", [(oracle.BF16, 4), (oracle.FP8, 4), (oracle.BF16, 1), (oracle.FP8, 1)],
+                         ids=["bf16", "fp8", "S1", "fp8S1"])
 def test_fused_global_streamed(dtype, S):
-    # units x tiles >= 2048: the append kernel, then the streamed pass with
-    # positions derived from pos0
+    # units x tiles >= 2048: the streamed pass with positions derived from
+    # pos0; S > 1 runs the append kernel first, S = 1 takes the token in the
+    # split that reads its tile
     kc = np.array([S, 63, 64, 65, 700, 2000, 4099, 5000], np.int32)
     assert kc.size * 2 * -(-int(kc.max()) // 32) >= 2048
     G, D = 8, 512
@@ -254,3 +256,43 @@ def test_fused_global_streamed(dtype, S):
     ks, vs = (4.2 / 448, 5.2 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
     out, ref = fused_global_case(x, S, 5056, dtype, ks, vs)
     assert_parity(host_f64(out), ref, "fused streamed global")
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("G,D", [(8, 512), (16, 128), (4, 256), (8, 64), (32, 128)])
+def test_fused_global_streamed_one_token(G, D, dtype):
+    # one token per request in a streamed call: the split holding the token's
+    # tile substitutes it and stores it.  Tokens at slot 0 (the only key), at
+    # the last and first slots of a 32-key tile, at the last slot of a
+    # request's capacity, and deep in long regions; the decode shapes (up to
+    # 16 rows) and, at G = 32, the 32-row shapes
+    kc = np.array([1, 32, 33, 64, 96, 191, 700, 2047, 4000, 4093, 4096], np.int32)
+    caps = np.array([64, 64, 64, 64, 128, 192, 704, 2048, 4032, 4096, 4096], np.int32)  # each >= pad64(count)
+    B = kc.size
+    assert B * 2 * -(-int(kc.max()) // 32) >= 2048
+    g = synthetic.rng(77)
+    x = dict(key_count=kc, k=synthetic.normal_bf16(g, (B, 4096, 2, D)),
+             v=synthetic.normal_bf16(g, (B, 4096, 2, D)), q=synthetic.normal_bf16(g, (B, 1, 2 * G, D)))
+    ks, vs = (3.9 / 448, 4.7 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    out, ref = fused_global_case(x, 1, int(caps.max()), dtype, ks, vs, caps=caps)
+    assert_parity(host_f64(out), ref, f"fused streamed global, one token, G={G} D={D}")
+    if dtype == oracle.BF16:  # the request whose only key is its own token returns its value bits
+        assert np.array_equal(host_bits(out)[0, 0], np.repeat(x["v"][0, 0], G, axis=0))
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+def test_fused_global_streamed_stack_layer(dtype):
+    # a global layer of the B=56 decode step at its full size (2 KV heads x
+    # 512, 8 query heads each, contexts U[1024, 4096], one new token per
+    # request, per-request capacities): the streamed pass that takes each
+    # token in the split reading its tile, as the 60-layer stack runs it
+    B, D, G = 56, 512, 8
+    g = synthetic.rng(78)
+    kc = (synthetic.uniform_int(g, 1024, 4096, B) + 1).astype(np.int32)
+    caps = ((kc + 63) // 64 * 64).astype(np.int32)
+    x = dict(key_count=kc, k=synthetic.normal_bf16(g, (B, int(kc.max()), 2, D)),
+             v=synthetic.normal_bf16(g, (B, int(kc.max()), 2, D)), q=synthetic.normal_bf16(g, (B, 1, 2 * G, D)))
+    ks, vs = (4.4 / 448, 4.6 / 448) if dtype == oracle.FP8 else (1.0, 1.0)
+    out, ref = fused_global_case(x, 1, int(caps.max()), dtype, ks, vs, caps=caps)
+    e = assert_parity(host_f64(out), ref, "fused streamed global, B=56 stack layer")
+    print("fused streamed global B=56 max-abs %.3e rel-L2 %.3e" % e)
