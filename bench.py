@@ -378,16 +378,31 @@ def read_ceiling(swr, torch):
     torch.cuda.empty_cache()
     # One-shot reads of the sizes of the chunked calls' K/V: what the chip
     # gives a job that is one burst, not a stream.  12 rotating buffers
-    # (more than the last-level cache), launches back to back.
+    # (more than the last-level cache), one launch each, captured in one HIP
+    # graph: launched from the host one by one, these short reads would be
+    # timed at the rate the host issues them.
     one_shot = {}
     for label, nbytes, grids in (("sliding_verify_b8_kv_64MiB", 64 << 20, (256, 512)),
                                  ("global_verify_6005_kv_24.6MB", KC * GHKV * GD * 2 * 2, (94, 188, 256))):
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(12)]
         for grid in grids:
             for pattern in (0, 1):
-                us = _timed(torch, lambda i: swr.read_ceiling(bufs[i], sink, grid, pattern), 48, len(bufs))
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for buf in bufs:
+                        swr.read_ceiling(buf, sink, grid, pattern)
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(4):
+                    graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / (4 * len(bufs)) * 1e3
                 one_shot[f"{label}_{('sweep', 'span')[pattern]}_{grid}"] = {
                     "us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                del graph
         del bufs
         torch.cuda.empty_cache()
     return {"GB/s": round(best[0], 1), "bytes_per_launch": nb, "grid": best[1],
