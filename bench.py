@@ -276,6 +276,27 @@ def cpu_baseline():
             "host": {"cpu": cpu, "logical_cpus": os.cpu_count(), "oracle_threads": threads}}
 
 
+def _graph_timed(torch, fn, calls, replays):
+    """Average us per call of fn(i), i = 0 .. calls-1, captured once in a HIP
+    graph and replayed `replays` times: for calls short enough that launching
+    them one by one from Python would time the host's issue rate.  The graph
+    must hold enough work that a replay outlasts its own launch from the host
+    (tens of microseconds): a few short calls per graph time the launch."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(calls):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * calls) * 1e3
+
+
 def _timed(torch, fn, reps, sets):
     """Average us per call of fn(i) over `reps` calls cycling through `sets`,
     with events on the current stream around the whole loop."""
@@ -378,31 +399,19 @@ def read_ceiling(swr, torch):
     torch.cuda.empty_cache()
     # One-shot reads of the sizes of the chunked calls' K/V: what the chip
     # gives a job that is one burst, not a stream.  12 rotating buffers
-    # (more than the last-level cache), one launch each, captured in one HIP
-    # graph: launched from the host one by one, these short reads would be
-    # timed at the rate the host issues them.
+    # (more than the last-level cache), four launches each, captured in one
+    # HIP graph: launched from the host one by one, these short reads would
+    # be timed at the rate the host issues them.
     one_shot = {}
     for label, nbytes, grids in (("sliding_verify_b8_kv_64MiB", 64 << 20, (256, 512)),
                                  ("global_verify_6005_kv_24.6MB", KC * GHKV * GD * 2 * 2, (94, 188, 256))):
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(12)]
         for grid in grids:
             for pattern in (0, 1):
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph):
-                    for buf in bufs:
-                        swr.read_ceiling(buf, sink, grid, pattern)
-                graph.replay()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(4):
-                    graph.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / (4 * len(bufs)) * 1e3
+                us = _graph_timed(torch, lambda i: swr.read_ceiling(bufs[i % len(bufs)], sink, grid, pattern),
+                                  4 * len(bufs), 4)
                 one_shot[f"{label}_{('sweep', 'span')[pattern]}_{grid}"] = {
                     "us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
-                del graph
         del bufs
         torch.cuda.empty_cache()
     return {"GB/s": round(best[0], 1), "bytes_per_launch": nb, "grid": best[1],
@@ -526,20 +535,7 @@ def global_verify_fp8(swr, torch, randn, dev, n_layers=48):
     torch.cuda.synchronize()
 
     def graph_us(layer_fn):
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for g in layers:
-                layer_fn(g)
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        g0.record()
-        for _ in range(reps):
-            graph.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        return g0.elapsed_time(g1) / (reps * len(layers)) * 1e3
+        return _graph_timed(torch, lambda i: layer_fn(layers[i]), len(layers), 10)
 
     us_attn = graph_us(lambda g: swr.global_attend(g["L"], g["q"], g["q_pos"], g["kc"], KC, GHKV, GD ** -0.5,
                                                    out=g["out"], ws=ws))
@@ -887,33 +883,24 @@ def main():
     # back over the 3 layer sets, events around the loop.
     sliding_b2b_us = _timed(torch, lambda i: sliding_layer(sliding[i]), 60, N_SLIDING_SETS)
 
-    # The separate calls, each timed back to back over the same layer sets:
-    # the decode without its append, and the append alone.
+    # The separate calls, each timed over the same layer sets: the decode
+    # without its append, back to back, and the append alone, a launch of a
+    # few microseconds, from a captured graph.
     decode_only_us = _timed(torch, lambda i: swr.swa_decode(sliding[i]["L"], sliding[i]["q"], sliding[i]["pos"], HKV,
                                                             scale_s, out=sliding[i]["out"], ws=dws),
                             30, N_SLIDING_SETS)
-    append_only_us = _timed(torch, lambda i: swr.ring_kv_append(sliding[i]["L"], sliding[i]["k_new"], sliding[i]["v_new"],
-                                                           sliding[i]["pos"]), 30, N_SLIDING_SETS)
+    def append_only(i):
+        s = sliding[i % N_SLIDING_SETS]
+        swr.ring_kv_append(s["L"], s["k_new"], s["v_new"], s["pos"])
+
+    append_only_us = _graph_timed(torch, append_only, 8 * N_SLIDING_SETS, 10)
 
     # The global layer's launches are short: also time them the way a serving
     # loop issues them, captured in one HIP graph holding all 24 global layers
     # -- the fused call, the separate append + attention, and the attention
     # call alone.
     def graph_us(layer_fn):
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for g in glob:
-                layer_fn(g)
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        g0.record()
-        for _ in range(reps):
-            graph.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        return g0.elapsed_time(g1) / (reps * N_GLOBAL_SETS) * 1e3
+        return _graph_timed(torch, lambda i: layer_fn(glob[i]), N_GLOBAL_SETS, 10)
 
     global_graph_us = graph_us(global_layer)
     global_sep_graph_us = graph_us(global_separate)
