@@ -14,7 +14,22 @@ from gpu_common import dev_bf16, dev_i32, layer, pool_bytes
 pytestmark = pytest.mark.gpu
 
 
-def run_both(B, T, hkv, d, cap, dtype, ks, vs, pos0, n_new, wrap, seed, special=False):
+def fitting(pos0, n_new, T, cap):
+    """(pos0, counts) of the tokens of each request that land below a global
+    region's capacity: what the library's dropping of positions past it
+    leaves written.  The oracle refuses such positions rather than dropping
+    them; a request none of whose tokens fit starts at the capacity with
+    none to write."""
+    p = np.asarray(pos0, np.int64)
+    n = np.full(len(p), T, np.int64) if n_new is None else np.asarray(n_new, np.int64)
+    fit = np.clip(np.minimum(n, cap - p), 0, None)
+    return np.minimum(p, cap).astype(np.int32), fit.astype(np.int32)
+
+
+def run_both(B, T, hkv, d, cap, dtype, ks, vs, pos0, n_new, wrap, seed, special=False, oracle_tokens=None):
+    """The library's append and the oracle's on the same starting bytes;
+    oracle_tokens: the oracle's (pos0, counts) where they differ (global
+    positions past the capacity, see fitting)."""
     g = synthetic.rng(seed)
     rb = oracle.region_bytes(cap, hkv, d, dtype)
     # start from the same random bytes on both sides so untouched slots are checked too
@@ -37,7 +52,8 @@ def run_both(B, T, hkv, d, cap, dtype, ks, vs, pos0, n_new, wrap, seed, special=
     swr.ring_kv_append(L, dev_bf16(k_new), dev_bf16(v_new), dev_i32(pos0),
                   None if n_new is None else dev_i32(n_new), wrap=wrap)
     torch.cuda.synchronize()
-    oracle.kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, ks, vs, k_new, v_new, pos0, n_new, wrap=wrap)
+    op0, on = (pos0, n_new) if oracle_tokens is None else oracle_tokens
+    oracle.kv_append(k_pool, v_pool, k_off, v_off, cap, dtype, ks, vs, k_new, v_new, op0, on, wrap=wrap)
     gk, gv = pool_bytes(L.k_base), pool_bytes(L.v_base)
     nk = int(np.count_nonzero(gk != k_pool))
     nv = int(np.count_nonzero(gv != v_pool))
@@ -66,9 +82,11 @@ def test_global_region_slots_are_positions():
 
 
 def test_global_positions_past_capacity_are_dropped():
-    # the oracle refuses positions past the capacity; the library drops them.
-    # Both leave bytes below the capacity identical when every token fits.
-    run_both(1, 8, 1, 64, 64, oracle.BF16, 1, 1, np.array([56], np.int32), None, False, seed=6)
+    # the library drops positions past the capacity: tokens 4..7 of request 0
+    # and all of request 1 fall past it, request 2 fits exactly; every byte
+    # equals the oracle's append of the tokens that fit
+    pos0 = np.array([60, 64, 56], np.int32)
+    run_both(3, 8, 1, 64, 64, oracle.BF16, 1, 1, pos0, None, False, seed=6, oracle_tokens=fitting(pos0, None, 8, 64))
 
 
 @pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.0123, 0.0456), (2.0 ** -4, 3.0), (1e-3, 7.5)])

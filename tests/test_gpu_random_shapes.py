@@ -6,7 +6,10 @@ case draws a whole configuration inside the documented envelope (include/
 swr.h): head dim, KV heads, query heads per KV head, proposals, window or
 capacity, positions or key counts (partial and wrapped rings, counts on and
 off tile and chunk edges), element type and scales, and per-request global
-capacities.  The draws fall on both sides of the launch-form thresholds:
+capacities.  The append call draws its token counts too
+(none, a few, more than a ring holds), positions past a global region's
+capacity (dropped) and special values (saturation, subnormals, signed
+zeros, infinities).  The draws fall on both sides of the launch-form thresholds:
 split-K or whole-unit decode, chunked or ring-kernel verify, chunked or
 streamed global calls (with one token per request or several for the fused
 call).  Outputs are held to the parity bar; the fused calls' region bytes
@@ -19,6 +22,7 @@ import oracle
 import synthetic
 from gpu_common import host_f64
 from helpers import assert_parity
+from test_gpu_append import fitting, run_both
 from test_gpu_attention import decode_case, global_case, verify_case
 from test_gpu_fused import fused_decode_case, fused_global_case
 
@@ -147,3 +151,19 @@ def test_random_fused_global(case):
              v=synthetic.normal_bf16(g, (B, kmax, Hkv, D)), q=synthetic.normal_bf16(g, (B, S, Hkv * G, D)))
     out, ref = fused_global_case(x, S, cap, dtype, ks, vs, caps=caps, seed=5900 + case)
     assert_parity(host_f64(out), ref, f"random fused global B={B} Hkv={Hkv} G={G} D={D} S={S} dtype={dtype}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_append(case):
+    g = synthetic.rng(6000 + case)
+    D = int(g.choice(DIMS))
+    hkv = int(g.choice((1, 2, 4, 8)))
+    B = int(g.integers(1, 9))
+    T = int(g.integers(1, 33))
+    wrap = bool(g.random() < 0.6)
+    dtype, ks, vs = draw_dtype(g)
+    cap = int(8 * g.integers(2, (512 if D == 512 else 2048) // 8 + 1))
+    pos0 = (g.integers(0, 4 * cap, B) if wrap else g.integers(0, cap + 8, B)).astype(np.int32)
+    n_new = None if g.random() < 0.4 else g.integers(0, T + 1, B).astype(np.int32)
+    run_both(B, T, hkv, D, cap, dtype, ks, vs, pos0, n_new, wrap, seed=6100 + case, special=bool(g.random() < 0.3),
+             oracle_tokens=None if wrap else fitting(pos0, n_new, T, cap))
