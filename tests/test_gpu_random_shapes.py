@@ -9,7 +9,9 @@ off tile and chunk edges), element type and scales, and per-request global
 capacities.  The append call draws its token counts too
 (none, a few, more than a ring holds), positions past a global region's
 capacity (dropped) and special values (saturation, subnormals, signed
-zeros, infinities).  The draws fall on both sides of the launch-form thresholds:
+zeros, infinities); the paged gather (the baseline the ring replaces)
+draws its page size and window.  The draws fall on both sides of the
+launch-form thresholds:
 split-K or whole-unit decode, chunked or ring-kernel verify, chunked or
 streamed global calls (with one token per request or several for the fused
 call).  Outputs are held to the parity bar; the fused calls' region bytes
@@ -25,6 +27,7 @@ from helpers import assert_parity
 from test_gpu_append import fitting, run_both
 from test_gpu_attention import decode_case, global_case, verify_case
 from test_gpu_fused import fused_decode_case, fused_global_case
+from test_gpu_gather import run_gather
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +170,14 @@ def test_random_append(case):
     n_new = None if g.random() < 0.4 else g.integers(0, T + 1, B).astype(np.int32)
     run_both(B, T, hkv, D, cap, dtype, ks, vs, pos0, n_new, wrap, seed=6100 + case, special=bool(g.random() < 0.3),
              oracle_tokens=None if wrap else fitting(pos0, n_new, T, cap))
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_paged_gather(case):
+    g = synthetic.rng(6200 + case)
+    D = int(g.choice(DIMS))
+    hkv = int(g.choice((1, 2, 4, 8)))
+    W = int(8 * g.integers(2, (512 if D == 512 else 1024) // 8 + 1))
+    pt = int(g.choice((1, 3, 8, 16, 32, 64)))
+    B = int(g.integers(1, 9))
+    run_gather(W, D, hkv, pt, draw_positions(g, B, W), seed=6300 + case)
