@@ -301,15 +301,51 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       }
     }
   };
+  // Q of the group's rows, once per workgroup, into LDS.  Rows past p.rows
+  // take row 0's values: their scores are masked and their outputs never
+  // stored, so any finite values do, and no select on the loaded data
+  // (which the compiler places right after the load, holding every later
+  // load of the wave behind a full round trip) is needed.  Q goes out ahead
+  // of K (it does not wait for the region offsets): loads return in issue
+  // order, so Q, and the staged tokens of a call that appends, reach LDS
+  // while K is still in flight.  Verify: the first half's scores then wait
+  // for that half's keys alone.  Global: issued after K, Q had made the LDS
+  // writes wait for every K load (a 6005-key call that appends, in a graph:
+  // 17.0 -> 16.5 us; the attention alone unchanged).
+  constexpr int QPIECES = ROWS * D / 8;
+  constexpr int QPT = (QPIECES + 64 * NW - 1) / (64 * NW);  // Q pieces per thread
+  bf16x8 qv[QPT];
+  auto load_q = [&] {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = threadIdx.x + k * 64 * NW;
+      const int row = min(idx, QPIECES - 1) / (D / 8), d8 = (min(idx, QPIECES - 1) - row * (D / 8)) * 8;
+      const int rr = row < p.rows ? row : 0;
+      const int i = rr / G, hq = rr - (rr / G) * G;
+      qv[k] = as_bf16x8(load16_global(p.q + ((size_t)(b * S + i) * p.Hq + g * G + hq) * D + d8));
+    }
+  };
+  auto store_q = [&] {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = threadIdx.x + k * 64 * NW;
+      if (idx < QPIECES) {
+        const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = qv[k];
+      }
+    }
+  };
+  load_q();
   // global call that appends its own S tokens (keys pos0 .. pos0+S-1):
   // the chunk holding any of their slots stages them in LDS (bf16: one
   // 16-byte piece of K and of V per thread, S*D/8 <= 512 pieces; fp8: one
   // 4-value piece of K or V per thread, each value encoded and decoded, so
-  // that the encodes spread over every wave of the workgroup), loaded here
-  // ahead of the region's loads and written to LDS after the Q loads have
-  // gone out (the load counter drains in order: the staging then waits for
-  // the tokens alone, and an LDS write placed before the Q loads would hold
-  // them back until the tokens arrived); the Q barrier covers the writes.
+  // that the encodes spread over every wave of the workgroup), loaded after
+  // Q and ahead of the region's loads (the load counter drains in order: the
+  // staging then waits for Q and the tokens, not for K; the tokens wait for
+  // their position, and Q issued behind them had waited too: 16.4 -> 16.2 us
+  // for the 6005-key call in a graph) and written to LDS after the region's
+  // loads have gone out; the Q barrier covers the writes.
   // V goes into the 8-slot block form (chunk_tokens), so that the value
   // operands take a key group's tokens with one 16-byte read and a mask per
   // tile: taken element by element, the 2-byte reads and their waits ran in
@@ -354,41 +390,6 @@ __device__ __forceinline__ void chunk_item(const AttnParams& p, ChunkSmem<D, NCT
       tok_vbits = load16_global(p.v_prop + src);
     }
   }
-  // Q of the group's rows, once per workgroup, into LDS.  Rows past p.rows
-  // take row 0's values: their scores are masked and their outputs never
-  // stored, so any finite values do, and no select on the loaded data
-  // (which the compiler places right after the load, holding every later
-  // load of the wave behind a full round trip) is needed.  Q goes out ahead
-  // of K (it does not wait for the region offsets): loads return in issue
-  // order, so Q, and the staged tokens of a call that appends, reach LDS
-  // while K is still in flight.  Verify: the first half's scores then wait
-  // for that half's keys alone.  Global: issued after K, Q had made the LDS
-  // writes wait for every K load (a 6005-key call that appends, in a graph:
-  // 17.0 -> 16.5 us; the attention alone unchanged).
-  constexpr int QPIECES = ROWS * D / 8;
-  constexpr int QPT = (QPIECES + 64 * NW - 1) / (64 * NW);  // Q pieces per thread
-  bf16x8 qv[QPT];
-  auto load_q = [&] {
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-      const int idx = threadIdx.x + k * 64 * NW;
-      const int row = min(idx, QPIECES - 1) / (D / 8), d8 = (min(idx, QPIECES - 1) - row * (D / 8)) * 8;
-      const int rr = row < p.rows ? row : 0;
-      const int i = rr / G, hq = rr - (rr / G) * G;
-      qv[k] = as_bf16x8(load16_global(p.q + ((size_t)(b * S + i) * p.Hq + g * G + hq) * D + d8));
-    }
-  };
-  auto store_q = [&] {
-#pragma unroll
-    for (int k = 0; k < QPT; ++k) {
-      const int idx = threadIdx.x + k * 64 * NW;
-      if (idx < QPIECES) {
-        const int row = idx / (D / 8), d8 = (idx - row * (D / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&qbuf[row][d8]) = qv[k];
-      }
-    }
-  };
-  load_q();
   {  // K of every half
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
