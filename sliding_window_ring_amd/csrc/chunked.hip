@@ -826,12 +826,19 @@ struct RunningRow {
 };
 
 // Adds chunks c = c0 + j*step (j < kMergeBatch, c < nvalid) of the row at
-// `slot0` (+ c*rows), four dims at `d`; `navail` partials are stored for the
-// row.  On the first batch the request's chunk count is read (the chunked
-// form; a streamed call's count is known), and `issued` runs, after the
-// batch's loads are issued: work that waits only for earlier loads then
-// overlaps them.
-template <int MODE, typename F>
+// `slot0` (+ c*rows), four dims at `d`; `navail` (>= 1) partials are stored
+// for the row.  On the first batch the request's chunk count is read (the
+// chunked form; a streamed call's count is known), and `issued` runs, after
+// the batch's loads are issued: work that waits only for earlier loads then
+// overlaps them.  CLAMP: indices past the stored partials read the last one
+// again (their values dropped by the selects below), so the batch's loads go
+// out with no branch between them; with a branch per partial the compiler
+// copied a loaded register inside one and waited there for the loads so far,
+// a round trip in the middle of the batch (6005-key global verify 15.5 ->
+// 15.3 us).  Where a row has only a few partials (the sliding verify's four)
+// the repeated loads cost more than that (21.4 -> 22.3 us) and each partial
+// keeps its branch.
+template <int MODE, bool CLAMP, typename F>
 __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, size_t slot0, int d, int c0,
                                             int step, int navail, bool first, int& nvalid, RunningRow& r,
                                             F&& issued) {
@@ -839,14 +846,21 @@ __device__ __forceinline__ void merge_batch(const AttnParams& p, int D, int b, s
   f32x4 a[kMergeBatch];
 #pragma unroll
   for (int j = 0; j < kMergeBatch; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-    a[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (c0 + j * step < navail) {  // past the stored partials: no load at all
-      const size_t at = slot0 + (size_t)(c0 + j * step) * p.rows;
+    if (CLAMP) {
+      const size_t at = slot0 + (size_t)min(c0 + j * step, navail - 1) * p.rows;
       m[j] = p.ws_pml[at * 2];
       l[j] = p.ws_pml[at * 2 + 1];
       a[j] = *reinterpret_cast<const f32x4*>(p.ws_part + at * D + d);
+    } else {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+      a[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c0 + j * step < navail) {  // past the stored partials: no load at all
+        const size_t at = slot0 + (size_t)(c0 + j * step) * p.rows;
+        m[j] = p.ws_pml[at * 2];
+        l[j] = p.ws_pml[at * 2 + 1];
+        a[j] = *reinterpret_cast<const f32x4*>(p.ws_part + at * D + d);
+      }
     }
   }
   if (first) {
@@ -935,7 +949,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_grouped(const AttnParams 
   int nvalid = navail;
   for (int c0 = grp; c0 < nvalid; c0 += kMergeBatch * NG) {
     // the tokens' stores go out once the first batch's loads are in flight
-    merge_batch<MODE>(p, D, b, slot0, d, c0, NG, navail, c0 == grp, nvalid, r, [&] { store_tokens(); });
+    merge_batch<MODE, true>(p, D, b, slot0, d, c0, NG, navail, c0 == grp, nvalid, r, [&] { store_tokens(); });
   }
   store_tokens();  // a group with no chunk to merge
   if constexpr (FP8) {  // rows * kMergeThreads < tok_values: the rest in turn
@@ -987,7 +1001,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_flat(const AttnParams p, 
   RunningRow r;
   int nvalid = p.nchunk;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch) {
-    merge_batch<MODE>(p, D, b, slot0, d, c0, 1, p.nchunk, c0 == 0, nvalid, r, [] {});
+    merge_batch<MODE, false>(p, D, b, slot0, d, c0, 1, p.nchunk, c0 == 0, nvalid, r, [] {});
   }
   if (MODE == MODE_GLOBAL && p.append) {
     if constexpr (FP8) {
@@ -1017,7 +1031,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_stream_flat(const AttnPar
   RunningRow r;
   int nvalid = x.n;
   for (int c0 = 0; c0 < nvalid; c0 += kMergeBatch)
-    merge_batch<MODE_GSTREAM>(p, D, b, slot0, d, c0, 1, x.n, c0 == 0, nvalid, r, [] {});
+    merge_batch<MODE_GSTREAM, true>(p, D, b, slot0, d, c0, 1, x.n, c0 == 0, nvalid, r, [] {});
   store_row4(p, D, b, g, row, d, r.L, r.O);
 }
 
