@@ -67,6 +67,19 @@ def test_noalloc_matches_workspace_call_twice_second_smaller(dtype):
     run_both(case(502, [300, 77], 2, 8, 512, 2, 320, dtype))
 
 
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
+def test_noalloc_streamed_one_token_twice_second_smaller(dtype):
+    # streamed calls (the units span >= 2048 tiles of 32 keys) of one token
+    # per request, whose split pass takes each token itself; at 64 head dims
+    # their partials (at least 512 slots) fit the scratch
+    kc1 = [4100, 4500, 4093, 5000, 4200, 4800, 4300, 4097]
+    assert len(kc1) * 2 * -(-max(kc1) // 32) >= 2048
+    run_both(case(503, kc1, 1, 8, 64, 2, 5056, dtype))
+    kc2 = [8300, 8200, 8192, 8257]
+    assert len(kc2) * 2 * -(-max(kc2) // 32) >= 2048
+    run_both(case(504, kc2, 1, 8, 64, 2, 8320, dtype))
+
+
 def test_noalloc_rejects_a_call_past_the_scratch():
     # 16 MiB of scratch: 16 requests of 8,000 keys need more
     need = swr.workspace_bytes(swr.SWR_OP_GLOBAL_APPEND_ATTEND, 16, 4, 16, 2, 512, 8000)
