@@ -608,6 +608,32 @@ def other_workloads(swr, torch, sweep=True):
                                     "algorithmic_bytes": nbytes, "sets": len(sets)}
     del sets, ws
 
+    # --- the same verify at B=32 (256 units: the batch fills the chip), bf16 (3 sets of 269 MB)
+    # and fp8 (4 sets of 135 MB)
+    w = synthetic.Workload("sliding verify B=32", B=32, Hkv=8, G=8, D=256, W=1024, S=4, pos_lo=1024, pos_hi=8192)
+    for dt, n_sets, name in ((swr.SWR_KV_BF16, 3, "sliding_verify_b32"), (swr.SWR_KV_FP8_E4M3, 4, "sliding_verify_b32_fp8")):
+        fp8 = dt == swr.SWR_KV_FP8_E4M3
+        sets = []
+        for _ in range(n_sets):
+            rb = swr.region_bytes(w.W, w.Hkv, w.D, dt)
+            kb = torch.empty(w.B * rb, dtype=torch.uint8, device=dev)
+            vb = torch.empty_like(kb)
+            off = torch.arange(w.B, device=dev, dtype=torch.int64) * rb
+            L = swr.KVLayer(kb, vb, off, off.clone(), w.W, *((dt, 4.5 / 448, 4.5 / 448) if fp8 else ()))
+            p0 = torch.randint(w.pos_lo, w.pos_hi + 1, (w.B,), device=dev, dtype=torch.int32, generator=gen)
+            swr.ring_kv_append(L, randn(w.B, w.W, w.Hkv, w.D), randn(w.B, w.W, w.Hkv, w.D), (p0 - w.W).to(torch.int32))
+            q = randn(w.B, w.S, w.Hq, w.D)
+            sets.append((L, randn(w.B, w.S, w.Hkv, w.D), randn(w.B, w.S, w.Hkv, w.D), q, p0, torch.empty_like(q)))
+        ws = torch.zeros(max(16, swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, w.B, w.S, w.Hq, w.Hkv, w.D, w.W)),
+                         dtype=torch.uint8, device=dev)
+        us = _timed(torch, lambda i: swr.gqa_verify(sets[i][0], sets[i][1], sets[i][2], sets[i][3], sets[i][4],
+                                                    w.D ** -0.5, out=sets[i][5], ws=ws), 40, len(sets))
+        nbytes = w.B * w.Hkv * (w.W - 1) * w.D * 2 * (1 if fp8 else 2) + 2 * w.B * w.S * w.Hkv * w.D * 2 + \
+            2 * w.B * w.S * w.Hq * w.D * 2
+        res[name] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1), "algorithmic_bytes": nbytes,
+                     "sets": len(sets)}
+        del sets, ws
+
     # --- one GPU's share of the B=56 decode under KV-head sharding (8 GPUs, one KV head each):
     # 10 sets of 58.7 MB, more than twice the 256 MB last-level cache
     w = synthetic.SWA_DECODE

@@ -266,9 +266,11 @@ swr_status swr_global_append_attend_noalloc(const swr_kv* kv, const void* k_new,
                                             int max_key_count, int B, int S, int Hq, int Hkv, int D,
                                             float scale, hipStream_t stream);
 
-/* Workspace bytes an attention call needs (0 when it needs none).  For
- * decode and verify `cap_or_max_keys` is the window W; for global attention it
- * is max_key_count.  Returns 0 for unsupported shapes as well (the call then
+/* Workspace bytes an attention call needs (0 when it needs none), for
+ * either element type: the larger of the bf16 and fp8 calls' needs, since
+ * the type can pick the launch form.  For decode and verify
+ * `cap_or_max_keys` is the window W; for global attention it is
+ * max_key_count.  Returns 0 for unsupported shapes as well (the call then
  * reports the shape error).  The workspace holds per-split partial results
  * (running maximum, weight sum and unnormalised output rows, fp32). */
 size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap_or_max_keys);

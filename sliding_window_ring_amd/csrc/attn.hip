@@ -878,10 +878,16 @@ bool plan_attention(int mode, int B, int S, int Hq, int Hkv, int D, int fp8, int
     }
     mode = MODE_GSTREAM;
   }
-  // A verify whose (request, KV head) units do not fill the chip runs in
-  // chunked form: every chunk's loads in flight at once, instead of a split
-  // that walks its tiles one after another.
-  if (mode == MODE_VERIFY && B >= 0 && Hkv >= 1 && (long)B * Hkv < kNumCU) {
+  // A verify runs in chunked form (every chunk's loads in flight at once,
+  // sixteen waves per 256 keys) unless its (request, KV head) units fill
+  // the chip twice over with bf16 K/V: this kernel gives a verify's 32 rows
+  // two waves per unit, one per 128-dim slice, each walking the unit's tiles
+  // alone, and over fp8 it converts each load as it lands.  W=1024, 8 KV
+  // heads x 256, S=4, this kernel against the chunked form: B=32 bf16 93 vs
+  // 77 us, fp8 136 vs 60; B=64 bf16 107-117 vs 143, fp8 146 vs 115; B=128
+  // bf16 203 vs 275, fp8 285 vs 218.  The chunked form's partials take
+  // about 132 KB of workspace per unit.
+  if (mode == MODE_VERIFY && B >= 0 && Hkv >= 1 && (fp8 || (long)B * Hkv < 2L * kNumCU)) {
     if (!plan_chunked(MODE_VERIFY, B, S, Hq, Hkv, D, cap_or_max_keys, pl)) return false;
     pl->fp8 = fp8 ? 1 : 0;
     return true;

@@ -251,9 +251,12 @@ size_t swr_workspace_bytes(int op, int B, int S, int Hq, int Hkv, int D, int cap
     }
     default: return 0;
   }
-  AttnPlan pl;
-  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, 0, cap_or_max_keys, &pl)) return 0;
-  return pl.ws_bytes;
+  // the larger of the bf16 and fp8 plans: the element type can pick the
+  // launch form (a verify over fp8 runs chunked at every batch)
+  AttnPlan p16, p8;
+  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, 0, cap_or_max_keys, &p16)) return 0;
+  if (!swr::plan_attention(mode, B, S, Hq, Hkv, D, 1, cap_or_max_keys, &p8)) return 0;
+  return std::max(p16.ws_bytes, p8.ws_bytes);
 }
 
 int64_t swr_kv_region_bytes(int cap, int Hkv, int D, int dtype) {

@@ -229,6 +229,15 @@ def test_verify_workspace_is_one_partial_per_256_ring_keys():
     assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 4, 64, 8, 256, 1024) == want
 
 
+def test_verify_workspace_covers_either_element_type():
+    # B=64 x 8 KV heads = 512 units: with bf16 K/V the verify runs unsplit in
+    # the ring kernel (no workspace), over fp8 in chunked form; the query has
+    # no element type, so it reports the chunked form's partials
+    units, chunks, rows, d = 64 * 8, 1024 // 256, 8 * 4, 256
+    want = units * chunks * rows * d * 4 + units * chunks * rows * 2 * 4
+    assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 64, 4, 64, 8, 256, 1024) == want
+
+
 def test_workspace_bytes_unsupported_is_zero():
     assert swr.workspace_bytes(swr.SWR_OP_GQA_VERIFY, 8, 9, 64, 8, 256, 1024) == 0
     assert swr.workspace_bytes(99, 8, 4, 64, 8, 256, 1024) == 0

@@ -191,11 +191,13 @@ def test_verify_head_dims(D):
 
 
 @pytest.mark.parametrize("dtype", [oracle.BF16, oracle.FP8], ids=["bf16", "fp8"])
-def test_verify_large_batch(dtype):
-    """B * Hkv >= 256 units fill the chip without splitting: the ring kernel
-    takes the call (smaller batches run in chunked form)."""
-    w = synthetic.Workload("t", B=32, Hkv=8, G=8, D=64, W=96, S=4)
-    x = synthetic.sliding_verify(w, seed=40, positions=synthetic.uniform_int(synthetic.rng(41), 0, 400, 32))
+@pytest.mark.parametrize("B", [32, 64])
+def test_verify_large_batch(dtype, B):
+    """Batches that fill the chip: 256 units run in chunked form, 512 units
+    with bf16 K/V in the ring kernel without splitting (over fp8 every batch
+    runs chunked)."""
+    w = synthetic.Workload("t", B=B, Hkv=8, G=8, D=64, W=96, S=4)
+    x = synthetic.sliding_verify(w, seed=40, positions=synthetic.uniform_int(synthetic.rng(41), 0, 400, B))
     out, ref = verify_case(w, x, dtype, *((0.0105, 0.0094) if dtype else (1.0, 1.0)))
     assert_parity(host_f64(out), ref, "large-batch verify")
 

@@ -68,7 +68,8 @@ def sliding_workload(g, verify):
         S, G = 1, int(g.choice((1, 2, 4, 8, 16)))
     big = g.random() < 0.2  # enough (request, KV head) units to fill the chip
     if big:
-        Hkv, B, D = 8, int(g.integers(32, 41)), int(g.choice((64, 128)))
+        # (a verify with bf16 K/V leaves the chunked form at 512 units)
+        Hkv, B, D = 8, int(g.integers(64 if verify else 32, 81)), int(g.choice((64, 128)))
         W = int(8 * g.integers(2, 17))
     else:
         Hkv = int(g.choice((1, 2, 4, 8)))
