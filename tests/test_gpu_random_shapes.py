@@ -31,7 +31,7 @@ from test_gpu_gather import run_gather
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 20
+N_CASES = 40
 DIMS = (64, 128, 256, 512)
 
 
